@@ -1,0 +1,431 @@
+// Video-tile pooling, pooled-score top-k selection and the compression branch.
+//
+// Semantics: FastVideo test_vsa256_backward.py (the VSA entry points select
+// `topk` KV tiles per Q tile and compose the sparse output with a gated
+// compression output; q_var only changes the compression divisor). The
+// reading implemented here: pooled tiles are means over valid slots, the
+// coarse score is C = scale <Qc_i, Kc_j> over non-empty KV tiles, top-k keeps
+// the largest scores (ties to the lower tile), the compression output is
+// O_c = softmax_j(C) V_c, and its gradient returns to the valid slots
+// divided by the tile's valid count.
+//
+// gfx950 design: these steps are small (tens of GFLOP at the largest video
+// shape) and run on fp32 VALU. Pooling is one work-group per tile with
+// coalesced 16-byte loads and an LDS reduction. The coarse kernels keep a
+// block of CR score rows in LDS, stream the pooled K/V tiles once per block,
+// select top-k per row with a 4-pass 8-bit radix select (per-wave LDS
+// histograms, ties resolved by ascending tile index with ballots) and write
+// the map bytes directly.
+#include "kernels.hpp"
+
+namespace vsa {
+
+namespace {
+
+template <class ET>
+__global__ __launch_bounds__(256) void pool_kernel(const Geom g, const uint16_t* __restrict__ x,
+                                                   int is_q, float* __restrict__ out) {
+  using E = Elem<ET>;
+  __shared__ float red[16][HD];
+  const int heads = is_q ? g.Hq : g.Hkv, nb = is_q ? g.Qb : g.KVb;
+  int id = blockIdx.x;
+  const int blk = id % nb;
+  id /= nb;
+  const int h = id % heads, b = id / heads;
+  const int n = is_q ? g.q_val(b, blk) : g.kv_val(b, blk);
+  const long long base = (is_q ? g.q_base(b, h) : g.kv_base(b, h)) +
+                         (long long)blk * (is_q ? g.q_block : g.kv_block) * (is_q ? g.q_rs() : g.kv_rs());
+  const long long rs = is_q ? g.q_rs() : g.kv_rs();
+  const int tid = threadIdx.x, slot = tid >> 4, dg = tid & 15;
+  float acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  for (int r = slot; r < n; r += 16) {
+    const uint4 v = ldg16(x + base + (long long)r * rs + 8 * dg);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[2 * u] += E::lo(w[u]);
+      acc[2 * u + 1] += E::hi(w[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) red[slot][8 * dg + u] = acc[u];
+  __syncthreads();
+  if (tid < HD) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += red[r][tid];
+    const long long o = is_q ? g.pq(b, h, blk) : g.pk(b, h, blk);
+    out[o + tid] = n > 0 ? s / (float)n : 0.f;
+  }
+}
+
+// order-preserving map of fp32 to uint32 (-0 folded onto +0)
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Coarse scores for CR Q tiles, then (optionally) top-k -> map bytes and the
+// coarse attention O_c / lse_c. Dynamic LDS: sc[CR][KVb], qcs[CR][HD], hist[4][256].
+__global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int CR, int want_topk,
+                                                         int want_gate) {
+  extern __shared__ float dsm[];
+  const Geom& g = a.g;
+  const int KVb = g.KVb;
+  float* sc = dsm;
+  float* qcs = sc + CR * KVb;
+  int* hist = reinterpret_cast<int*>(qcs + CR * HD);
+  const int nrb = (g.Qb + CR - 1) / CR;
+  int id = blockIdx.x;
+  const int rb = id % nrb;
+  id /= nrb;
+  const int h = id % g.Hq, b = id / g.Hq;
+  const int hk = h / g.group;
+  const int i0 = rb * CR, nr = min(CR, g.Qb - i0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int t = tid; t < CR * HD; t += 256) {
+    const int r = t / HD, d = t % HD;
+    qcs[t] = r < nr ? a.qc[g.pq(b, h, i0 + r) + d] : 0.f;
+  }
+  __syncthreads();
+  // scores: one KV tile per thread at a time
+  for (int j = tid; j < KVb; j += 256) {
+    const bool valid = g.kv_val(b, j) > 0;
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    if (valid) {
+      const float4* kp = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j));
+      for (int d4 = 0; d4 < HD / 4; ++d4) {
+        const float4 kv = kp[d4];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (r < CR) {
+            const float4 qv = *reinterpret_cast<const float4*>(qcs + r * HD + 4 * d4);
+            acc[r] = __builtin_fmaf(qv.x, kv.x, acc[r]);
+            acc[r] = __builtin_fmaf(qv.y, kv.y, acc[r]);
+            acc[r] = __builtin_fmaf(qv.z, kv.z, acc[r]);
+            acc[r] = __builtin_fmaf(qv.w, kv.w, acc[r]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r < CR) sc[r * KVb + j] = valid ? g.scale * acc[r] : -INFINITY;
+  }
+  __syncthreads();
+
+  if (want_topk) {
+    int* hw = hist + wave * 256;
+    for (int r = wave; r < nr; r += 4) {
+      const float* row = sc + r * KVb;
+      int nv = 0;
+      for (int j0 = 0; j0 < KVb; j0 += 64) {
+        const int j = j0 + lane;
+        nv += __popcll(__ballot(j < KVb && row[j] != -INFINITY));
+      }
+      int kk = min(a.topk, nv);
+      uint32_t prefix = 0, pmask = 0;
+      if (kk > 0) {
+        for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) hw[lane * 4 + u] = 0;
+          __builtin_amdgcn_wave_barrier();
+          for (int j = lane; j < KVb; j += 64) {
+            const float f = row[j];
+            if (f == -INFINITY) continue;
+            const uint32_t u = fkey(f);
+            if ((u & pmask) == prefix) atomicAdd(&hw[(u >> shift) & 255u], 1);
+          }
+          __builtin_amdgcn_wave_barrier();
+          // lane L owns bins 255-4L .. 252-4L (descending digit order)
+          int cnt[4], tot = 0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            cnt[u] = hw[255 - 4 * lane - u];
+            tot += cnt[u];
+          }
+          int incl = tot;  // inclusive prefix over lanes
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
+          }
+          const unsigned long long hit = __ballot(incl >= kk);
+          const int L = __ffsll((long long)hit) - 1;
+          int above = __shfl(incl - tot, L, 64);  // elements in bins above lane L's
+          int digit = 0;
+          if (lane == L) {
+            int acc = above;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              if (acc + cnt[u] >= kk) {
+                digit = 255 - 4 * lane - u;
+                above = acc;
+                break;
+              }
+              acc += cnt[u];
+            }
+          }
+          digit = __shfl(digit, L, 64);
+          above = __shfl(above, L, 64);
+          kk -= above;
+          prefix |= (uint32_t)digit << shift;
+          pmask |= 0xffu << shift;
+          __builtin_amdgcn_wave_barrier();
+        }
+      }
+      // select: keys above the threshold, plus the first kk keys equal to it
+      uint8_t* mrow = a.map + (((long long)b * g.Hq + h) * g.Qb + i0 + r) * KVb;
+      int taken_eq = 0;
+      const unsigned long long below = (1ull << lane) - 1ull;
+      for (int j0 = 0; j0 < KVb; j0 += 64) {
+        const int j = j0 + lane;
+        const float f = j < KVb ? row[j] : -INFINITY;
+        const bool valid = f != -INFINITY && a.topk > 0 && nv > 0;
+        const uint32_t u = valid ? fkey(f) : 0u;
+        const bool eq = valid && u == prefix;
+        const unsigned long long be = __ballot(eq);
+        const int rank = taken_eq + __popcll(be & below);
+        const bool sel = valid && (u > prefix || (eq && rank < kk));
+        if (j < KVb) mrow[j] = sel ? 1 : 0;
+        taken_eq += __popcll(be);
+      }
+    }
+  }
+
+  if (want_gate) {
+    __syncthreads();
+    // row softmax in place, lse_c
+    for (int r = wave; r < nr; r += 4) {
+      float* row = sc + r * KVb;
+      float m = -INFINITY;
+      for (int j = lane; j < KVb; j += 64) m = fmaxf(m, row[j]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      float l = 0.f;
+      if (m != -INFINITY)
+        for (int j = lane; j < KVb; j += 64) l += __expf(row[j] - m);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      for (int j = lane; j < KVb; j += 64) row[j] = m == -INFINITY ? 0.f : __expf(row[j] - m) * inv;
+      if (lane == 0) a.lse_c[((long long)b * g.Hq + h) * g.Qb + i0 + r] = l > 0.f ? m + __logf(l) : -INFINITY;
+    }
+    __syncthreads();
+    // O_c[r][d] = sum_j P[r][j] V_c[j][d]
+    const int d = tid & (HD - 1), half = tid >> 7;
+    float acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+    const float* vcb = a.vc + g.pk(b, hk, 0) + d;
+    for (int j = 0; j < KVb; ++j) {
+      const float v = vcb[(long long)j * HD];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = half * 8 + u;
+        if (r < CR) acc[u] = __builtin_fmaf(sc[r * KVb + j], v, acc[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = half * 8 + u;
+      if (r < nr) a.oc[g.pq(b, h, i0 + r) + d] = acc[u];
+    }
+  }
+}
+
+// Coarse backward, row form: P_c, dS_c for CR2 rows (kept in workspace for the
+// column pass) and dQ_c = scale dS_c K_c.
+constexpr int CR2 = 8;
+__global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a) {
+  extern __shared__ float dsm[];
+  const Geom& g = a.g;
+  const int KVb = g.KVb;
+  float* P = dsm;                 // [CR2][KVb]
+  float* dS = P + CR2 * KVb;      // [CR2][KVb]
+  float* qcs = dS + CR2 * KVb;    // [CR2][HD]
+  float* dos = qcs + CR2 * HD;    // [CR2][HD]
+  float* lsc = dos + CR2 * HD;    // [CR2]
+  const int nrb = (g.Qb + CR2 - 1) / CR2;
+  int id = blockIdx.x;
+  const int rb = id % nrb;
+  id /= nrb;
+  const int h = id % g.Hq, b = id / g.Hq;
+  const int hk = h / g.group;
+  const int i0 = rb * CR2, nr = min(CR2, g.Qb - i0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int t = tid; t < CR2 * HD; t += 256) {
+    const int r = t / HD, d = t % HD;
+    qcs[t] = r < nr ? a.qc[g.pq(b, h, i0 + r) + d] : 0.f;
+    dos[t] = r < nr ? a.doc[g.pq(b, h, i0 + r) + d] : 0.f;
+  }
+  if (tid < CR2) lsc[tid] = tid < nr ? a.lse_c[((long long)b * g.Hq + h) * g.Qb + i0 + tid] : -INFINITY;
+  __syncthreads();
+  for (int j = tid; j < KVb; j += 256) {
+    const bool valid = g.kv_val(b, j) > 0;
+    float cs[CR2], dp[CR2];
+#pragma unroll
+    for (int r = 0; r < CR2; ++r) cs[r] = dp[r] = 0.f;
+    if (valid) {
+      const float4* kp = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j));
+      const float4* vp = reinterpret_cast<const float4*>(a.vc + g.pk(b, hk, j));
+      for (int d4 = 0; d4 < HD / 4; ++d4) {
+        const float4 kv = kp[d4], vv = vp[d4];
+#pragma unroll
+        for (int r = 0; r < CR2; ++r) {
+          const float4 qv = *reinterpret_cast<const float4*>(qcs + r * HD + 4 * d4);
+          const float4 ov = *reinterpret_cast<const float4*>(dos + r * HD + 4 * d4);
+          cs[r] += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
+          dp[r] += ov.x * vv.x + ov.y * vv.y + ov.z * vv.z + ov.w * vv.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < CR2; ++r) {
+      const float p = (valid && lsc[r] != -INFINITY) ? __expf(g.scale * cs[r] - lsc[r]) : 0.f;
+      P[r * KVb + j] = p;
+      dS[r * KVb + j] = p == 0.f ? 0.f : dp[r];
+    }
+  }
+  __syncthreads();
+  for (int r = wave; r < nr; r += 4) {
+    float s = 0.f;
+    for (int j = lane; j < KVb; j += 64) s += P[r * KVb + j] * dS[r * KVb + j];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    const long long ro = (((long long)b * g.Hq + h) * g.Qb + i0 + r) * KVb;
+    for (int j = lane; j < KVb; j += 64) {
+      const float p = P[r * KVb + j];
+      const float ds = p * (dS[r * KVb + j] - s);
+      dS[r * KVb + j] = ds;
+      a.dss[ro + j] = ds;
+      a.ps[ro + j] = p;
+    }
+  }
+  __syncthreads();
+  const int d = tid & (HD - 1), half = tid >> 7;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* kcb = a.kc + g.pk(b, hk, 0) + d;
+  for (int j = 0; j < KVb; ++j) {
+    const float kv = kcb[(long long)j * HD];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = __builtin_fmaf(dS[(half * 4 + u) * KVb + j], kv, acc[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = half * 4 + u;
+    if (r < nr) a.dqc[g.pq(b, h, i0 + r) + d] = g.scale * acc[u];
+  }
+}
+
+// Coarse backward, column form: dK_c = scale sum dS_c^T Q_c, dV_c = sum P_c^T dO_c
+// over the Q heads of the group (16 KV tiles per work-group, thread = (d, 8 tiles)).
+constexpr int CC = 16;
+__global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(const CoarseArgs a) {
+  const Geom& g = a.g;
+  const int KVb = g.KVb;
+  const int ncb = (KVb + CC - 1) / CC;
+  int id = blockIdx.x;
+  const int cb = id % ncb;
+  id /= ncb;
+  const int hk = id % g.Hkv, b = id / g.Hkv;
+  const int tid = threadIdx.x, d = tid & (HD - 1), half = tid >> 7;
+  const int j0 = cb * CC + half * 8;
+  float dk[8], dv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) dk[u] = dv[u] = 0.f;
+  for (int hh = 0; hh < g.group; ++hh) {
+    const int h = hk * g.group + hh;
+    for (int i = 0; i < g.Qb; ++i) {
+      const float q = a.qc[g.pq(b, h, i) + d];
+      const float o = a.doc[g.pq(b, h, i) + d];
+      const long long ro = (((long long)b * g.Hq + h) * g.Qb + i) * KVb;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < KVb) {
+          dk[u] = __builtin_fmaf(a.dss[ro + j0 + u], q, dk[u]);
+          dv[u] = __builtin_fmaf(a.ps[ro + j0 + u], o, dv[u]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (j0 + u < KVb) {
+      a.dkc[g.pk(b, hk, j0 + u) + d] = g.scale * dk[u];
+      a.dvc[g.pk(b, hk, j0 + u) + d] = dv[u];
+    }
+}
+
+__global__ void zero_kernel(uint8_t* p, size_t n) {
+  const size_t n16 = n / 16;
+  uint4* p16 = reinterpret_cast<uint4*>(p);
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < n16;
+       t += (size_t)gridDim.x * blockDim.x)
+    p16[t] = make_uint4(0, 0, 0, 0);
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n - n16 * 16) p[n16 * 16 + t] = 0;
+}
+
+}  // namespace
+
+int coarse_rows_per_block(int KVb) {
+  // scores [CR][KVb] + qc [CR][HD] + 4 histograms must fit in 160 KiB
+  const long long budget = 160 * 1024 - 4 * 256 * 4;
+  int cr = 16;
+  while (cr > 1 && (long long)cr * (KVb + HD) * 4 > budget) cr >>= 1;
+  return cr;
+}
+
+hipError_t launch_pool(const Geom& g, int dtype, const void* q, const void* k, const void* v,
+                       float* qc, float* kc, float* vc, hipStream_t st) {
+  const unsigned nq = (unsigned)((long long)g.B * g.Hq * g.Qb);
+  const unsigned nk = (unsigned)((long long)g.B * g.Hkv * g.KVb);
+  auto go = [&](auto tag) {
+    using ET = decltype(tag);
+    if (nq) pool_kernel<ET><<<nq, 256, 0, st>>>(g, (const uint16_t*)q, 1, qc);
+    if (nk) {
+      pool_kernel<ET><<<nk, 256, 0, st>>>(g, (const uint16_t*)k, 0, kc);
+      pool_kernel<ET><<<nk, 256, 0, st>>>(g, (const uint16_t*)v, 0, vc);
+    }
+  };
+  if (dtype == VSA_BF16) go(bf16_tag{});
+  else go(f16_tag{});
+  return hipGetLastError();
+}
+
+hipError_t launch_coarse_fwd(const CoarseArgs& a, bool want_topk, bool want_gate, hipStream_t st) {
+  const Geom& g = a.g;
+  const int cr = coarse_rows_per_block(g.KVb);
+  const long long n = (long long)g.B * g.Hq * ((g.Qb + cr - 1) / cr);
+  if (n == 0) return hipSuccess;
+  const size_t lds = ((size_t)cr * (g.KVb + HD) + 4 * 256) * 4;
+  coarse_fwd_kernel<<<(unsigned)n, 256, lds, st>>>(a, cr, want_topk ? 1 : 0, want_gate ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_coarse_bwd(const CoarseArgs& a, hipStream_t st) {
+  const Geom& g = a.g;
+  const long long nr = (long long)g.B * g.Hq * ((g.Qb + CR2 - 1) / CR2);
+  const long long nc = (long long)g.B * g.Hkv * ((g.KVb + CC - 1) / CC);
+  if (nr == 0 || nc == 0) return hipSuccess;
+  const size_t lds = ((size_t)2 * CR2 * g.KVb + 2 * CR2 * HD + CR2) * 4;
+  coarse_bwd_rows_kernel<<<(unsigned)nr, 256, lds, st>>>(a);
+  coarse_bwd_cols_kernel<<<(unsigned)nc, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
+  if (bytes == 0) return hipSuccess;
+  const size_t n16 = bytes / 16;
+  unsigned grid = (unsigned)std::min<size_t>((n16 + 255) / 256 + 1, 65536);
+  zero_kernel<<<grid, 256, 0, st>>>((uint8_t*)p, bytes);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

@@ -1,0 +1,147 @@
+// Block map -> CSR index of the live (Q block, KV block) pairs.
+//
+// FastVideo block_sparse_attn_cute_fwd.py: `_map_to_index` turns the boolean
+// map into per-row block lists, `_build_sparse_tensors` drops KV tiles with no
+// valid token and builds the backward's KV-owned lists from the transposed map.
+// Here both directions are CSR (nnz-sized instead of dense [.., KVb, Qb]):
+// count -> exclusive scan -> fill, all deterministic, columns ascending.
+#include "kernels.hpp"
+
+namespace vsa {
+
+// Q-owned count: one wave per row (b, h, i); lanes read 64 consecutive map
+// bytes per step and a ballot counts the live ones.
+__global__ __launch_bounds__(256) void index_count_q(Geom g, const uint8_t* __restrict__ map,
+                                                     int32_t* __restrict__ row_ptr) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long rows = (long long)g.B * g.Hq * g.Qb;
+  if (row >= rows) return;
+  const int i = (int)(row % g.Qb);
+  const long long bh = row / g.Qb;
+  const int h = (int)(bh % g.Hq), b = (int)(bh / g.Hq);
+  const uint8_t* m = map + b * g.map_bstride + ((long long)h * g.Qb + i) * g.KVb;
+  const bool qok = i < g.nqb(b);
+  const int nk = g.nkb(b);
+  int cnt = 0;
+  for (int j0 = 0; j0 < g.KVb; j0 += 64) {
+    const int j = j0 + lane;
+    const bool live = qok && j < nk && m[j] != 0 && g.kv_val(b, j) > 0;
+    cnt += __popcll(__ballot(live));
+  }
+  if (lane == 0) row_ptr[row + 1] = cnt;
+}
+
+// Q-owned fill: same walk, each live entry written at its rank in the row.
+__global__ __launch_bounds__(256) void index_fill_q(Geom g, const uint8_t* __restrict__ map,
+                                                    const int32_t* __restrict__ row_ptr,
+                                                    int32_t* __restrict__ col, long long cap) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long rows = (long long)g.B * g.Hq * g.Qb;
+  if (row >= rows) return;
+  const int i = (int)(row % g.Qb);
+  const long long bh = row / g.Qb;
+  const int h = (int)(bh % g.Hq), b = (int)(bh / g.Hq);
+  const uint8_t* m = map + b * g.map_bstride + ((long long)h * g.Qb + i) * g.KVb;
+  const bool qok = i < g.nqb(b);
+  const int nk = g.nkb(b);
+  long long pos = row_ptr[row];
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int j0 = 0; j0 < g.KVb; j0 += 64) {
+    const int j = j0 + lane;
+    const bool live = qok && j < nk && m[j] != 0 && g.kv_val(b, j) > 0;
+    const unsigned long long bal = __ballot(live);
+    const long long at = pos + __popcll(bal & below);
+    if (live && at < cap) col[at] = j;
+    pos += __popcll(bal);
+  }
+}
+
+// KV-owned count / fill: one thread per column (b, h, j), walking i; lanes of a
+// wave read consecutive bytes of one map row per step.
+__global__ __launch_bounds__(256) void index_count_kv(Geom g, const uint8_t* __restrict__ map,
+                                                      int32_t* __restrict__ row_ptr) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long rows = (long long)g.B * g.Hq * g.KVb;
+  if (t >= rows) return;
+  const int j = (int)(t % g.KVb);
+  const long long bh = t / g.KVb;
+  const int h = (int)(bh % g.Hq), b = (int)(bh / g.Hq);
+  int cnt = 0;
+  if (j < g.nkb(b) && g.kv_val(b, j) > 0) {
+    const uint8_t* m = map + b * g.map_bstride + (long long)h * g.Qb * g.KVb + j;
+    const int nq = g.nqb(b);
+    for (int i = 0; i < nq; ++i) cnt += m[(long long)i * g.KVb] != 0;
+  }
+  row_ptr[t + 1] = cnt;
+}
+
+__global__ __launch_bounds__(256) void index_fill_kv(Geom g, const uint8_t* __restrict__ map,
+                                                     const int32_t* __restrict__ row_ptr,
+                                                     int32_t* __restrict__ col, long long cap) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long rows = (long long)g.B * g.Hq * g.KVb;
+  if (t >= rows) return;
+  const int j = (int)(t % g.KVb);
+  const long long bh = t / g.KVb;
+  const int h = (int)(bh % g.Hq), b = (int)(bh / g.Hq);
+  if (j >= g.nkb(b) || g.kv_val(b, j) == 0) return;
+  const uint8_t* m = map + b * g.map_bstride + (long long)h * g.Qb * g.KVb + j;
+  const int nq = g.nqb(b);
+  long long pos = row_ptr[t];
+  for (int i = 0; i < nq; ++i)
+    if (m[(long long)i * g.KVb] != 0) {
+      if (pos < cap) col[pos] = i;
+      ++pos;
+    }
+}
+
+// In-place exclusive scan of the counts row_ptr[1..rows] by one work-group:
+// every thread sums a contiguous segment, the segment sums are scanned in LDS,
+// then each thread rewrites its segment.
+__global__ __launch_bounds__(1024) void index_scan(int32_t* __restrict__ row_ptr, long long rows) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const long long per = (rows + 1023) / 1024;
+  const long long beg = t * per, end = min(beg + per, rows);
+  int32_t s = 0;
+  for (long long r = beg; r < end; ++r) s += row_ptr[r + 1];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int32_t acc = part[t] - s;  // exclusive prefix of this segment
+  for (long long r = beg; r < end; ++r) {
+    acc += row_ptr[r + 1];
+    row_ptr[r + 1] = acc;
+  }
+  if (t == 0) row_ptr[0] = 0;
+}
+
+hipError_t launch_index(const Geom& g, const uint8_t* map, int kv_owned, int32_t* row_ptr,
+                        int32_t* col, long long cap, hipStream_t st) {
+  const long long rows = (long long)g.B * g.Hq * (kv_owned ? g.KVb : g.Qb);
+  if (rows == 0) {  // only row_ptr[0] = 0
+    index_scan<<<1, 1024, 0, st>>>(row_ptr, 0);
+    return hipGetLastError();
+  }
+  if (!kv_owned) {
+    const unsigned grid = (unsigned)((rows + 3) / 4);
+    index_count_q<<<grid, 256, 0, st>>>(g, map, row_ptr);
+    index_scan<<<1, 1024, 0, st>>>(row_ptr, rows);
+    index_fill_q<<<grid, 256, 0, st>>>(g, map, row_ptr, col, cap);
+  } else {
+    const unsigned grid = (unsigned)((rows + 255) / 256);
+    index_count_kv<<<grid, 256, 0, st>>>(g, map, row_ptr);
+    index_scan<<<1, 1024, 0, st>>>(row_ptr, rows);
+    index_fill_kv<<<grid, 256, 0, st>>>(g, map, row_ptr, col, cap);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vsa

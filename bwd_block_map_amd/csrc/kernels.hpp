@@ -1,0 +1,87 @@
+// Launch interface of the gfx950 kernels (called by the C ABI in vsa_api.cpp).
+#pragma once
+
+#include "common.hpp"
+
+namespace vsa {
+
+// Sparse-branch forward (plus the gate composition in its epilogue).
+struct FwdArgs {
+  Geom g;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* gate;  // gate_mode != NONE
+  const float* oc;       // pooled coarse output [B,Hq,Qb,HD] (gate only)
+  int gate_mode;
+  uint16_t* out;
+  uint16_t* osel;  // un-gated sparse output (gate + training), else null
+  float* lse;
+  const int32_t* row_ptr;  // Q-owned CSR
+  const int32_t* col;
+};
+
+// Backward of the sparse branch.
+struct BwdArgs {
+  Geom g;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;
+  const float* dr;         // rowsum(dO * O_sel), laid out like lse
+  const int32_t* row_ptr;  // Q-owned (dQ) or KV-owned (dK/dV) CSR
+  const int32_t* col;
+  const float* dqc;  // gate: pooled-tile gradients added to valid slots, else null
+  const float* dkc;
+  const float* dvc;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+};
+
+// Row term and gate-side reductions of the backward.
+struct PreArgs {
+  Geom g;
+  const uint16_t* dout;
+  const uint16_t* osel;  // sparse-branch output
+  const uint16_t* gate;
+  const float* oc;
+  int gate_mode;
+  float* dr;
+  float* doc;       // gate: [B,Hq,Qb,HD] sum over the tile of gate * dO
+  uint16_t* dgate;  // gate: optional
+};
+
+// Pooled tiles, coarse scores, top-k and coarse attention.
+struct CoarseArgs {
+  Geom g;
+  const float* qc;  // [B,Hq,Qb,HD]
+  const float* kc;  // [B,Hkv,KVb,HD]
+  const float* vc;
+  int topk;
+  uint8_t* map;   // topk > 0: [B,Hq,Qb,KVb]
+  float* oc;      // gate: [B,Hq,Qb,HD]
+  float* lse_c;   // gate: [B,Hq,Qb]
+  // backward
+  const float* doc;
+  float* ps;      // workspace [B,Hq,Qb,KVb]: P_c
+  float* dss;     // workspace [B,Hq,Qb,KVb]: dS_c
+  float* dqc;
+  float* dkc;
+  float* dvc;
+};
+
+hipError_t launch_index(const Geom& g, const uint8_t* map, int kv_owned, int32_t* row_ptr,
+                        int32_t* col, long long cap, hipStream_t st);
+hipError_t launch_pool(const Geom& g, int dtype, const void* q, const void* k, const void* v,
+                       float* qc, float* kc, float* vc, hipStream_t st);
+hipError_t launch_coarse_fwd(const CoarseArgs& a, bool want_topk, bool want_gate, hipStream_t st);
+hipError_t launch_coarse_bwd(const CoarseArgs& a, hipStream_t st);
+hipError_t launch_sparse_fwd(const FwdArgs& a, int dtype, hipStream_t st);
+hipError_t launch_bwd_pre(const PreArgs& a, int dtype, hipStream_t st);
+hipError_t launch_sparse_dkdv(const BwdArgs& a, int dtype, hipStream_t st);
+hipError_t launch_sparse_dq(const BwdArgs& a, int dtype, hipStream_t st);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace vsa

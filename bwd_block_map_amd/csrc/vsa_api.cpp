@@ -1,0 +1,467 @@
+// C ABI of the block-sparse attention library: argument checks, buffer sizes,
+// workspace / saved-state carving and the launch sequence of vsa_fwd / vsa_bwd.
+// Declarations and argument contracts: include/vsa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace vsa {
+int coarse_rows_per_block(int KVb);
+}
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return VSA_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(VSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Sub-buffers of one caller buffer, each 256-byte aligned. With base == nullptr
+// it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(long long count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += (size_t)count * sizeof(T);
+    return p;
+  }
+};
+
+bool is_video(const vsa_problem* p) { return p->topk > 0 || p->gate_mode != VSA_GATE_NONE; }
+
+long long nnz_cap(const vsa_problem* p) {
+  const long long per = p->topk > 0 ? std::min<long long>(p->topk, p->KVb) : p->KVb;
+  return (long long)p->B * p->Hq * p->Qb * per;
+}
+
+long long q_elems(const vsa_problem* p) {
+  return p->layout == VSA_TND ? (long long)p->Sq * p->Hq * p->D
+                              : (long long)p->B * p->Sq * p->Hq * p->D;
+}
+
+long long rows_total(const vsa_problem* p) {
+  return p->layout == VSA_TND ? (long long)p->Hq * p->Sq : (long long)p->B * p->Hq * p->Sq;
+}
+
+// Pieces of the saved state (training forward -> backward).
+struct Saved {
+  int32_t* q_rp;
+  int32_t* q_col;
+  int32_t* kv_rp;
+  int32_t* kv_col;
+  float* qc;
+  float* kc;
+  float* vc;
+  float* oc;
+  float* lse_c;
+  uint16_t* osel;
+};
+
+Saved carve_saved(const vsa_problem* p, void* base, size_t* bytes) {
+  Carver c(base);
+  Saved s{};
+  const long long cap = nnz_cap(p);
+  s.q_rp = c.take<int32_t>((long long)p->B * p->Hq * p->Qb + 1);
+  s.q_col = c.take<int32_t>(std::max(cap, 1LL));
+  s.kv_rp = c.take<int32_t>((long long)p->B * p->Hq * p->KVb + 1);
+  s.kv_col = c.take<int32_t>(std::max(cap, 1LL));
+  if (p->gate_mode != VSA_GATE_NONE) {
+    s.qc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
+    s.kc = c.take<float>((long long)p->B * p->Hkv * p->KVb * p->D);
+    s.vc = c.take<float>((long long)p->B * p->Hkv * p->KVb * p->D);
+    s.oc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
+    s.lse_c = c.take<float>((long long)p->B * p->Hq * p->Qb);
+    s.osel = c.take<uint16_t>(q_elems(p));
+  }
+  if (bytes) *bytes = c.off;
+  return s;
+}
+
+// Forward workspace: the inference-mode index and coarse state, the pooled
+// tiles and the selection map of the top-k path.
+struct FwdWs {
+  int32_t* q_rp;
+  int32_t* q_col;
+  float* qc;
+  float* kc;
+  float* vc;
+  float* oc;
+  float* lse_c;
+  uint8_t* map;
+};
+
+FwdWs carve_fwd(const vsa_problem* p, void* base, size_t* bytes) {
+  Carver c(base);
+  FwdWs w{};
+  const long long cap = nnz_cap(p);
+  w.q_rp = c.take<int32_t>((long long)p->B * p->Hq * p->Qb + 1);
+  w.q_col = c.take<int32_t>(std::max(cap, 1LL));
+  if (is_video(p)) {
+    w.qc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
+    w.kc = c.take<float>((long long)p->B * p->Hkv * p->KVb * p->D);
+    w.vc = c.take<float>((long long)p->B * p->Hkv * p->KVb * p->D);
+  }
+  if (p->gate_mode != VSA_GATE_NONE) {
+    w.oc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
+    w.lse_c = c.take<float>((long long)p->B * p->Hq * p->Qb);
+  }
+  if (p->topk > 0) w.map = c.take<uint8_t>((long long)p->B * p->Hq * p->Qb * p->KVb);
+  if (bytes) *bytes = c.off;
+  return w;
+}
+
+struct BwdWs {
+  float* dr;
+  float* doc;
+  float* dqc;
+  float* dkc;
+  float* dvc;
+  float* ps;
+  float* dss;
+};
+
+BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
+  Carver c(base);
+  BwdWs w{};
+  w.dr = c.take<float>(std::max(rows_total(p), 1LL));
+  if (p->gate_mode != VSA_GATE_NONE) {
+    w.doc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
+    w.dqc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
+    w.dkc = c.take<float>((long long)p->B * p->Hkv * p->KVb * p->D);
+    w.dvc = c.take<float>((long long)p->B * p->Hkv * p->KVb * p->D);
+    w.ps = c.take<float>((long long)p->B * p->Hq * p->Qb * p->KVb);
+    w.dss = c.take<float>((long long)p->B * p->Hq * p->Qb * p->KVb);
+  }
+  if (bytes) *bytes = c.off;
+  return w;
+}
+
+vsa::Geom make_geom(const vsa_problem* p) {
+  vsa::Geom g;
+  g.layout = p->layout;
+  g.B = p->B;
+  g.Hq = p->Hq;
+  g.Hkv = p->Hkv;
+  g.Sq = p->Sq;
+  g.Skv = p->Skv;
+  g.q_block = p->q_block;
+  g.kv_block = p->kv_block;
+  g.Qb = p->Qb;
+  g.KVb = p->KVb;
+  g.group = p->Hq / p->Hkv;
+  g.q_valid = p->q_valid;
+  g.kv_valid = p->kv_valid;
+  g.cu_q = p->cu_seqlens_q;
+  g.cu_kv = p->cu_seqlens_kv;
+  g.scale = p->scale;
+  g.map_bstride = p->map_batch_stride;
+  return g;
+}
+
+int validate(const vsa_problem* p) {
+  if (!p) return fail(VSA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->abi_version != VSA_ABI_VERSION)
+    return fail(VSA_ERR_INVALID_ARG, "abi_version %d, library has %d", p->abi_version,
+                VSA_ABI_VERSION);
+  if (p->dtype != VSA_BF16 && p->dtype != VSA_FP16)
+    return fail(VSA_ERR_INVALID_ARG, "dtype must be VSA_BF16 or VSA_FP16");
+  if (p->layout != VSA_BHSD && p->layout != VSA_BSHD && p->layout != VSA_TND)
+    return fail(VSA_ERR_INVALID_ARG, "layout must be BHSD, BSHD or TND");
+  if (p->B < 1 || p->Hq < 1 || p->Hkv < 1)
+    return fail(VSA_ERR_INVALID_ARG, "B, Hq and Hkv must be positive (B=%d Hq=%d Hkv=%d)", p->B,
+                p->Hq, p->Hkv);
+  if (p->Hq % p->Hkv != 0)
+    return fail(VSA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->D < 1) return fail(VSA_ERR_INVALID_ARG, "D must be positive");
+  if (p->D != vsa::HD) return fail(VSA_ERR_UNSUPPORTED, "head dimension %d: this build has D=128", p->D);
+  if (p->q_block < 1 || p->kv_block < 1)
+    return fail(VSA_ERR_INVALID_ARG, "q_block and kv_block must be positive");
+  if (p->q_block % 32 != 0 || p->kv_block % 64 != 0)
+    return fail(VSA_ERR_UNSUPPORTED, "q_block must be a multiple of 32 and kv_block of 64 (got %d, %d)",
+                p->q_block, p->kv_block);
+  if (p->Sq < 0 || p->Skv < 0) return fail(VSA_ERR_INVALID_ARG, "Sq and Skv must be >= 0");
+  if (!(p->scale > 0.f) || !std::isfinite(p->scale))
+    return fail(VSA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (p->topk < 0) return fail(VSA_ERR_INVALID_ARG, "topk must be >= 0");
+  if (p->gate_mode < VSA_GATE_NONE || p->gate_mode > VSA_GATE_PER_ELEMENT)
+    return fail(VSA_ERR_INVALID_ARG, "gate_mode must be NONE, PER_TOKEN or PER_ELEMENT");
+  if (p->map_batch_stride < 0) return fail(VSA_ERR_INVALID_ARG, "map_batch_stride must be >= 0");
+  if (p->layout == VSA_TND) {
+    if (!p->cu_seqlens_q) return fail(VSA_ERR_INVALID_ARG, "actual_seq_lengths must be specified");
+    if (!p->cu_seqlens_kv)
+      return fail(VSA_ERR_INVALID_ARG, "actual_seq_lengths_kv must be specified");
+    if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0)
+      return fail(VSA_ERR_INVALID_ARG, "max_seqlen_q / max_seqlen_kv must be >= 0");
+    if (p->Qb != ceil_div(p->max_seqlen_q, p->q_block) || p->KVb != ceil_div(p->max_seqlen_kv, p->kv_block))
+      return fail(VSA_ERR_INVALID_ARG,
+                  "Qb/KVb must be ceil(max_seqlen/block): got %d/%d, want %lld/%lld", p->Qb, p->KVb,
+                  ceil_div(p->max_seqlen_q, p->q_block), ceil_div(p->max_seqlen_kv, p->kv_block));
+    if (p->topk > 0 || p->gate_mode != VSA_GATE_NONE)
+      return fail(VSA_ERR_UNSUPPORTED, "top-k selection and the compression gate need BHSD or BSHD");
+    if (p->q_valid || p->kv_valid)
+      return fail(VSA_ERR_INVALID_ARG, "TND derives valid counts from the sequence lengths");
+  } else {
+    if (p->Qb != ceil_div(p->Sq, p->q_block) || p->KVb != ceil_div(p->Skv, p->kv_block))
+      return fail(VSA_ERR_INVALID_ARG, "Qb/KVb must be ceil(S/block): got %d/%d, want %lld/%lld",
+                  p->Qb, p->KVb, ceil_div(p->Sq, p->q_block), ceil_div(p->Skv, p->kv_block));
+  }
+  if ((long long)p->B * p->Hq * p->Qb * std::max(p->KVb, 1) >= (1LL << 31))
+    return fail(VSA_ERR_UNSUPPORTED, "B*Hq*Qb*KVb must stay below 2^31");
+  if (rows_total(p) >= (1LL << 31)) return fail(VSA_ERR_UNSUPPORTED, "B*Hq*Sq must stay below 2^31");
+  if (is_video(p) && vsa::coarse_rows_per_block(p->KVb) < 1)
+    return fail(VSA_ERR_UNSUPPORTED, "KVb %d too large for the coarse kernels", p->KVb);
+  if (p->gate_mode != VSA_GATE_NONE && ((size_t)2 * 8 * p->KVb + 2 * 8 * 128 + 8) * 4 > 160 * 1024)
+    return fail(VSA_ERR_UNSUPPORTED, "KVb %d too large for the compression backward", p->KVb);
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa_last_error(void) { return g_err.c_str(); }
+
+int vsa_abi_version(void) { return VSA_ABI_VERSION; }
+
+int vsa_validate(const vsa_problem* p) {
+  const int rc = validate(p);
+  return rc == VSA_OK ? ok() : rc;
+}
+
+int vsa_sizes(const vsa_problem* p, size_t* ws_fwd, size_t* ws_bwd, size_t* saved_bytes,
+              int64_t* nnz_capacity) {
+  const int rc = validate(p);
+  if (rc != VSA_OK) return rc;
+  size_t f = 0, b = 0, s = 0;
+  carve_fwd(p, nullptr, &f);
+  carve_bwd(p, nullptr, &b);
+  carve_saved(p, nullptr, &s);
+  if (ws_fwd) *ws_fwd = f;
+  if (ws_bwd) *ws_bwd = b;
+  if (saved_bytes) *saved_bytes = s;
+  if (nnz_capacity) *nnz_capacity = nnz_cap(p);
+  return ok();
+}
+
+int block_map_to_index(const vsa_problem* p, const uint8_t* block_map, int kv_owned,
+                       int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, void* ws,
+                       size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const int rc = validate(p);
+  if (rc != VSA_OK) return rc;
+  if (!block_map) return fail(VSA_ERR_INVALID_ARG, "block_map must be a device tensor (got NULL)");
+  if (!row_ptr || (!col_idx && col_capacity > 0))
+    return fail(VSA_ERR_INVALID_ARG, "row_ptr / col_idx must be device buffers");
+  if (col_capacity < 0) return fail(VSA_ERR_INVALID_ARG, "col_capacity must be >= 0");
+  const vsa::Geom g = make_geom(p);
+  hipError_t e = vsa::launch_index(g, block_map, kv_owned ? 1 : 0, row_ptr, col_idx, col_capacity,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "block_map_to_index");
+  return ok();
+}
+
+int vsa_fwd(const vsa_problem* p, const void* q, const void* k, const void* v, uint8_t* block_map,
+            const void* gate, void* out, float* lse, void* saved, size_t saved_bytes, void* ws,
+            size_t ws_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc != VSA_OK) return rc;
+  if (!q || !k || !v || !out || !lse)
+    return fail(VSA_ERR_INVALID_ARG, "q, k, v, out and lse must be device buffers");
+  if (p->topk == 0 && !block_map)
+    return fail(VSA_ERR_INVALID_ARG, "block_map must be given when topk == 0");
+  if (p->topk > 0 && block_map && p->map_batch_stride != (long long)p->Hq * p->Qb * p->KVb &&
+      !(p->map_batch_stride == 0 && p->B == 1))
+    return fail(VSA_ERR_INVALID_ARG, "an output block_map must be a dense [B,Hq,Qb,KVb] buffer");
+  if (p->gate_mode != VSA_GATE_NONE && !gate)
+    return fail(VSA_ERR_INVALID_ARG, "gate must be given when gate_mode != NONE");
+  size_t need_ws = 0, need_saved = 0;
+  carve_fwd(p, nullptr, &need_ws);
+  carve_saved(p, nullptr, &need_saved);
+  if (ws_bytes < need_ws || (!ws && need_ws))
+    return fail(VSA_ERR_WORKSPACE, "forward workspace: %zu bytes needed, %zu given", need_ws, ws_bytes);
+  if (saved && saved_bytes < need_saved)
+    return fail(VSA_ERR_WORKSPACE, "saved state: %zu bytes needed, %zu given", need_saved,
+                saved_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  const FwdWs w = carve_fwd(p, ws, nullptr);
+  const Saved s = saved ? carve_saved(p, saved, nullptr) : Saved{};
+  vsa::Geom g = make_geom(p);
+  hipError_t e = hipSuccess;
+  const long long cap = nnz_cap(p);
+
+  // pooled tiles, top-k selection and the coarse attention
+  const bool gated = p->gate_mode != VSA_GATE_NONE;
+  float* qc = (gated && saved) ? s.qc : w.qc;
+  float* kc = (gated && saved) ? s.kc : w.kc;
+  float* vc = (gated && saved) ? s.vc : w.vc;
+  float* oc = (gated && saved) ? s.oc : w.oc;
+  float* lse_c = (gated && saved) ? s.lse_c : w.lse_c;
+  const uint8_t* sel_map = block_map;
+  if (is_video(p)) {
+    e = vsa::launch_pool(g, p->dtype, q, k, v, qc, kc, vc, st);
+    if (e != hipSuccess) return hip_fail(e, "pool");
+    vsa::CoarseArgs ca{};
+    ca.g = g;
+    ca.qc = qc;
+    ca.kc = kc;
+    ca.vc = vc;
+    ca.topk = p->topk;
+    ca.map = p->topk > 0 ? (block_map ? block_map : w.map) : nullptr;
+    ca.oc = oc;
+    ca.lse_c = lse_c;
+    e = vsa::launch_coarse_fwd(ca, p->topk > 0, gated, st);
+    if (e != hipSuccess) return hip_fail(e, "coarse forward");
+    if (p->topk > 0) {
+      sel_map = ca.map;
+      g.map_bstride = (long long)p->Hq * p->Qb * p->KVb;
+    }
+  }
+  // index: Q-owned always, KV-owned only when a backward follows
+  int32_t* q_rp = saved ? s.q_rp : w.q_rp;
+  int32_t* q_col = saved ? s.q_col : w.q_col;
+  e = vsa::launch_index(g, sel_map, 0, q_rp, q_col, cap, st);
+  if (e != hipSuccess) return hip_fail(e, "index (Q-owned)");
+  if (saved) {
+    e = vsa::launch_index(g, sel_map, 1, s.kv_rp, s.kv_col, cap, st);
+    if (e != hipSuccess) return hip_fail(e, "index (KV-owned)");
+  }
+  vsa::FwdArgs fa{};
+  fa.g = g;
+  fa.q = (const uint16_t*)q;
+  fa.k = (const uint16_t*)k;
+  fa.v = (const uint16_t*)v;
+  fa.gate = (const uint16_t*)gate;
+  fa.oc = oc;
+  fa.gate_mode = p->gate_mode;
+  fa.out = (uint16_t*)out;
+  fa.osel = (gated && saved) ? s.osel : nullptr;
+  fa.lse = lse;
+  fa.row_ptr = q_rp;
+  fa.col = q_col;
+  e = vsa::launch_sparse_fwd(fa, p->dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "sparse forward");
+  return ok();
+}
+
+int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, const void* gate,
+            const void* dout, const void* out, const float* lse, const void* saved,
+            size_t saved_bytes, void* dq, void* dk, void* dv, void* dgate, void* ws,
+            size_t ws_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc != VSA_OK) return rc;
+  if (!q || !k || !v || !lse || !dq || !dk || !dv)
+    return fail(VSA_ERR_INVALID_ARG, "q, k, v, lse, dq, dk and dv must be device buffers");
+  if (!saved) return fail(VSA_ERR_INVALID_ARG, "saved must be the state of a training vsa_fwd");
+  const bool gated = p->gate_mode != VSA_GATE_NONE;
+  if (gated && !gate) return fail(VSA_ERR_INVALID_ARG, "gate must be given when gate_mode != NONE");
+  if (!gated && !out && dout) return fail(VSA_ERR_INVALID_ARG, "out must be given");
+  size_t need_ws = 0, need_saved = 0;
+  carve_bwd(p, nullptr, &need_ws);
+  carve_saved(p, nullptr, &need_saved);
+  if (saved_bytes < need_saved)
+    return fail(VSA_ERR_WORKSPACE, "saved state: %zu bytes needed, %zu given", need_saved, saved_bytes);
+  if (ws_bytes < need_ws || (!ws && need_ws))
+    return fail(VSA_ERR_WORKSPACE, "backward workspace: %zu bytes needed, %zu given", need_ws, ws_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  const long long qn = q_elems(p);
+  const long long kn = p->layout == VSA_TND ? (long long)p->Skv * p->Hkv * p->D
+                                            : (long long)p->B * p->Skv * p->Hkv * p->D;
+  hipError_t e = hipSuccess;
+  if (!dout) {  // no upstream gradient: every gradient is zero
+    e = vsa::launch_zero(dq, (size_t)qn * 2, st);
+    if (e == hipSuccess) e = vsa::launch_zero(dk, (size_t)kn * 2, st);
+    if (e == hipSuccess) e = vsa::launch_zero(dv, (size_t)kn * 2, st);
+    if (e == hipSuccess && gated && dgate)
+      e = vsa::launch_zero(dgate, (size_t)(p->gate_mode == VSA_GATE_PER_TOKEN ? qn / p->D : qn) * 2, st);
+    if (e != hipSuccess) return hip_fail(e, "zero gradients");
+    return ok();
+  }
+  const Saved s = carve_saved(p, const_cast<void*>(saved), nullptr);
+  const BwdWs w = carve_bwd(p, ws, nullptr);
+  const vsa::Geom g = make_geom(p);
+
+  vsa::PreArgs pa{};
+  pa.g = g;
+  pa.dout = (const uint16_t*)dout;
+  pa.osel = gated ? s.osel : (const uint16_t*)out;
+  pa.gate = (const uint16_t*)gate;
+  pa.oc = s.oc;
+  pa.gate_mode = p->gate_mode;
+  pa.dr = w.dr;
+  pa.doc = w.doc;
+  pa.dgate = (uint16_t*)dgate;
+  e = vsa::launch_bwd_pre(pa, p->dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "backward preprocess");
+
+  if (gated) {
+    vsa::CoarseArgs ca{};
+    ca.g = g;
+    ca.qc = s.qc;
+    ca.kc = s.kc;
+    ca.vc = s.vc;
+    ca.lse_c = s.lse_c;
+    ca.doc = w.doc;
+    ca.ps = w.ps;
+    ca.dss = w.dss;
+    ca.dqc = w.dqc;
+    ca.dkc = w.dkc;
+    ca.dvc = w.dvc;
+    e = vsa::launch_coarse_bwd(ca, st);
+    if (e != hipSuccess) return hip_fail(e, "coarse backward");
+  }
+
+  vsa::BwdArgs ba{};
+  ba.g = g;
+  ba.q = (const uint16_t*)q;
+  ba.k = (const uint16_t*)k;
+  ba.v = (const uint16_t*)v;
+  ba.dout = (const uint16_t*)dout;
+  ba.lse = lse;
+  ba.dr = w.dr;
+  ba.dqc = gated ? w.dqc : nullptr;
+  ba.dkc = gated ? w.dkc : nullptr;
+  ba.dvc = gated ? w.dvc : nullptr;
+  ba.dq = (uint16_t*)dq;
+  ba.dk = (uint16_t*)dk;
+  ba.dv = (uint16_t*)dv;
+  ba.row_ptr = s.kv_rp;
+  ba.col = s.kv_col;
+  e = vsa::launch_sparse_dkdv(ba, p->dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "dK/dV");
+  ba.row_ptr = s.q_rp;
+  ba.col = s.q_col;
+  e = vsa::launch_sparse_dq(ba, p->dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "dQ");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+"""The C-ABI library on the host: it loads, exports every entry point that
+include/vsa.h declares, and its host-only calls (argument checks, buffer
+sizes) behave as documented. No compute entry point is called here."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import bwd_block_map_amd as vsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "vsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = _declared()
+    assert {"vsa_fwd", "vsa_bwd", "block_map_to_index", "vsa_sizes", "vsa_validate"} <= set(names)
+    lib = ctypes.CDLL(vsa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(vsa.EXPORTS) == set(names)
+    assert vsa.vsa_abi_version() == vsa.ABI_VERSION
+
+
+def _prob(**kw):
+    base = dict(dtype=torch.bfloat16, layout="bhsd", B=1, Hq=2, Hkv=2, Sq=768, Skv=1024, D=128,
+                q_block=256, kv_block=256)
+    base.update(kw)
+    return vsa.make_problem(**base)
+
+
+def test_validate_accepts_the_workload_shapes():
+    vsa.vsa_validate(_prob())
+    vsa.vsa_validate(_prob(layout="bshd", Hq=40, Hkv=40, Sq=368640, Skv=368640, topk=144,
+                           gate_mode="per_token"))
+    vsa.vsa_validate(_prob(dtype=torch.float16, B=2, Hq=8, Hkv=8, Sq=4096, Skv=4096,
+                           q_block=128, kv_block=128))
+
+
+def _code(p):
+    with pytest.raises(vsa.VsaError) as e:
+        vsa.vsa_validate(p)
+    return e.value.code, e.value.msg
+
+
+def test_validate_rejects_bad_problems_with_messages():
+    fake = torch.zeros(4, dtype=torch.int32)  # host tensor: only its address is recorded
+    c, m = _code(_prob(layout="tnd", Sq=30, Skv=40, max_seqlen_q=30, max_seqlen_kv=40,
+                       q_block=128, kv_block=128, cu_seqlens_kv=fake))
+    assert c == vsa.ERR_INVALID_ARG and m == "actual_seq_lengths must be specified"
+    c, m = _code(_prob(layout="tnd", Sq=30, Skv=40, max_seqlen_q=30, max_seqlen_kv=40,
+                       q_block=128, kv_block=128, cu_seqlens_q=fake))
+    assert c == vsa.ERR_INVALID_ARG and m == "actual_seq_lengths_kv must be specified"
+    assert _code(_prob(Hq=3, Hkv=2))[0] == vsa.ERR_INVALID_ARG
+    assert _code(_prob(D=64))[0] == vsa.ERR_UNSUPPORTED
+    assert _code(_prob(q_block=48))[0] == vsa.ERR_UNSUPPORTED
+    assert _code(_prob(scale=float("nan")))[0] == vsa.ERR_INVALID_ARG
+    assert _code(_prob(scale=-1.0))[0] == vsa.ERR_INVALID_ARG
+    assert _code(_prob(topk=-1))[0] == vsa.ERR_INVALID_ARG
+    p = _prob()
+    p.struct.Qb = 4
+    assert _code(p)[0] == vsa.ERR_INVALID_ARG
+    p = _prob()
+    p.struct.abi_version = 99
+    assert _code(p)[0] == vsa.ERR_INVALID_ARG
+    c, _ = _code(_prob(layout="tnd", Sq=30, Skv=40, max_seqlen_q=30, max_seqlen_kv=40,
+                       q_block=128, kv_block=128, cu_seqlens_q=fake, cu_seqlens_kv=fake, topk=2))
+    assert c == vsa.ERR_UNSUPPORTED
+
+
+def test_sizes_cover_index_and_state():
+    s = vsa.vsa_sizes(_prob(topk=2, gate_mode="per_token"))
+    assert s["nnz_capacity"] == 1 * 2 * 3 * 2
+    # saved holds both CSR directions, the pooled/coarse state and O_sel
+    assert s["saved"] >= 2 * 768 * 128 * 2 + 2 * (1 * 2 * 3 + 1) * 4
+    s2 = vsa.vsa_sizes(_prob())
+    assert s2["nnz_capacity"] == 1 * 2 * 3 * 4
+    assert s2["saved"] < s["saved"]
+    big = vsa.vsa_sizes(_prob(layout="bshd", Hq=40, Hkv=40, Sq=368640, Skv=368640, topk=144,
+                              gate_mode="per_token"))
+    assert big["nnz_capacity"] == 40 * 1440 * 144
+
+
+def test_compute_calls_reject_bad_arguments_before_launching():
+    # no GPU is needed: the checks run on the host and return before any launch
+    p = _prob()
+    with pytest.raises(vsa.VsaError) as e:
+        vsa.vsa_fwd(p, None, None, None, None, None, None, None, None, None)
+    assert e.value.code == vsa.ERR_INVALID_ARG
+    with pytest.raises(vsa.VsaError) as e:
+        vsa.vsa_bwd(p, None, None, None, None, None, None, None, None, None, None, None, None, None)
+    assert e.value.code == vsa.ERR_INVALID_ARG
