@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: vsa_fwd (pooling,
+pooled-score top-k, block index in both directions, coarse attention, sparse
+forward with the gated composition) followed by vsa_bwd (row term, coarse
+backward, KV-owned dK/dV, Q-owned dQ). Inputs are resident in HBM before the
+timed region starts.
+
+Throughput is effective TFLOP/s over the selected blocks only, counting valid
+query x valid key pairs: 4*D flops per pair for the forward (QK^T and PV) and
+10*D for the backward (recomputed S, dP, dV, dQ, dK). `value` is the fwd+bwd
+rate; fwd and bwd are also reported separately, with their fraction of the
+MI355X dense bf16 MFMA peak.
+
+Prints one JSON line. `--gpus N` with N > 1 is refused: this build runs on
+one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "block-sparse attn fwd/bwd effective TFLOP/s (bf16) and % of MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def device_inputs(case):
+    d = {n: getattr(case, n) for n in ("q", "k", "v", "dout", "gate")}
+    dev = case.q.device
+    d["q_valid"] = torch.as_tensor(case.q_var, dtype=torch.int32, device=dev) \
+        if case.q_var is not None else None
+    d["kv_valid"] = torch.as_tensor(case.kv_var, dtype=torch.int32, device=dev) \
+        if case.kv_var is not None else None
+    if case.layout == "tnd":
+        d["cu_q"] = torch.as_tensor(np.concatenate([[0], np.cumsum(case.q_lens)]),
+                                    dtype=torch.int32, device=dev)
+        d["cu_kv"] = torch.as_tensor(np.concatenate([[0], np.cumsum(case.kv_lens)]),
+                                     dtype=torch.int32, device=dev)
+    else:
+        d["cu_q"] = d["cu_kv"] = None
+    d["map"] = case.block_map.to(dev).contiguous() if case.block_map is not None else None
+    return d
+
+
+def valid_pairs(case, bmap: torch.Tensor):
+    """(valid q x valid k pairs, padded pairs) over the selected blocks."""
+    dev = bmap.device
+    if case.layout == "tnd":
+        qv = torch.zeros(case.B, case.Qb, device=dev)
+        kv = torch.zeros(case.B, case.KVb, device=dev)
+        for b in range(case.B):
+            for i in range(case.Qb):
+                qv[b, i] = max(0, min(case.q_block, case.q_lens[b] - i * case.q_block))
+            for j in range(case.KVb):
+                kv[b, j] = max(0, min(case.kv_block, case.kv_lens[b] - j * case.kv_block))
+    else:
+        qi = torch.arange(case.Qb, device=dev)
+        kj = torch.arange(case.KVb, device=dev)
+        qv = (case.Sq - qi * case.q_block).clamp(0, case.q_block).float()
+        kv = (case.Skv - kj * case.kv_block).clamp(0, case.kv_block).float()
+        if case.q_var is not None:
+            qv = torch.minimum(qv, torch.as_tensor(case.q_var, device=dev).float())
+            kv = torch.minimum(kv, torch.as_tensor(case.kv_var, device=dev).float())
+        qv = qv.expand(case.B, -1)
+        kv = kv.expand(case.B, -1)
+    m = bmap.float()
+    w = qv[:, None, :, None] * kv[:, None, None, :]
+    live = (kv > 0).float()[:, None, None, :]
+    valid = float((m * w).sum().item())
+    padded = float((m * live).sum().item()) * case.q_block * case.kv_block
+    return valid, padded
+
+
+def cpu_baseline(case, gpu_map_rows_seed=0, target_s=15.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    every row of a random set of Q tiles of head 0 (its own pooled-score top-k
+    selection), forward only; rate in the same effective-TFLOP/s unit."""
+    import oracle
+    from workloads.synth import build_case
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    sub = build_case(case.name + "_head0", dtype=case.dtype, layout=case.layout, B=1, Hq=1,
+                     Hkv=1, D=case.D, q_block=case.q_block, kv_block=case.kv_block,
+                     q_var=case.q_var, kv_var=case.kv_var, topk=case.topk, map_kind="none",
+                     gate_mode=case.gate_mode, seed=0)
+    sl = (slice(None), slice(None), slice(0, 1)) if case.layout == "bshd" else \
+        (slice(None), slice(0, 1))
+    tens = {n: getattr(case, n)[sl].contiguous().cpu() for n in ("q", "k", "v", "dout")}
+    tens["gate"] = case.gate[sl].contiguous().cpu() if case.gate is not None else None
+    orc = oracle.Oracle(sub, np.float32, threads=threads, tensors=tens)
+    t0 = time.perf_counter()
+    bmap = orc.block_map()  # pooling + top-k for the head
+    if sub.gate_mode != "none":
+        orc.coarse()
+    t_sel = time.perf_counter() - t0
+    qv = np.minimum(np.asarray(sub.q_var), sub.q_block) if sub.q_var is not None else None
+    kv = np.asarray(sub.kv_var) if sub.kv_var is not None else None
+    rng = np.random.default_rng(1234)
+    tiles = rng.permutation(sub.Qb)
+    # calibrate on one tile, then size the sample to the time target
+    def rows_of(ts):
+        return np.array([[0, 0, t * sub.q_block + r] for t in ts for r in range(sub.q_block)],
+                        np.int32)
+    t0 = time.perf_counter()
+    orc.fwd_rows(rows_of(tiles[:1]))
+    one = time.perf_counter() - t0
+    n_tiles = int(max(1, min(len(tiles) - 1, target_s / max(one, 1e-3))))
+    sample = tiles[1:1 + n_tiles]
+    t0 = time.perf_counter()
+    orc.fwd_rows(rows_of(sample))
+    dt = time.perf_counter() - t0
+    flops = 0.0
+    for t in sample:
+        sel = bmap[0, 0, t].astype(bool)
+        flops += 4.0 * sub.D * sub.q_block * float(kv[sel].sum())  # every row of the tile
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fwd of all {sub.q_block} rows of {len(sample)} random Q tiles of head 0 "
+                   f"(of {sub.Qb} tiles x {case.Hq} heads), fp32 oracle, {dt:.1f} s; "
+                   f"rate over the sampled rows' valid keys"),
+        "seconds": round(dt, 2),
+        "selection_seconds": round(t_sel, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="c5_vsa256_720p_gate")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(sharding by head groups is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    import bwd_block_map_amd as vsa
+    from workloads.synth import make_case
+
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {args.workload} on cuda:0")
+    case = make_case(args.workload, device="cuda")
+    d = device_inputs(case)
+    p = vsa.make_problem(
+        dtype=case.torch_dtype, layout=case.layout, B=case.B, Hq=case.Hq, Hkv=case.Hkv,
+        Sq=case.Sq, Skv=case.Skv, D=case.D, q_block=case.q_block, kv_block=case.kv_block,
+        q_valid=d["q_valid"], kv_valid=d["kv_valid"], cu_seqlens_q=d["cu_q"],
+        cu_seqlens_kv=d["cu_kv"], max_seqlen_q=max(case.q_lens) if case.q_lens else 0,
+        max_seqlen_kv=max(case.kv_lens) if case.kv_lens else 0, scale=case.scale,
+        topk=case.topk, gate_mode=case.gate_mode)
+    buf = vsa.Buffers(p, d["q"], training=True)
+    bmap = d["map"] if case.topk == 0 else buf.map
+    dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+    dg = torch.empty_like(d["gate"]) if d["gate"] is not None else None
+
+    def fwd():
+        vsa.vsa_fwd(p, d["q"], d["k"], d["v"], bmap, d["gate"], buf.out, buf.lse, buf.saved,
+                    buf.ws_fwd)
+
+    def bwd():
+        vsa.vsa_bwd(p, d["q"], d["k"], d["v"], d["gate"], d["dout"], buf.out, buf.lse, buf.saved,
+                    dq, dk, dv, dg, buf.ws_bwd)
+
+    for w in range(args.warmup):
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {w + 1}/{args.warmup} done")
+    valid, padded = valid_pairs(case, bmap)
+    fwd_flops, bwd_flops = 4.0 * case.D * valid, 10.0 * case.D * valid
+
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    vsa.vsa_profile_begin()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(st)
+        fwd()
+        ev[s][1].record(st)
+        bwd()
+        ev[s][2].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    prof = vsa.vsa_profile_end()
+    fwd_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
+    step_ms = wall * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: fwd {fwd_ms:.2f} ms, bwd {bwd_ms:.2f} ms")
+
+    per_kernel = {k: {"ms_per_launch": (ms / n if n else 0.0), "launches_per_step": n / args.steps}
+                  for k, (ms, n) in prof.items()}
+    kflops = {"sparse_fwd": 4.0 * case.D * valid, "sparse_dkdv": 8.0 * case.D * valid,
+              "sparse_dq": 6.0 * case.D * valid}
+    dom = max(kflops, key=lambda k: prof[k][0])
+    dom_ms = prof[dom][0] / max(prof[dom][1], 1)
+    achieved = kflops[dom] / (dom_ms * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "ms_per_launch": round(dom_ms, 3)}
+
+    fwd_t = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    bwd_t = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    value = (fwd_flops + bwd_flops) / (step_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.dtype, "data": "synthetic (seeded N(0,1) inputs, sigmoid(N(0,1)) gate)",
+        "config": {"workload": case.name, "layout": case.layout, "B": case.B, "H": case.Hq,
+                   "D": case.D, "tiles": case.Qb, "tile": case.q_block, "topk": case.topk,
+                   "gate": case.gate_mode, "tokens_valid": int(np.sum(case.q_var))
+                   if case.q_var is not None else case.Sq},
+        "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+        "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2),
+        "fwd_frac_of_peak": round(fwd_t / PEAK_BF16_TFLOPS, 4),
+        "bwd_frac_of_peak": round(bwd_t / PEAK_BF16_TFLOPS, 4),
+        "valid_pairs": valid, "padded_pairs": padded,
+        "fwd_tflops_padded": round(4.0 * case.D * padded / (fwd_ms * 1e-3) / 1e12, 2),
+        "per_kernel_ms": {k: round(v["ms_per_launch"] * v["launches_per_step"], 3)
+                          for k, v in per_kernel.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(case, target_s=args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

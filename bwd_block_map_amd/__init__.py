@@ -29,7 +29,9 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 ABI_VERSION = 1
 
 EXPORTS = ("vsa_last_error", "vsa_abi_version", "vsa_validate", "vsa_sizes",
-           "block_map_to_index", "vsa_fwd", "vsa_bwd")
+           "block_map_to_index", "vsa_fwd", "vsa_bwd", "vsa_profile_begin", "vsa_profile_end")
+KERNELS = ("index", "pool", "coarse_fwd", "sparse_fwd", "bwd_pre", "coarse_bwd", "sparse_dkdv",
+           "sparse_dq")
 
 _DTYPES = {torch.bfloat16: BF16, torch.float16: FP16}
 _LAYOUTS = {"bhsd": BHSD, "bshd": BSHD, "tnd": TND}
@@ -70,7 +72,7 @@ def lib():
         L = C.CDLL(LIB_PATH)
         L.vsa_last_error.restype = C.c_char_p
         for name in ("vsa_abi_version", "vsa_validate", "vsa_sizes", "block_map_to_index",
-                     "vsa_fwd", "vsa_bwd"):
+                     "vsa_fwd", "vsa_bwd", "vsa_profile_begin", "vsa_profile_end"):
             getattr(L, name).restype = C.c_int
         _LIB = L
     return _LIB
@@ -258,6 +260,19 @@ def vsa_bwd(p: Problem, q, k, v, gate, dout, out, lse, saved, dq, dk, dv, dgate,
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate),
         _ptr(ws), C.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
         _stream(stream)))
+
+
+def vsa_profile_begin() -> None:
+    _check(lib().vsa_profile_begin())
+
+
+def vsa_profile_end() -> dict:
+    """{kernel name: (total ms, launches)} of the launches since vsa_profile_begin."""
+    n = len(KERNELS)
+    ms = (C.c_double * n)()
+    cnt = (C.c_int64 * n)()
+    _check(lib().vsa_profile_end(ms, cnt, C.c_int(n)))
+    return {KERNELS[i]: (ms[i], cnt[i]) for i in range(n)}
 
 
 # ---------------------------------------------------------------------------

@@ -7,7 +7,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -39,6 +41,41 @@ int hip_fail(hipError_t e, const char* where) {
 }
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// ---- opt-in kernel timing: event pairs around each launch --------------------
+struct ProfRec {
+  int kid;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<hipEvent_t> g_prof_pool;
+std::vector<ProfRec> g_prof_recs;
+size_t g_prof_next = 0;
+constexpr size_t kProfMax = 65536;
+
+// Records events around one launch when profiling is on.
+struct Prof {
+  ProfRec* r = nullptr;
+  hipStream_t st;
+  Prof(int kid, hipStream_t s) : st(s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_recs.size() >= kProfMax) return;
+    while (g_prof_pool.size() < 2 * (g_prof_recs.size() + 1)) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return;
+      g_prof_pool.push_back(e);
+    }
+    ProfRec rec{kid, g_prof_pool[2 * g_prof_recs.size()], g_prof_pool[2 * g_prof_recs.size() + 1]};
+    g_prof_recs.push_back(rec);
+    r = &g_prof_recs.back();
+    (void)hipEventRecord(r->a, st);
+  }
+  ~Prof() {
+    if (r) (void)hipEventRecord(r->b, st);
+  }
+};
 
 // Sub-buffers of one caller buffer, each 256-byte aligned. With base == nullptr
 // it only measures.
@@ -283,8 +320,12 @@ int block_map_to_index(const vsa_problem* p, const uint8_t* block_map, int kv_ow
     return fail(VSA_ERR_INVALID_ARG, "row_ptr / col_idx must be device buffers");
   if (col_capacity < 0) return fail(VSA_ERR_INVALID_ARG, "col_capacity must be >= 0");
   const vsa::Geom g = make_geom(p);
-  hipError_t e = vsa::launch_index(g, block_map, kv_owned ? 1 : 0, row_ptr, col_idx, col_capacity,
-                                   (hipStream_t)stream);
+  hipError_t e;
+  {
+    Prof pr(VSA_KERNEL_INDEX, (hipStream_t)stream);
+    e = vsa::launch_index(g, block_map, kv_owned ? 1 : 0, row_ptr, col_idx, col_capacity,
+                          (hipStream_t)stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "block_map_to_index");
   return ok();
 }
@@ -327,7 +368,10 @@ int vsa_fwd(const vsa_problem* p, const void* q, const void* k, const void* v, u
   float* lse_c = (gated && saved) ? s.lse_c : w.lse_c;
   const uint8_t* sel_map = block_map;
   if (is_video(p)) {
-    e = vsa::launch_pool(g, p->dtype, q, k, v, qc, kc, vc, st);
+    {
+      Prof pr(VSA_KERNEL_POOL, st);
+      e = vsa::launch_pool(g, p->dtype, q, k, v, qc, kc, vc, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "pool");
     vsa::CoarseArgs ca{};
     ca.g = g;
@@ -338,7 +382,10 @@ int vsa_fwd(const vsa_problem* p, const void* q, const void* k, const void* v, u
     ca.map = p->topk > 0 ? (block_map ? block_map : w.map) : nullptr;
     ca.oc = oc;
     ca.lse_c = lse_c;
-    e = vsa::launch_coarse_fwd(ca, p->topk > 0, gated, st);
+    {
+      Prof pr(VSA_KERNEL_COARSE_FWD, st);
+      e = vsa::launch_coarse_fwd(ca, p->topk > 0, gated, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "coarse forward");
     if (p->topk > 0) {
       sel_map = ca.map;
@@ -348,9 +395,13 @@ int vsa_fwd(const vsa_problem* p, const void* q, const void* k, const void* v, u
   // index: Q-owned always, KV-owned only when a backward follows
   int32_t* q_rp = saved ? s.q_rp : w.q_rp;
   int32_t* q_col = saved ? s.q_col : w.q_col;
-  e = vsa::launch_index(g, sel_map, 0, q_rp, q_col, cap, st);
+  {
+    Prof pr(VSA_KERNEL_INDEX, st);
+    e = vsa::launch_index(g, sel_map, 0, q_rp, q_col, cap, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "index (Q-owned)");
   if (saved) {
+    Prof pr(VSA_KERNEL_INDEX, st);
     e = vsa::launch_index(g, sel_map, 1, s.kv_rp, s.kv_col, cap, st);
     if (e != hipSuccess) return hip_fail(e, "index (KV-owned)");
   }
@@ -367,7 +418,10 @@ int vsa_fwd(const vsa_problem* p, const void* q, const void* k, const void* v, u
   fa.lse = lse;
   fa.row_ptr = q_rp;
   fa.col = q_col;
-  e = vsa::launch_sparse_fwd(fa, p->dtype, st);
+  {
+    Prof pr(VSA_KERNEL_SPARSE_FWD, st);
+    e = vsa::launch_sparse_fwd(fa, p->dtype, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "sparse forward");
   return ok();
 }
@@ -419,7 +473,10 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   pa.dr = w.dr;
   pa.doc = w.doc;
   pa.dgate = (uint16_t*)dgate;
-  e = vsa::launch_bwd_pre(pa, p->dtype, st);
+  {
+    Prof pr(VSA_KERNEL_BWD_PRE, st);
+    e = vsa::launch_bwd_pre(pa, p->dtype, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "backward preprocess");
 
   if (gated) {
@@ -435,7 +492,10 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
     ca.dqc = w.dqc;
     ca.dkc = w.dkc;
     ca.dvc = w.dvc;
-    e = vsa::launch_coarse_bwd(ca, st);
+    {
+      Prof pr(VSA_KERNEL_COARSE_BWD, st);
+      e = vsa::launch_coarse_bwd(ca, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "coarse backward");
   }
 
@@ -455,12 +515,48 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   ba.dv = (uint16_t*)dv;
   ba.row_ptr = s.kv_rp;
   ba.col = s.kv_col;
-  e = vsa::launch_sparse_dkdv(ba, p->dtype, st);
+  {
+    Prof pr(VSA_KERNEL_SPARSE_DKDV, st);
+    e = vsa::launch_sparse_dkdv(ba, p->dtype, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "dK/dV");
   ba.row_ptr = s.q_rp;
   ba.col = s.q_col;
-  e = vsa::launch_sparse_dq(ba, p->dtype, st);
+  {
+    Prof pr(VSA_KERNEL_SPARSE_DQ, st);
+    e = vsa::launch_sparse_dq(ba, p->dtype, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "dQ");
+  return ok();
+}
+
+int vsa_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_recs.clear();
+  g_prof_recs.reserve(kProfMax);
+  g_prof_on = true;
+  return ok();
+}
+
+int vsa_profile_end(double* ms_total, int64_t* launches, int n) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = false;
+  for (int k = 0; k < n; ++k) {
+    if (ms_total) ms_total[k] = 0.0;
+    if (launches) launches[k] = 0;
+  }
+  for (const ProfRec& r : g_prof_recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "vsa_profile_end");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "vsa_profile_end");
+    if (r.kid < n) {
+      if (ms_total) ms_total[r.kid] += ms;
+      if (launches) launches[r.kid] += 1;
+    }
+  }
+  g_prof_recs.clear();
   return ok();
 }
 

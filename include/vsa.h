@@ -213,6 +213,30 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
             size_t saved_bytes, void* dq, void* dk, void* dv, void* dgate, void* ws,
             size_t ws_bytes, void* stream);
 
+/*
+ * Opt-in per-kernel timing (instrumentation, not needed for computing).
+ * Between vsa_profile_begin() and vsa_profile_end() the library records a
+ * pair of HIP events around each of its kernel launches, on the launch
+ * stream. vsa_profile_end() waits for those events and writes, for every
+ * kernel id k < n, the summed duration in milliseconds (ms_total[k]) and the
+ * number of launches (launches[k]). Recording stops silently after 65536
+ * launches. Process-wide state: do not profile from several threads at once.
+ */
+enum vsa_kernel_id {
+  VSA_KERNEL_INDEX = 0,       /* block map -> CSR (count, scan, fill) */
+  VSA_KERNEL_POOL = 1,        /* mean-pooled tiles                    */
+  VSA_KERNEL_COARSE_FWD = 2,  /* coarse scores, top-k, coarse attention */
+  VSA_KERNEL_SPARSE_FWD = 3,  /* sparse-branch forward                */
+  VSA_KERNEL_BWD_PRE = 4,     /* row term rowsum(dO * O_sel), gate sums */
+  VSA_KERNEL_COARSE_BWD = 5,  /* compression-branch backward          */
+  VSA_KERNEL_SPARSE_DKDV = 6, /* KV-owned dK / dV                     */
+  VSA_KERNEL_SPARSE_DQ = 7,   /* Q-owned dQ                           */
+  VSA_KERNEL_COUNT = 8
+};
+
+int vsa_profile_begin(void);
+int vsa_profile_end(double* ms_total, int64_t* launches, int n);
+
 #ifdef __cplusplus
 }
 #endif
