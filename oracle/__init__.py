@@ -252,6 +252,22 @@ class Oracle:
         return out
 
 
+def _dkdv_tiles(self, tiles: np.ndarray):
+    """dk, dv [n, kv_block, D] of sampled KV tiles, rows of (b, kv_head, j)."""
+    c = self.case
+    tiles = np.ascontiguousarray(np.asarray(tiles, np.int32).reshape(-1, 3))
+    m = self.block_map()
+    dk = np.zeros((len(tiles), c.kv_block, c.D), self.dt)
+    dv = np.zeros((len(tiles), c.kv_block, c.D), self.dt)
+    self._f("dkdv_tiles")(self.P.ref, self._p(self.q), self._p(self.k), self._p(self.v),
+                          self._p(self.gate), self._p(self.dout), _ptr(m, C.c_uint8),
+                          C.c_int64(len(tiles)), _ptr(tiles, C.c_int32), self._p(dk), self._p(dv))
+    return dk, dv
+
+
+Oracle.dkdv_tiles = _dkdv_tiles
+
+
 def block_index(case, block_map: np.ndarray, kv_owned: bool):
     """Brute-force CSR of the live blocks: (row_ptr int32, col int32)."""
     P = Prob(case)

@@ -621,6 +621,95 @@ void dq_rows(const Geo& g, const T* q, const T* k, const T* v, const T* gate, co
   }
 }
 
+// dK / dV of sampled KV tiles (b, hk, j): the key-pass formulas above for the
+// keys of those tiles only, with the row statistics (lse_s, Dr_s) of every row
+// that attends them evaluated from their own rows. Outputs [n, kv_block, D].
+template <class T>
+void dkdv_tiles(const Geo& g, const T* q, const T* k, const T* v, const T* gate, const T* dout,
+                const uint8_t* map, int64_t ntiles, const int32_t* tiles, T* dk_out, T* dv_out) {
+  const auto& p = g.p;
+  const int D = p.D;
+  const T sc = (T)p.scale;
+  Coarse<T> c;
+  if (p.gate_mode != 0) {
+    const int64_t nq = (int64_t)p.B * p.Hq * p.Qb * D, nk = (int64_t)p.B * p.Hkv * p.KVb * D;
+    c.qc.assign(nq, 0);
+    c.kc.assign(nk, 0);
+    c.vc.assign(nk, 0);
+    c.oc.assign(nq, 0);
+    c.lse_c.assign((int64_t)p.B * p.Hq * p.Qb, 0);
+    pool(g, q, k, v, c.qc.data(), c.kc.data(), c.vc.data());
+    coarse_fwd(g, c.qc.data(), c.kc.data(), c.vc.data(), c.oc.data(), c.lse_c.data());
+    std::vector<uint8_t> gm((size_t)p.B * p.Hkv, 0);
+    for (int64_t u = 0; u < ntiles; ++u) gm[tiles[3 * u] * p.Hkv + tiles[3 * u + 1]] = 1;
+    coarse_bwd(g, gate, dout, c, (T*)nullptr, gm.data());
+  }
+  // rows attending any requested tile
+  std::vector<uint8_t> need(g.rows_total(), 0);
+  for (int64_t u = 0; u < ntiles; ++u) {
+    const int b = tiles[3 * u], hk = tiles[3 * u + 1], j = tiles[3 * u + 2];
+    for (int h = hk * g.group(); h < (hk + 1) * g.group(); ++h)
+      for (int i = 0; i < g.nqb(b); ++i)
+        if (g.live_block(map, b, h, i, j))
+          for (int r = 0; r < g.q_exist(b, i); ++r) need[g.row_id(b, h, i * p.q_block + r)] = 1;
+  }
+  std::vector<int64_t> jobs;
+  for (int b = 0; b < p.B; ++b)
+    for (int h = 0; h < p.Hq; ++h)
+      for (int s = 0; s < g.q_len(b); ++s)
+        if (need[g.row_id(b, h, s)]) jobs.push_back(((int64_t)(b * p.Hq + h) << 32) | s);
+  std::vector<T> lse(g.rows_total(), 0), dr(g.rows_total(), 0);
+#pragma omp parallel
+  {
+    KeyList kl;
+    std::vector<T> P;
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t u = 0; u < (int64_t)jobs.size(); ++u) {
+      const int bh = (int)(jobs[u] >> 32), s = (int)(jobs[u] & 0xffffffff);
+      const int b = bh / p.Hq, h = bh % p.Hq;
+      const int64_t qo = g.q_off(b, h, s), rid = g.row_id(b, h, s);
+      row_keys(g, map, b, h, s, kl);
+      row_softmax(g, q, k, qo, kl, P, lse[rid]);
+      T r = 0;
+      for (size_t t = 0; t < kl.off.size(); ++t) r += P[t] * dot(dout + qo, v + kl.off[t], D);
+      dr[rid] = r;
+    }
+  }
+#pragma omp parallel for collapse(2) schedule(dynamic, 8)
+  for (int64_t u = 0; u < ntiles; ++u)
+    for (int tk = 0; tk < p.kv_block; ++tk) {
+      const int b = tiles[3 * u], hk = tiles[3 * u + 1], j = tiles[3 * u + 2];
+      T* dko = dk_out + (u * p.kv_block + tk) * D;
+      T* dvo = dv_out + (u * p.kv_block + tk) * D;
+      for (int e = 0; e < D; ++e) dko[e] = dvo[e] = 0;
+      const int n = g.kv_valid(b, j);
+      if (tk >= n) continue;
+      const int64_t ko = g.kv_off(b, hk, j * p.kv_block + tk);
+      for (int h = hk * g.group(); h < (hk + 1) * g.group(); ++h)
+        for (int i = 0; i < g.nqb(b); ++i) {
+          if (!g.live_block(map, b, h, i, j)) continue;
+          for (int r = 0; r < g.q_exist(b, i); ++r) {
+            const int s = i * p.q_block + r;
+            const int64_t qo = g.q_off(b, h, s), rid = g.row_id(b, h, s);
+            const T P = std::exp(sc * dot(q + qo, k + ko, D) - lse[rid]);
+            const T ds = P * (dot(dout + qo, v + ko, D) - dr[rid]);
+            for (int e = 0; e < D; ++e) {
+              dko[e] += sc * ds * q[qo + e];
+              dvo[e] += P * dout[qo + e];
+            }
+          }
+        }
+      if (p.gate_mode != 0) {
+        const T* a = c.dkc.data() + g.pk(b, hk, j);
+        const T* bb = c.dvc.data() + g.pk(b, hk, j);
+        for (int e = 0; e < D; ++e) {
+          dko[e] += a[e] / (T)n;
+          dvo[e] += bb[e] / (T)n;
+        }
+      }
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -710,6 +799,17 @@ int64_t oracle_block_index(const oracle_problem* p, const uint8_t* map, int32_t 
     Geo g(*p);                                                                                  \
     dq_rows(g, q, k, v, gate, dout, map, nrows, rows, dq_rows_out);                             \
   }
+
+#define ORACLE_TILE_ENTRY(SUF, T)                                                                \
+  void oracle_dkdv_tiles_##SUF(const oracle_problem* p, const T* q, const T* k, const T* v,      \
+                               const T* gate, const T* dout, const uint8_t* map, int64_t ntiles, \
+                               const int32_t* tiles, T* dk_out, T* dv_out) {                     \
+    set_threads(p);                                                                              \
+    Geo g(*p);                                                                                   \
+    dkdv_tiles(g, q, k, v, gate, dout, map, ntiles, tiles, dk_out, dv_out);                      \
+  }
+ORACLE_TILE_ENTRY(f32, float)
+ORACLE_TILE_ENTRY(f64, double)
 
 ORACLE_ENTRY_POINTS(f32, float)
 ORACLE_ENTRY_POINTS(f64, double)

@@ -1,0 +1,132 @@
+"""GPU parity at the video workloads' full sizes, in the launch configuration
+bench.py times (C4: 360 tiles x 12 heads; C5: 1440 tiles x 40 heads + gate).
+
+The oracle cannot evaluate whole heads at these sizes in seconds, so it checks
+(a) the top-k selection of sampled heads (equal, or a valid near-tie), (b)
+sampled rows (out, lse, dq) across full, partial and padded Q rows, (c) dk/dv of
+sampled KV tiles (a full one and a partial one, the least-selected of their
+kind), and (d) over all heads, two identities that hold at any size: the key-
+shift identity sum_t dk_t = 0 and the value-shift identity
+sum_t dv_t = sum_s dO_s (+ sum_s gate_s dO_s with the gate).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.helpers import GRAD_TOL, OUT_TOL, check
+from workloads.synth import make_case
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from tests.gpu_run import run_case  # noqa: E402
+from tests.test_gpu_parity import _topk_agreement  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _heads_subcase(case, heads):
+    """The same workload restricted to the listed heads (MHA), tensors on the host."""
+    idx = torch.as_tensor(heads, device=case.q.device)
+
+    def pick(t, dim):
+        return None if t is None else t.index_select(dim, idx).contiguous().cpu()
+
+    hd = 2 if case.layout == "bshd" else 1
+    gd = 2 if case.layout == "bshd" else 1
+    return dataclasses.replace(case, Hq=len(heads), Hkv=len(heads), q=pick(case.q, hd),
+                               k=pick(case.k, hd), v=pick(case.v, hd), dout=pick(case.dout, hd),
+                               gate=pick(case.gate, gd))
+
+
+def _rows_of(case, res_map_same, rng, n):
+    """n sampled (b, h_local, s) rows from Q tiles whose selection agrees, spread
+    over full and partial tiles and over valid and padded slots."""
+    qv = np.asarray(case.q_var)
+    rows = []
+    kinds = [np.nonzero(qv == case.q_block)[0], np.nonzero(qv < case.q_block)[0]]
+    for h in range(case.Hq):
+        for kind in kinds:
+            tiles = [t for t in kind if res_map_same[0, h, t]]
+            for t in rng.choice(tiles, size=min(len(tiles), n // (2 * case.Hq)), replace=False):
+                r = int(rng.integers(0, case.q_block))
+                rows.append((0, h, int(t) * case.q_block + r))
+    return np.array(rows, np.int32)
+
+
+def _fullsize(name, heads, nrows):
+    case = make_case(name, device="cuda")
+    _say(f"[{name}] running fwd+bwd on the GPU")
+    res = run_case(case, keep_device=True)
+    gmap = res["map"].cpu().numpy()
+
+    # (d) identities over all heads (test-side float64 reductions of the inputs)
+    dk = res["dk"].double()
+    dv = res["dv"].double()
+    do = case.dout.double()
+    sdim = 1  # BSHD
+    tot_dk = dk.sum(sdim)
+    l1_dk = dk.abs().sum(sdim)
+    assert float((tot_dk.abs() / l1_dk.clamp_min(1e-30)).max()) < 2e-3, "sum dk != 0"
+    want = do.sum(sdim)
+    if case.gate is not None:
+        want = want + (case.gate.double()[..., None] * do).sum(sdim)
+    err = (dv.sum(sdim) - want).abs() / dv.abs().sum(sdim).clamp_min(1e-30)
+    assert float(err.max()) < 2e-3, f"sum dv != sum dO: {float(err.max()):.2e}"
+    _say(f"  identities ok (max rel {float(err.max()):.1e})")
+
+    sub = _heads_subcase(case, heads)
+    orc = oracle.Oracle(sub, np.float32, threads=16)
+    same = _topk_agreement(orc, gmap[:, heads])
+    _say(f"  top-k: {int(same.sum())}/{same.size} sampled rows identical, the rest valid near-ties")
+
+    # (b) sampled rows
+    rng = np.random.default_rng(7)
+    rows = _rows_of(sub, same, rng, nrows)
+    o_r, l_r = orc.fwd_rows(rows)
+    dq_r = orc.dq_rows(rows)
+    hs = torch.as_tensor([heads[h] for h in rows[:, 1]], device="cuda")
+    ss = torch.as_tensor(rows[:, 2].astype(np.int64), device="cuda")
+    got_o = res["out"][0, ss, hs].float().cpu().numpy()
+    got_l = res["lse"][0, hs, ss].float().cpu().numpy()
+    got_dq = res["dq"][0, ss, hs].float().cpu().numpy()
+    check("out rows", o_r, got_o, OUT_TOL)
+    check("lse rows", l_r, got_l, OUT_TOL)
+    check("dq rows", dq_r, got_dq, GRAD_TOL)
+
+    # (c) sampled KV tiles: the least-selected full and partial tile of head 0
+    m = orc.block_map()[0, 0]
+    kvv = np.asarray(sub.kv_var)
+    bad = set()
+    for i in np.nonzero(~same[0, 0])[0]:
+        bad |= set(np.nonzero(m[i] != gmap[0, heads[0], i])[0].tolist())
+    cnt = m.sum(0).astype(np.int64)
+    tiles = []
+    for kind in (kvv == sub.kv_block, (kvv < sub.kv_block) & (kvv > 0)):
+        cand = [j for j in np.nonzero(kind & (cnt > 0))[0] if j not in bad]
+        if cand:
+            tiles.append([0, 0, int(min(cand, key=lambda j: cnt[j]))])
+    tk, tv = orc.dkdv_tiles(np.array(tiles, np.int32))
+    for n, (_, _, j) in enumerate(tiles):
+        sl = slice(j * sub.kv_block, (j + 1) * sub.kv_block)
+        _say(f"  tile {j}: valid {kvv[j]}, selected by {cnt[j]} Q tiles")
+        check(f"dk tile {j}", tk[n], res["dk"][0, sl, heads[0]].float().cpu().numpy(), GRAD_TOL)
+        check(f"dv tile {j}", tv[n], res["dv"][0, sl, heads[0]].float().cpu().numpy(), GRAD_TOL)
+
+
+def test_c4_video_full_size():
+    _fullsize("c4_vsa256_video", heads=[0, 7], nrows=512)
+
+
+def test_c5_720p_gate_full_size():
+    _fullsize("c5_vsa256_720p_gate", heads=[3, 38], nrows=384)

@@ -492,3 +492,15 @@ def test_sampled_rows_match_full_evaluation():
         np.testing.assert_allclose(o_r[n], out[b, s, h], atol=1e-15)  # BSHD
         np.testing.assert_allclose(l_r[n], lse[b, h, s], atol=1e-15)
         np.testing.assert_allclose(d_r[n], dq[b, s, h], atol=1e-14)
+
+
+def test_sampled_tiles_match_full_backward():
+    for gm in ("none", "per_token"):
+        case = _vsa_small(topk=3, gate_mode=gm)
+        orc = oracle.Oracle(case)
+        _, dk, dv, _ = orc.bwd()
+        tiles = np.array([[0, 0, 0], [0, 1, 4], [0, 1, 1], [0, 0, 2]], np.int32)
+        tk, tv = orc.dkdv_tiles(tiles)
+        for n, (b, hk, j) in enumerate(tiles):
+            np.testing.assert_allclose(tk[n], dk[b, j * 8:(j + 1) * 8, hk], atol=1e-14)  # BSHD
+            np.testing.assert_allclose(tv[n], dv[b, j * 8:(j + 1) * 8, hk], atol=1e-14)
