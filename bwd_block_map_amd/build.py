@@ -28,11 +28,20 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source register form of the MFMA accumulators: the forward and dQ keep
+# them in VGPRs; dK/dV keeps its large accumulator set in AGPRs.
+EXTRA = {
+    "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_bwd.hip": [],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = EXTRA.get(src, [])
+    if os.environ.get("VSA_MFMA_VGPR_FORM") is not None:  # build experiments
+        extra = ["-mllvm", f"-amdgpu-mfma-vgpr-form={os.environ['VSA_MFMA_VGPR_FORM']}"]
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stderr}")

@@ -22,6 +22,7 @@
 //  * dQ: like the forward (Q-owned list, 64-key chunks, S^T and dP^T with
 //    lane = query row); dQ^T += K^T dS^T with K^T staged in LDS.
 #include "kernels.hpp"
+#include "lds_tiles.hpp"
 
 namespace vsa {
 
@@ -73,7 +74,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
     for (int u = 0; u < 8; ++u) part += dof[u] * of[u];
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 16);
-    if (dg == 0) a.dr[g.lse_base(b, h) + blk0 + s] = part;
+    if (dg == 0) {
+      const long long lr = g.lse_base(b, h) + blk0 + s;
+      a.dr[lr] = part;
+      const float l = a.lse[lr];
+      a.lse2[lr] = l == -INFINITY ? INFINITY : l * LOG2E;  // exp2 domain; empty rows give P = 0
+    }
     if (gated) {
       if (a.gate_mode == VSA_GATE_PER_TOKEN) {
         const float gt = E::lo(a.gate[g.gtok_base(b, h) + (long long)(blk0 + s) * g.gtok_rs()]);
@@ -117,23 +123,37 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
 // ---------------------------------------------------------------------------
 // dK / dV (KV-owned)
 // ---------------------------------------------------------------------------
-constexpr int QC = 32;         // query rows per chunk
-constexpr int NSTR = HD + 8;   // row-major stride (elements)
-constexpr int TSTR = QC + 4;   // transposed stride (elements): 72 B, conflict-free b64 reads
-constexpr int KV_STAGE = 2 * QC * NSTR + 2 * HD * TSTR + 2 * QC * 2;  // + lse2, dr (as floats)
+// Which 128-key sub-tiles a launch owns: sub-tiles with more than 64 live keys
+// go to the wide launch (4 waves x 32 keys), the others (the partial video
+// tiles) to a narrow launch over their first 64 keys, where the 4 waves form
+// 2 key slots x 2 row groups (each chunk's rows are split, and the two row
+// groups' sums are added through LDS at the end), so no wave sits on absent keys.
+enum DkdvPart { DKDV_ALL = 0, DKDV_WIDE = 1, DKDV_NARROW = 2 };
 
-template <class ET, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void sparse_dkdv_kernel(const BwdArgs a) {
+template <int NW, int RG, int NBUF>
+struct DkdvShape {
+  static constexpr int KS = NW / RG;          // key slots (32 keys each)
+  static constexpr int KW = 32 * KS;          // keys of the work-group
+  static constexpr int QC = 32 * RG;          // query rows per chunk
+  static constexpr int QT = QC * HD * 2;      // bytes of a QC-row tile
+  static constexpr int STAGE = 2 * QT + 2 * QC * 4;  // Q | dO | lse2 | dr
+  static constexpr int LDS = NBUF * STAGE + KW * HD * 2;  // stages, then the K tile
+};
+
+template <class ET, int NW, int RG, int NBUF>
+__global__ __launch_bounds__(NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a, int part) {
   using E = Elem<ET>;
-  constexpr int NT = NW * 64;
-  constexpr int TU = (2 * (QC / 4) * (HD / 8)) / NT;  // (4 rows x 8 d) pieces of Q and dO per thread
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KV_STAGE];
+  using S = DkdvShape<NW, RG, NBUF>;
+  constexpr int QC = S::QC, QT = S::QT, STAGE = S::STAGE, KW = S::KW;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS];
 
   const Geom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hl = lane >> 5, l32 = lane & 31;
-  const int nsub = g.kv_block / (32 * NW);
-  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int hl = lane >> 5;
+  const int kslot = wave % S::KS, rg = wave / S::KS;
+  const int unit = part == DKDV_ALL ? KW : 128;  // keys per grid sub-tile
+  const int nsub = g.kv_block / unit;
+  int id = xcd_group(blockIdx.x, gridDim.x, nsub);
   const int sub = id % nsub;
   id /= nsub;
   const int j = id % g.KVb;
@@ -141,13 +161,16 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dkdv_kernel(const BwdArgs a
   const int hk = id % g.Hkv, b = id / g.Hkv;
 
   const int kexist = g.kv_exist(b, j);
-  const int k0 = sub * 32 * NW;
+  const int k0 = sub * unit;
   if (k0 >= kexist) return;  // no key of this sub-tile exists
   const int nval = g.kv_val(b, j);
-  const int mykey = k0 + wave * 32 + l32;  // key inside the KV block
-  const bool key_ok = mykey < kexist, key_live = mykey < nval;
+  const int live = max(0, min(unit, nval - k0));  // live keys of the sub-tile
+  if (part == DKDV_WIDE && live > 0 && live <= 64) return;
+  if (part == DKDV_NARROW && !(live > 0 && live <= 64)) return;
   const long long krs = g.kv_rs();
-  const long long koff = g.kv_base(b, hk) + (long long)(j * g.kv_block + mykey) * krs;
+  const long long kbase = g.kv_base(b, hk) + (long long)j * g.kv_block * krs;
+  const int mykey = k0 + 32 * kslot + (lane & 31);  // key inside the KV block
+  const bool key_live = mykey < nval;
 
   f32x16_t dka[4], dva[4];
 #pragma unroll
@@ -155,88 +178,101 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dkdv_kernel(const BwdArgs a
 #pragma unroll
     for (int r = 0; r < 16; ++r) dka[mb][r] = dva[mb][r] = 0.f;
 
-  if (k0 < nval) {
-    // B operands: K^T and V^T columns (lane: key l32, d = 16ks + 8hl + 0..7)
-    uint4 kr[8], vr[8];
+  if (live > 0) {
+    // the work-group's K rows stay in LDS for the whole walk (rows past the
+    // valid keys repeat the last valid one and are masked); V^T columns are
+    // register B operands (lane: key, d = 16ks + 8hl + 0..7)
+    uint8_t* Kt = smem + NBUF * STAGE;
+    const int lastk = min(live, KW) - 1;
+    stage_tile<KW, NW>(Kt, wave, lane, [&](int row) {
+      return a.k + kbase + (long long)(k0 + min(row, lastk)) * krs;
+    });
+    uint4 vr[8];
+    const long long koff = kbase + (long long)mykey * krs;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      kr[ks] = key_live ? ldg16(a.k + koff + 16 * ks + 8 * hl) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < 8; ++ks)
       vr[ks] = key_live ? ldg16(a.v + koff + 16 * ks + 8 * hl) : make_uint4(0, 0, 0, 0);
-    }
+    const float kmask = key_live ? 0.f : -INFINITY;  // added to the exp2 argument
     const float c2 = g.scale * LOG2E;
     const long long qrs = g.q_rs();
-    uint4 st[TU][4];
-    float lst = 0.f;  // lse2 or dr of one staged row (threads 0..63)
+    const RowOffs ro(lane);
+    const TrOffs to(lane);
+    const int rb = 32 * rg;  // this wave's rows inside a chunk
 
-    // one chunk = (head h, Q block i, rows 32c .. 32c+31)
-    auto load_chunk = [&](int h, int i, int c) {
-      const int qex = g.q_exist(b, i);
-      const int r0 = c * QC;
-      const long long base = g.q_base(b, h) + (long long)(i * g.q_block + r0) * qrs;
+    // one chunk = (head h, Q block i, rows QC*c ..); rows past the block repeat
+    // its last row (in bounds) and are masked in the compute
+    auto stage = [&](int buf, int h, int i, int c) {
+      const int last = g.q_exist(b, i) - c * QC - 1;
+      const long long base = g.q_base(b, h) + (long long)(i * g.q_block + c * QC) * qrs;
+      uint8_t* st = smem + buf * STAGE;
+      stage_tile<QC, NW>(st, wave, lane, [&](int row) { return a.q + base + min(row, last) * qrs; });
+      stage_tile<QC, NW>(st + QT, wave, lane,
+                         [&](int row) { return a.dout + base + min(row, last) * qrs; });
+      const long long lb = g.lse_base(b, h) + i * g.q_block + c * QC;
+      if (wave == 0) stage_f32<QC>((float*)(st + 2 * QT), a.lse2 + lb, lane, last);
+      if (wave == NW - 1) stage_f32<QC>((float*)(st + 2 * QT) + QC, a.dr + lb, lane, last);
+    };
+
+    auto compute = [&](int buf, int rows_valid) {
+      const uint8_t* Qs = smem + buf * STAGE;
+      const uint8_t* Ds = Qs + QT;
+      const float* lse2 = reinterpret_cast<const float*>(Qs + 2 * QT);
+      const float* drs = lse2 + QC;
+      // S = Q K^T and dP = dO V^T (rows rb + 8(r/4) + 4hl + r%4, key column)
+      f32x16_t s, dp;
 #pragma unroll
-      for (int u = 0; u < TU; ++u) {
-        const int it = tid + u * NT;  // 0..255: first half Q, second half dO
-        const int which = it >> 7, w = it & 127, dg = w & 15, rg = w >> 4;
-        const uint16_t* src = which ? a.dout : a.q;
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = 4 * rg + rr;
-          st[u][rr] = (r0 + row < qex) ? ldg16(src + base + (long long)row * qrs + 8 * dg)
-                                       : make_uint4(0, 0, 0, 0);
-        }
+      for (int ks = 0; ks < 8; ++ks) {
+        s = E::mfma(ro.at(Qs, rb, ks), ro.at(Kt, 32 * kslot, ks), s);
+        dp = E::mfma(ro.at(Ds, rb, ks), vr[ks], dp);
       }
-      if (tid < 2 * QC) {
-        const int row = tid & (QC - 1);
-        const long long lb = g.lse_base(b, h) + i * g.q_block + r0 + row;
-        if (r0 + row < qex) {
-          if (tid < QC) {
-            const float l = a.lse[lb];
-            lst = l == -INFINITY ? INFINITY : l * LOG2E;
-          } else {
-            lst = a.dr[lb];
+      const bool partial = rows_valid < rb + 32;  // rows past the Q block get P = 0
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2 + rb + 8 * q4 + 4 * hl);
+        const float4 d4 = *reinterpret_cast<const float4*>(drs + rb + 8 * q4 + 4 * hl);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        if (partial) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * q4 + u;
+            const float l = rb + 8 * q4 + 4 * hl + u >= rows_valid ? INFINITY : lv[u];
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -l) + kmask);
+            s[r] = p;
+            dp[r] = p * (dp[r] - dv[u]);
           }
         } else {
-          lst = tid < QC ? INFINITY : 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * q4 + u;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lv[u]) + kmask);
+            s[r] = p;
+            dp[r] = p * (dp[r] - dv[u]);
+          }
         }
       }
-    };
-    auto store_chunk = [&](int buf) {
-      uint16_t* base = smem + buf * KV_STAGE;
+      // dV^T += dO^T P, dK^T += Q^T dS (row steps of 16)
 #pragma unroll
-      for (int u = 0; u < TU; ++u) {
-        const int it = tid + u * NT;
-        const int which = it >> 7, w = it & 127, dg = w & 15, rg = w >> 4;
-        uint16_t* nat = base + which * (QC * NSTR);
-        uint16_t* tr = base + 2 * QC * NSTR + which * (HD * TSTR);
+      for (int kt = 0; kt < 2; ++kt) {
+        const int o = 8 * kt;
+        const uint4 pp = make_uint4(E::pack(s[o], s[o + 1]), E::pack(s[o + 2], s[o + 3]),
+                                    E::pack(s[o + 4], s[o + 5]), E::pack(s[o + 6], s[o + 7]));
+        const uint4 ps = make_uint4(E::pack(dp[o], dp[o + 1]), E::pack(dp[o + 2], dp[o + 3]),
+                                    E::pack(dp[o + 4], dp[o + 5]), E::pack(dp[o + 6], dp[o + 7]));
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          *reinterpret_cast<uint4*>(nat + (4 * rg + rr) * NSTR + 8 * dg) = st[u][rr];
-        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&st[u][0]);
-        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&st[u][1]);
-        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&st[u][2]);
-        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&st[u][3]);
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          uint2 even, odd;
-          even.x = (r0[w2] & 0xffffu) | (r1[w2] << 16);
-          even.y = (r2[w2] & 0xffffu) | (r3[w2] << 16);
-          odd.x = (r0[w2] >> 16) | (r1[w2] & 0xffff0000u);
-          odd.y = (r2[w2] >> 16) | (r3[w2] & 0xffff0000u);
-          *reinterpret_cast<uint2*>(tr + (8 * dg + 2 * w2) * TSTR + 4 * rg) = even;
-          *reinterpret_cast<uint2*>(tr + (8 * dg + 2 * w2 + 1) * TSTR + 4 * rg) = odd;
+        for (int mb = 0; mb < 4; ++mb) {
+          dva[mb] = E::mfma(to.at(Ds, rb + 16 * kt, mb), pp, dva[mb]);
+          dka[mb] = E::mfma(to.at(Qs, rb + 16 * kt, mb), ps, dka[mb]);
         }
-      }
-      if (tid < 2 * QC) {
-        float* fl = reinterpret_cast<float*>(base + 2 * QC * NSTR + 2 * HD * TSTR);
-        fl[tid] = lst;
       }
     };
 
     // walk (head in group, KV-owned entry, row chunk)
     int hh = 0, e = 0, e1 = 0, c = 0, i = 0, nch = 0;
     auto row_of = [&](int hx) { return ((long long)b * g.Hq + hk * g.group + hx) * g.KVb + j; };
-    // advance (hh, e) to the next non-empty position, starting at the current one
-    auto settle = [&]() {
+    auto settle = [&]() {  // advance (hh, e) to the next entry with rows, from the current one
       while (hh < g.group) {
         if (e < e1) {
           i = a.col[e];
@@ -260,12 +296,11 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dkdv_kernel(const BwdArgs a
       settle();
     }
     if (hh < g.group) {
-      load_chunk(hk * g.group + hh, i, 0);
-      store_chunk(0);
+      stage(0, hk * g.group + hh, i, 0);
+      wait_vmem();
       __syncthreads();
       int buf = 0;
       while (true) {
-        // the chunk after this one
         int nhh = hh, ne = e, ne1 = e1, nc = c + 1, ni = i, nnch = nch;
         if (nc >= nch) {
           const int shh = hh, se = e, se1 = e1, si = i, snch = nch;
@@ -284,63 +319,21 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dkdv_kernel(const BwdArgs a
           nch = snch;
         }
         const bool has_next = nhh < g.group;
-        if (has_next) load_chunk(hk * g.group + nhh, ni, nc);
-
-        const uint16_t* base = smem + buf * KV_STAGE;
-        const uint16_t* Qn = base;
-        const uint16_t* Dn = base + QC * NSTR;
-        const uint16_t* Qt = base + 2 * QC * NSTR;
-        const uint16_t* Dt = Qt + HD * TSTR;
-        const float* lse2 = reinterpret_cast<const float*>(base + 2 * QC * NSTR + 2 * HD * TSTR);
-        const float* drs = lse2 + QC;
-
-        // S = Q K^T and dP = dO V^T (rows 8(r/4) + 4hl + r%4, key column l32)
-        f32x16_t s, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const uint4 aq = *reinterpret_cast<const uint4*>(Qn + l32 * NSTR + 16 * ks + 8 * hl);
-          const uint4 ad = *reinterpret_cast<const uint4*>(Dn + l32 * NSTR + 16 * ks + 8 * hl);
-          s = E::mfma(aq, kr[ks], s);
-          dp = E::mfma(ad, vr[ks], dp);
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 l4 = *reinterpret_cast<const float4*>(lse2 + 8 * q4 + 4 * hl);
-          const float4 d4 = *reinterpret_cast<const float4*>(drs + 8 * q4 + 4 * hl);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = 4 * q4 + u;
-            const float p = key_live ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lv[u])) : 0.f;
-            s[r] = p;
-            dp[r] = p * (dp[r] - dv[u]);
+        const int rows_valid = g.q_exist(b, i) - c * QC;
+        if (NBUF == 2) {
+          if (has_next) stage(buf ^ 1, hk * g.group + nhh, ni, nc);
+          compute(buf, rows_valid);
+          wait_vmem();
+          __syncthreads();
+        } else {
+          compute(0, rows_valid);
+          __syncthreads();
+          if (has_next) {
+            stage(0, hk * g.group + nhh, ni, nc);
+            wait_vmem();
+            __syncthreads();
           }
         }
-        // dV^T += dO^T P, dK^T += Q^T dS (row steps of 16)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int o = 8 * kt;
-          const uint4 pp = make_uint4(E::pack(s[o], s[o + 1]), E::pack(s[o + 2], s[o + 3]),
-                                      E::pack(s[o + 4], s[o + 5]), E::pack(s[o + 6], s[o + 7]));
-          const uint4 ps = make_uint4(E::pack(dp[o], dp[o + 1]), E::pack(dp[o + 2], dp[o + 3]),
-                                      E::pack(dp[o + 4], dp[o + 5]), E::pack(dp[o + 6], dp[o + 7]));
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) {
-            const int ro = (32 * mb + l32) * TSTR + 16 * kt + 4 * hl;
-            const uint2 dlo = *reinterpret_cast<const uint2*>(Dt + ro);
-            const uint2 dhi = *reinterpret_cast<const uint2*>(Dt + ro + 8);
-            const uint2 qlo = *reinterpret_cast<const uint2*>(Qt + ro);
-            const uint2 qhi = *reinterpret_cast<const uint2*>(Qt + ro + 8);
-            dva[mb] = E::mfma(make_uint4(dlo.x, dlo.y, dhi.x, dhi.y), pp, dva[mb]);
-            dka[mb] = E::mfma(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y), ps, dka[mb]);
-          }
-        }
-
-        if (has_next) store_chunk(buf ^ 1);
-        __syncthreads();
         if (!has_next) break;
         hh = nhh;
         e = ne;
@@ -348,16 +341,49 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dkdv_kernel(const BwdArgs a
         c = nc;
         i = ni;
         nch = nnch;
-        buf ^= 1;
+        if (NBUF == 2) buf ^= 1;
       }
     }
   }
 
+  int outkey = mykey;
+  bool out_live = key_live;
+  if (RG == 2) {
+    // row group 1 hands its sums to row group 0 through LDS, then writes the
+    // zero gradients of the sub-tile's other (padded) keys
+    // one accumulator set at a time: [KS waves][64 values][64 lanes] of fp32
+    static_assert(S::KS * 64 * 64 * 4 <= S::LDS, "reduction fits in the tiles' LDS");
+    float* red = reinterpret_cast<float*>(smem) + kslot * 64 * 64 + lane;
+    auto reduce = [&](f32x16_t(&acc)[4]) {
+      __syncthreads();
+      if (live > 0 && rg == 1) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[(mb * 16 + r) * 64] = acc[mb][r];
+      }
+      __syncthreads();
+      if (live > 0 && rg == 0) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mb][r] += red[(mb * 16 + r) * 64];
+      }
+    };
+    reduce(dka);
+    reduce(dva);
+    if (rg == 1) {
+      outkey = k0 + KW + 32 * kslot + (lane & 31);
+      out_live = false;
+    }
+  }
+
   // ---- epilogue: dk = scale * dK + dK_c / valid, dv = dV + dV_c / valid ----
-  if (!key_ok) return;
+  if (outkey >= kexist || outkey >= k0 + unit) return;
+  const long long koff = kbase + (long long)outkey * krs;
   const float* dkc = a.dkc ? a.dkc + g.pk(b, hk, j) : nullptr;
   const float* dvc = a.dvc ? a.dvc + g.pk(b, hk, j) : nullptr;
-  const float invn = (key_live && dkc) ? 1.f / (float)nval : 0.f;
+  const float invn = (out_live && dkc) ? 1.f / (float)nval : 0.f;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -366,10 +392,10 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dkdv_kernel(const BwdArgs a
       float kx[4], vx[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        kx[u] = key_live ? g.scale * dka[mb][4 * q4 + u] : 0.f;
-        vx[u] = key_live ? dva[mb][4 * q4 + u] : 0.f;
+        kx[u] = out_live ? g.scale * dka[mb][4 * q4 + u] : 0.f;
+        vx[u] = out_live ? dva[mb][4 * q4 + u] : 0.f;
       }
-      if (dkc && key_live) {
+      if (dkc && out_live) {
         const float4 ck = *reinterpret_cast<const float4*>(dkc + d0);
         const float4 cv = *reinterpret_cast<const float4*>(dvc + d0);
         kx[0] += ck.x * invn;
@@ -391,24 +417,19 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dkdv_kernel(const BwdArgs a
 // ---------------------------------------------------------------------------
 // dQ (Q-owned)
 // ---------------------------------------------------------------------------
-constexpr int KC = 64;
-constexpr int KSTR = HD + 8;
-constexpr int KTSTR = KC + 4;
-constexpr int DQ_STAGE = 2 * KC * KSTR + HD * KTSTR;  // K, V row-major + K^T
+constexpr int KC = 64;             // keys per chunk
+constexpr int KTILE = KC * HD * 2;
 
 template <class ET, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void sparse_dq_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) {
   using E = Elem<ET>;
-  constexpr int NT = NW * 64;
-  constexpr int KU = (KC * HD / 8) / NT;
-  constexpr int TU = (KC / 4) * (HD / 8) / NT;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * DQ_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * KTILE];  // [stage][K | V]
 
   const Geom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
   const int nsub = g.q_block / (32 * NW);
-  int id = xcd_remap(blockIdx.x, gridDim.x);
+  int id = xcd_group(blockIdx.x, gridDim.x, nsub);
   const int sub = id % nsub;
   id /= nsub;
   const int i = id % g.Qb;
@@ -431,13 +452,10 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dq_kernel(const BwdArgs a) 
     dor[ks] = row_ok ? ldg16(a.dout + qoff + 16 * ks + 8 * hl) : make_uint4(0, 0, 0, 0);
   }
   const long long lrow = g.lse_base(b, h) + blk0 + myrow;
-  float lse2 = INFINITY, drv = 0.f;
-  if (row_ok) {
-    const float l = a.lse[lrow];
-    lse2 = l == -INFINITY ? INFINITY : l * LOG2E;
-    drv = a.dr[lrow];
-  }
+  const float lse2 = row_ok ? a.lse2[lrow] : INFINITY;
+  const float drv = row_ok ? a.dr[lrow] : 0.f;
   const float c2 = g.scale * LOG2E;
+  const TrLane tl(lane);
 
   f32x16_t acc[4];
 #pragma unroll
@@ -447,66 +465,25 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dq_kernel(const BwdArgs a) 
 
   const long long rid = ((long long)b * g.Hq + h) * g.Qb + i;
   const int e0 = a.row_ptr[rid], e1 = a.row_ptr[rid + 1];
-  uint4 kst[KU], vst[KU], tst[TU][4];
 
-  auto load_chunk = [&](int j, int c, int nval) {
+  auto stage = [&](int buf, int j, int c, int nval) {
     const int t0 = j * g.kv_block + c * KC;
-    const int rem = nval - c * KC;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int idx = tid + u * NT, key = idx >> 4, dq = idx & 15;
-      const bool ok = key < rem;
-      const long long off = kvb + (long long)(t0 + key) * krs + 8 * dq;
-      kst[u] = ok ? ldg16(a.k + off) : make_uint4(0, 0, 0, 0);
-      vst[u] = ok ? ldg16(a.v + off) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < TU; ++u) {
-      const int it = tid + u * NT, dg = it & 15, kg = it >> 4;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = 4 * kg + rr;
-        tst[u][rr] = key < rem ? ldg16(a.k + kvb + (long long)(t0 + key) * krs + 8 * dg)
-                               : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_chunk = [&](int buf) {
-    uint16_t* Ks = smem + buf * DQ_STAGE;
-    uint16_t* Vs = Ks + KC * KSTR;
-    uint16_t* Kt = Vs + KC * KSTR;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int idx = tid + u * NT, key = idx >> 4, dq = idx & 15;
-      *reinterpret_cast<uint4*>(Ks + key * KSTR + 8 * dq) = kst[u];
-      *reinterpret_cast<uint4*>(Vs + key * KSTR + 8 * dq) = vst[u];
-    }
-#pragma unroll
-    for (int u = 0; u < TU; ++u) {
-      const int it = tid + u * NT, dg = it & 15, kg = it >> 4;
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&tst[u][0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&tst[u][1]);
-      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&tst[u][2]);
-      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&tst[u][3]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint2 even, odd;
-        even.x = (r0[w] & 0xffffu) | (r1[w] << 16);
-        even.y = (r2[w] & 0xffffu) | (r3[w] << 16);
-        odd.x = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-        odd.y = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-        *reinterpret_cast<uint2*>(Kt + (8 * dg + 2 * w) * KTSTR + 4 * kg) = even;
-        *reinterpret_cast<uint2*>(Kt + (8 * dg + 2 * w + 1) * KTSTR + 4 * kg) = odd;
-      }
-    }
+    const int last = nval - c * KC - 1;
+    uint8_t* Ks = smem + buf * 2 * KTILE;
+    stage_tile<KC, NW>(Ks, wave, lane, [&](int row) {
+      return a.k + kvb + (long long)(t0 + min(row, last)) * krs;
+    });
+    stage_tile<KC, NW>(Ks + KTILE, wave, lane, [&](int row) {
+      return a.v + kvb + (long long)(t0 + min(row, last)) * krs;
+    });
   };
 
   if (e0 < e1) {
     int e = e0, c = 0;
     int j = a.col[e];
     int nval = g.kv_val(b, j);
-    load_chunk(j, c, nval);
-    store_chunk(0);
+    stage(0, j, 0, nval);
+    wait_vmem();
     __syncthreads();
     int buf = 0;
     while (true) {
@@ -520,30 +497,30 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dq_kernel(const BwdArgs a) 
         }
       }
       const bool has_next = ne < e1;
-      if (has_next) load_chunk(nj, nc, nnval);
+      if (has_next) stage(buf ^ 1, nj, nc, nnval);
 
-      const uint16_t* Ks = smem + buf * DQ_STAGE;
-      const uint16_t* Vs = Ks + KC * KSTR;
-      const uint16_t* Kt = Vs + KC * KSTR;
+      const uint8_t* Ks = smem + buf * 2 * KTILE;
+      const uint8_t* Vs = Ks + KTILE;
       f32x16_t s0, s1, p0, p1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s0[r] = s1[r] = p0[r] = p1[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int o0 = l32 * KSTR + 16 * ks + 8 * hl, o1 = o0 + 32 * KSTR;
-        s0 = E::mfma(*reinterpret_cast<const uint4*>(Ks + o0), qr[ks], s0);
-        s1 = E::mfma(*reinterpret_cast<const uint4*>(Ks + o1), qr[ks], s1);
-        p0 = E::mfma(*reinterpret_cast<const uint4*>(Vs + o0), dor[ks], p0);
-        p1 = E::mfma(*reinterpret_cast<const uint4*>(Vs + o1), dor[ks], p1);
+        s0 = E::mfma(row16(Ks, l32, 2 * ks + hl), qr[ks], s0);
+        s1 = E::mfma(row16(Ks, 32 + l32, 2 * ks + hl), qr[ks], s1);
+        p0 = E::mfma(row16(Vs, l32, 2 * ks + hl), dor[ks], p0);
+        p1 = E::mfma(row16(Vs, 32 + l32, 2 * ks + hl), dor[ks], p1);
       }
       const int rem = nval - c * KC;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
         float a0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, -lse2));
         float a1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, -lse2));
-        if (key >= rem) a0 = 0.f;
-        if (key + 32 >= rem) a1 = 0.f;
+        if (rem < KC) {
+          const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key >= rem) a0 = 0.f;
+          if (key + 32 >= rem) a1 = 0.f;
+        }
         s0[r] = a0 * (p0[r] - drv);
         s1[r] = a1 * (p1[r] - drv);
       }
@@ -555,14 +532,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_dq_kernel(const BwdArgs a) 
         const uint4 pb = make_uint4(E::pack(s[o], s[o + 1]), E::pack(s[o + 2], s[o + 3]),
                                     E::pack(s[o + 4], s[o + 5]), E::pack(s[o + 6], s[o + 7]));
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const uint16_t* kp = Kt + (32 * mb + l32) * KTSTR + 16 * kt + 4 * hl;
-          const uint2 lo = *reinterpret_cast<const uint2*>(kp);
-          const uint2 hi = *reinterpret_cast<const uint2*>(kp + 8);
-          acc[mb] = E::mfma(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[mb]);
-        }
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = E::mfma(tr_operand(Ks, tl, 16 * kt, mb), pb, acc[mb]);
       }
-      if (has_next) store_chunk(buf ^ 1);
+      wait_vmem();
       __syncthreads();
       if (!has_next) break;
       e = ne;
@@ -614,11 +586,15 @@ hipError_t launch_pre_t(const PreArgs& a, hipStream_t st) {
 template <class ET>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
-  const int nw = (g.kv_block % 128 == 0) ? 4 : 2;
-  const long long nwg = (long long)g.B * g.Hkv * g.KVb * (g.kv_block / (32 * nw));
-  if (nwg == 0) return hipSuccess;
-  if (nw == 4) sparse_dkdv_kernel<ET, 4><<<(unsigned)nwg, 256, 0, st>>>(a);
-  else sparse_dkdv_kernel<ET, 2><<<(unsigned)nwg, 128, 0, st>>>(a);
+  const long long tiles = (long long)g.B * g.Hkv * g.KVb;
+  if (tiles == 0) return hipSuccess;
+  if (g.kv_block % 128 == 0) {
+    const unsigned n = (unsigned)(tiles * (g.kv_block / 128));
+    sparse_dkdv_kernel<ET, 4, 1, 2><<<n, 256, 0, st>>>(a, DKDV_WIDE);
+    sparse_dkdv_kernel<ET, 4, 2, 1><<<n, 256, 0, st>>>(a, DKDV_NARROW);
+  } else {
+    sparse_dkdv_kernel<ET, 2, 1, 2><<<(unsigned)(tiles * (g.kv_block / 64)), 128, 0, st>>>(a, DKDV_ALL);
+  }
   return hipGetLastError();
 }
 

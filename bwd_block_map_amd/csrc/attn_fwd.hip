@@ -9,41 +9,36 @@
 //
 // gfx950 design. One work-group = NW waves x 32 rows of one Q block; every
 // wave keeps its 32 query rows in registers as MFMA B operands and walks the
-// block's KV list in chunks of 64 keys staged through LDS (double-buffered:
-// the next chunk's global loads are issued before this chunk's MFMAs and
-// written to the other LDS stage after them). Scores are formed transposed,
-// S^T = K Q^T with v_mfma_f32_32x32x16, so each lane owns one query row and
-// the row max / sum are in-lane plus one exchange with lane ^ 32. P^T feeds
-// O^T += V^T P^T directly from registers: the MFMA contraction order is free,
-// so the (4 keys, 4 keys) split of each lane's P values is matched by reading
-// V^T from LDS at the same key positions. V is transposed once, while it is
-// written to LDS. The chunk loop of a KV block stops after ceil(valid/64)
-// chunks; only a partial last chunk runs the key mask.
+// block's KV list in chunks of 64 keys. K and V chunks go global -> LDS with
+// direct 16-byte loads (no staging registers), double-buffered: the next
+// chunk is in flight while this one is computed. Scores are formed
+// transposed, S^T = K Q^T with v_mfma_f32_32x32x16, so each lane owns one
+// query row and the row max / sum are in-lane plus one exchange with lane ^ 32.
+// P^T stays in registers as the B operand of O^T += V^T P^T; the V^T operand
+// comes straight from the row-major V tile through ds_read_b64_tr_b16, in the
+// key order that matches the lane's P values. The chunk loop of a KV block
+// stops after ceil(valid/64) chunks; only a partial last chunk runs the mask.
 #include "kernels.hpp"
+#include "lds_tiles.hpp"
 
 namespace vsa {
 
 namespace {
 
-constexpr int KC = 64;         // keys per chunk
-constexpr int KSTR = HD + 8;   // LDS row stride of K (elements): 272 B, conflict-free b128 reads
-constexpr int VSTR = KC + 4;   // LDS row stride of V^T (elements): 136 B, conflict-free b64 reads
-constexpr int STAGE = KC * KSTR + HD * VSTR;  // elements per LDS stage
+constexpr int KC = 64;             // keys per chunk
+constexpr int TILE = KC * HD * 2;  // bytes of one 64-row tile
 
 template <class ET, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a) {
   using E = Elem<ET>;
-  constexpr int NT = NW * 64;
-  constexpr int KU = (KC * HD / 8) / NT;  // 16-byte K pieces per thread
-  constexpr int VU = (KC / 4) * (HD / 8) / NT;  // (4 keys x 8 d) V pieces per thread
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TILE];  // [stage][K | V]
 
   const Geom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
 
   const int nsub = g.q_block / (32 * NW);
-  int id = xcd_remap(blockIdx.x, gridDim.x);
+  int id = xcd_group(blockIdx.x, gridDim.x, nsub);
   const int sub = id % nsub;
   id /= nsub;
   const int i = id % g.Qb;
@@ -77,67 +72,28 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
+  const TrLane tl(lane);
 
-  uint4 kst[KU];
-  uint4 vst[VU][4];
-
-  // global -> registers for chunk c of KV block j (keys >= nval read as zero)
-  auto load_chunk = [&](int j, int c, int nval) {
+  // global -> LDS for chunk c of KV block j (rows past the valid keys repeat
+  // the last valid row: in bounds, and masked out of the softmax)
+  auto stage = [&](int buf, int j, int c, int nval) {
     const int t0 = j * g.kv_block + c * KC;
-    const int rem = nval - c * KC;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int idx = tid + u * NT, key = idx >> 4, dq = idx & 15;
-      kst[u] = key < rem ? ldg16(a.k + kvb + (long long)(t0 + key) * krs + 8 * dq)
-                         : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int it = tid + u * NT, dg = it & 15, kg = it >> 4;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = 4 * kg + rr;
-        vst[u][rr] = key < rem ? ldg16(a.v + kvb + (long long)(t0 + key) * krs + 8 * dg)
-                               : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  // registers -> LDS stage: K row-major, V transposed (V^T[d][key])
-  auto store_chunk = [&](int buf) {
-    uint16_t* Ks = smem + buf * STAGE;
-    uint16_t* Vt = Ks + KC * KSTR;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int idx = tid + u * NT, key = idx >> 4, dq = idx & 15;
-      *reinterpret_cast<uint4*>(Ks + key * KSTR + 8 * dq) = kst[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int it = tid + u * NT, dg = it & 15, kg = it >> 4;
-      const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vst[u][0]);
-      const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vst[u][1]);
-      const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vst[u][2]);
-      const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vst[u][3]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // d = 8dg + 2w (low halves) and 8dg + 2w + 1 (high halves)
-        uint2 even, odd;
-        even.x = (r0[w] & 0xffffu) | (r1[w] << 16);
-        even.y = (r2[w] & 0xffffu) | (r3[w] << 16);
-        odd.x = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-        odd.y = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-        *reinterpret_cast<uint2*>(Vt + (8 * dg + 2 * w) * VSTR + 4 * kg) = even;
-        *reinterpret_cast<uint2*>(Vt + (8 * dg + 2 * w + 1) * VSTR + 4 * kg) = odd;
-      }
-    }
+    const int last = nval - c * KC - 1;
+    uint8_t* Ks = smem + buf * 2 * TILE;
+    stage_tile<KC, NW>(Ks, wave, lane, [&](int row) {
+      return a.k + kvb + (long long)(t0 + min(row, last)) * krs;
+    });
+    stage_tile<KC, NW>(Ks + TILE, wave, lane, [&](int row) {
+      return a.v + kvb + (long long)(t0 + min(row, last)) * krs;
+    });
   };
 
   if (e0 < e1) {
     int e = e0, c = 0;
     int j = a.col[e];
     int nval = g.kv_val(b, j);
-    load_chunk(j, c, nval);
-    store_chunk(0);
+    stage(0, j, 0, nval);
+    wait_vmem();
     __syncthreads();
     int buf = 0;
     while (true) {
@@ -152,21 +108,18 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
         }
       }
       const bool has_next = ne < e1;
-      if (has_next) load_chunk(nj, nc, nnval);
+      if (has_next) stage(buf ^ 1, nj, nc, nnval);
 
       // ---- this chunk: S^T = K Q^T (2 x 32 keys by 32 rows) ----
-      const uint16_t* Ks = smem + buf * STAGE;
-      const uint16_t* Vt = Ks + KC * KSTR;
+      const uint8_t* Ks = smem + buf * 2 * TILE;
+      const uint8_t* Vs = Ks + TILE;
       f32x16_t s0, s1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const uint4 a0 = *reinterpret_cast<const uint4*>(Ks + l32 * KSTR + 16 * ks + 8 * hl);
-        const uint4 a1 =
-            *reinterpret_cast<const uint4*>(Ks + (32 + l32) * KSTR + 16 * ks + 8 * hl);
-        s0 = E::mfma(a0, qr[ks], s0);
-        s1 = E::mfma(a1, qr[ks], s1);
+        s0 = E::mfma(row16(Ks, l32, 2 * ks + hl), qr[ks], s0);
+        s1 = E::mfma(row16(Ks, 32 + l32, 2 * ks + hl), qr[ks], s1);
       }
       // lane holds keys 8(r/4) + 4hl + (r%4) (+32 for s1) of its row
       const int rem = nval - c * KC;
@@ -184,8 +137,6 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
       mx = xhalf_max(mx);
       const float mnew = fmaxf(m_run, mx);
       const float msc = mnew == -INFINITY ? 0.f : mnew * c2;
-      const float alpha = __builtin_amdgcn_exp2f(m_run * c2 - msc);
-      m_run = mnew;
       float lsum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -193,32 +144,29 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
         s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, -msc));
         lsum += s0[r] + s1[r];
       }
-      l_run = l_run * alpha + lsum;
+      if (mnew > m_run) {  // rescale only when the running max moved
+        const float alpha = __builtin_amdgcn_exp2f(m_run * c2 - msc);
+        l_run *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+      }
+      m_run = mnew;
+      l_run += lsum;
 
       // ---- O^T += V^T P^T: 4 key steps of 16 ----
-      uint4 pb[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const f32x16_t& s = (kt < 2) ? s0 : s1;
         const int o = 8 * (kt & 1);
-        pb[kt] = make_uint4(E::pack(s[o + 0], s[o + 1]), E::pack(s[o + 2], s[o + 3]),
-                            E::pack(s[o + 4], s[o + 5]), E::pack(s[o + 6], s[o + 7]));
+        const uint4 pb = make_uint4(E::pack(s[o + 0], s[o + 1]), E::pack(s[o + 2], s[o + 3]),
+                                    E::pack(s[o + 4], s[o + 5]), E::pack(s[o + 6], s[o + 7]));
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = E::mfma(tr_operand(Vs, tl, 16 * kt, mb), pb, acc[mb]);
       }
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const uint16_t* vp = Vt + (32 * mb + l32) * VSTR + 16 * kt + 4 * hl;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-          acc[mb] = E::mfma(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[kt], acc[mb]);
-        }
 
-      if (has_next) store_chunk(buf ^ 1);
+      wait_vmem();
       __syncthreads();
       if (!has_next) break;
       e = ne;

@@ -147,14 +147,18 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Work-group order: the hardware deals consecutive work-group ids round-robin
-// to the 8 XCDs (each with its own L2). Remap so that each XCD receives a
-// contiguous range of logical ids (neighbouring tiles of one head share an L2).
-__device__ __forceinline__ int xcd_remap(int id, int n) {
+// Work-group order. The hardware deals consecutive work-group ids round-robin
+// to the 8 XCDs (each with its own L2), so consecutive ids run on different
+// XCDs at the same time. Keep that sweep (all XCDs work through the same head
+// together, so the Infinity Cache holds one head's operands), but hand each
+// group of G consecutive logical ids to one XCD, so the work-groups that read
+// the same tile (the sub-tiles of one block) share an L2.
+__device__ __forceinline__ int xcd_group(int p, int n, int G) {
   constexpr int X = 8;
-  const int per = n / X, rem = n % X, xcd = id % X, k = id / X;
-  // xcds < rem own per + 1 ids, the others per
-  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + k;
+  const int full = n / (X * G) * (X * G);
+  if (p >= full) return p;  // ragged tail: keep the hardware order
+  const int q = p / X;
+  return ((q / G) * X + p % X) * G + q % G;
 }
 
 constexpr float LOG2E = 1.4426950408889634f;

@@ -28,7 +28,7 @@ struct BwdArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* lse;
+  const float* lse2;       // lse * log2(e), +inf for rows without a live key
   const float* dr;         // rowsum(dO * O_sel), laid out like lse
   const int32_t* row_ptr;  // Q-owned (dQ) or KV-owned (dK/dV) CSR
   const int32_t* col;
@@ -48,7 +48,9 @@ struct PreArgs {
   const uint16_t* gate;
   const float* oc;
   int gate_mode;
+  const float* lse;
   float* dr;
+  float* lse2;
   float* doc;       // gate: [B,Hq,Qb,HD] sum over the tile of gate * dO
   uint16_t* dgate;  // gate: optional
 };

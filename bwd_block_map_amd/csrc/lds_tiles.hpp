@@ -1,0 +1,123 @@
+// LDS tiles of 16-bit rows of HD = 128 elements (256 B = 16 chunks of 16 B)
+// for the MFMA kernels, filled by direct global->LDS loads and read either
+// row-wise (an MFMA operand whose contraction runs along d) or transposed
+// with ds_read_b64_tr_b16 (an operand whose contraction runs along the rows).
+//
+// Swizzle: chunk c of row r is stored at chunk c ^ swz(r), with swz swapping
+// the two low 2-bit fields of r. Then 16 consecutive rows read at one chunk hit
+// 16 distinct chunk slots (row-wise 16-byte reads), and the transposed read of
+// 4 consecutive rows x 4 consecutive chunks also hits 16 distinct slots.
+#pragma once
+
+#include "common.hpp"
+
+namespace vsa {
+
+typedef __attribute__((ext_vector_type(4))) short short4_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// byte offset of chunk c of row r inside a tile
+__device__ __forceinline__ uint32_t toff(int r, int c) {
+  return (uint32_t)(r * 256 + ((c ^ swz(r)) << 4));
+}
+
+// Stage RT rows into a tile with direct 16-byte global->LDS loads. Each wave
+// instruction fills 4 rows (1 KiB); lane l writes physical chunk l & 15 of
+// row 4p + (l >> 4), so it fetches logical chunk (l & 15) ^ swz(row).
+// src(row) returns the global address of element 0 of that tile row.
+template <int RT, int NW, class F>
+__device__ __forceinline__ void stage_tile(uint8_t* tile, int wave, int lane, F src) {
+#pragma unroll
+  for (int p = wave; p < RT / 4; p += NW) {
+    const int row = 4 * p + (lane >> 4);
+    const int c = (lane & 15) ^ swz(row);
+    __builtin_amdgcn_global_load_lds((const void*)(src(row) + 8 * c), (void*)(tile + p * 1024), 16,
+                                     0, 0);
+  }
+}
+
+// Stage N <= 64 consecutive fp32 values with one wave instruction: lane i
+// (i < N) writes word i of dst; entries past `last` repeat entry `last`.
+template <int N>
+__device__ __forceinline__ void stage_f32(float* dst, const float* src, int lane, int last) {
+  static_assert(N <= 64, "one wave instruction");
+  if (lane < N)
+    __builtin_amdgcn_global_load_lds((const void*)(src + min(lane, last)), (void*)dst, 4, 0, 0);
+}
+
+// all outstanding vector-memory operations (including direct LDS fills) done
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Row-wise MFMA operand: lane reads 8 elements (16 B) of row r, chunk c.
+__device__ __forceinline__ uint4 row16(const uint8_t* tile, int r, int c) {
+  return *reinterpret_cast<const uint4*>(tile + toff(r, c));
+}
+
+// Per-lane byte offsets of the row-wise operand reads. A wave reads rows
+// R + (lane & 31) (R a multiple of 16, so the swizzle depends on the lane
+// only) at chunk 2ks + (lane >> 5): offset = R*256 + o[ks].
+struct RowOffs {
+  uint32_t o[8];
+  __device__ __forceinline__ explicit RowOffs(int lane) {
+    const int r = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) o[ks] = toff(r, 2 * ks + hl);
+  }
+  __device__ __forceinline__ uint4 at(const uint8_t* tile, int R, int ks) const {
+    return *reinterpret_cast<const uint4*>(tile + R * 256 + o[ks]);
+  }
+};
+
+__device__ __forceinline__ uint2 tr8(const uint8_t* tile, uint32_t off) {
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(tile + off));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Transposed A operand of a 32x32x16 MFMA whose M index is d (32*mb + lane%32)
+// and whose contraction runs over tile rows rb .. rb+15, in the lane order the
+// transposed accumulators use: k-slot e (0..3) of lane half hl is row
+// rb + 4hl + e, k-slot 4 + e is row rb + 8 + 4hl + e. ds_read_b64_tr_b16 works
+// on 16-lane groups: source lane 4e + i reads 4 elements (d = D0 + 4i .. +3) of
+// row e; result lane 4i + c receives element c of the four rows.
+struct TrLane {
+  uint32_t row_off;  // (4hl + e) rows, as a row index
+  int c_off;         // 2g + (i >> 1)
+  uint32_t half;     // 8 * (i & 1) bytes
+  __device__ __forceinline__ explicit TrLane(int lane) {
+    const int s = lane & 15, e = s >> 2, i = s & 3, g = (lane >> 4) & 1, hl = lane >> 5;
+    row_off = (uint32_t)(4 * hl + e);
+    c_off = 2 * g + (i >> 1);
+    half = 8u * (uint32_t)(i & 1);
+  }
+};
+
+__device__ __forceinline__ uint4 tr_operand(const uint8_t* tile, const TrLane& t, int rb, int mb) {
+  const int r = rb + (int)t.row_off, c = 4 * mb + t.c_off;
+  const uint2 lo = tr8(tile, toff(r, c) + t.half);
+  const uint2 hi = tr8(tile, toff(r + 8, c) + t.half);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// Per-lane byte offsets of the transposed operand reads: rows rb + {0..15}
+// with rb a multiple of 16, so for each (low / high row group, mb) the offset
+// is rb*256 + o[hi][mb].
+struct TrOffs {
+  uint32_t o[2][4];
+  __device__ __forceinline__ explicit TrOffs(int lane) {
+    const TrLane t(lane);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        o[hi][mb] = toff((int)t.row_off + 8 * hi, 4 * mb + t.c_off) + t.half;
+  }
+  __device__ __forceinline__ uint4 at(const uint8_t* tile, int rb, int mb) const {
+    const uint2 lo = tr8(tile, (uint32_t)(rb * 256) + o[0][mb]);
+    const uint2 hi = tr8(tile, (uint32_t)(rb * 256) + o[1][mb]);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+};
+
+}  // namespace vsa

@@ -177,6 +177,7 @@ FwdWs carve_fwd(const vsa_problem* p, void* base, size_t* bytes) {
 
 struct BwdWs {
   float* dr;
+  float* lse2;
   float* doc;
   float* dqc;
   float* dkc;
@@ -189,6 +190,7 @@ BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
   Carver c(base);
   BwdWs w{};
   w.dr = c.take<float>(std::max(rows_total(p), 1LL));
+  w.lse2 = c.take<float>(std::max(rows_total(p), 1LL));
   if (p->gate_mode != VSA_GATE_NONE) {
     w.doc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
     w.dqc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
@@ -470,7 +472,9 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   pa.gate = (const uint16_t*)gate;
   pa.oc = s.oc;
   pa.gate_mode = p->gate_mode;
+  pa.lse = lse;
   pa.dr = w.dr;
+  pa.lse2 = w.lse2;
   pa.doc = w.doc;
   pa.dgate = (uint16_t*)dgate;
   {
@@ -505,7 +509,7 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   ba.k = (const uint16_t*)k;
   ba.v = (const uint16_t*)v;
   ba.dout = (const uint16_t*)dout;
-  ba.lse = lse;
+  ba.lse2 = w.lse2;
   ba.dr = w.dr;
   ba.dqc = gated ? w.dqc : nullptr;
   ba.dkc = gated ? w.dkc : nullptr;
