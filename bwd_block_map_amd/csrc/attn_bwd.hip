@@ -123,54 +123,63 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
 // ---------------------------------------------------------------------------
 // dK / dV (KV-owned)
 // ---------------------------------------------------------------------------
-// Which 128-key sub-tiles a launch owns: sub-tiles with more than 64 live keys
-// go to the wide launch (4 waves x 32 keys), the others (the partial video
-// tiles) to a narrow launch over their first 64 keys, where the 4 waves form
-// 2 key slots x 2 row groups (each chunk's rows are split, and the two row
-// groups' sums are added through LDS at the end), so no wave sits on absent keys.
-enum DkdvPart { DKDV_ALL = 0, DKDV_WIDE = 1, DKDV_NARROW = 2 };
+// One work-group of 8 waves owns a span of up to 256 keys of a KV block and
+// walks every (head of the group, selecting Q block, row chunk). Each wave
+// keeps dK^T and dV^T of 32 keys in registers. A span picks the narrowest of
+// three shapes that covers its live keys, so no wave sits on absent keys:
+//   KS = 8 key slots x 1 row group  (256 keys, 32-row chunks)
+//   KS = 4 key slots x 2 row groups (128 keys, 64-row chunks)
+//   KS = 2 key slots x 4 row groups ( 64 keys, 128-row chunks)
+// Each row group takes 32 rows of a chunk; the row groups' sums are added
+// through LDS at the end. One launch per shape; a work-group whose span has
+// another shape returns at once.
+constexpr int DKDV_NW = 8;
+constexpr int DKDV_SPAN = 256;
 
-template <int NW, int RG, int NBUF>
+template <int KS>
 struct DkdvShape {
-  static constexpr int KS = NW / RG;          // key slots (32 keys each)
-  static constexpr int KW = 32 * KS;          // keys of the work-group
-  static constexpr int QC = 32 * RG;          // query rows per chunk
-  static constexpr int QT = QC * HD * 2;      // bytes of a QC-row tile
-  static constexpr int STAGE = 2 * QT + 2 * QC * 4;  // Q | dO | lse2 | dr
-  static constexpr int LDS = NBUF * STAGE + KW * HD * 2;  // stages, then the K tile
+  static constexpr int NW = DKDV_NW;
+  static constexpr int RG = NW / KS;                  // row groups
+  static constexpr int KW = 32 * KS;                  // keys of the work-group
+  static constexpr int QC = 32 * RG;                  // query rows per chunk
+  static constexpr int QT = QC * HD * 2;              // bytes of a QC-row tile
+  static constexpr int STAGE = 2 * QT + 2 * QC * 4;   // Q | dO | lse2 | dr
+  static constexpr int LDS = 2 * STAGE + KW * HD * 2;  // two stages, then the K tile
+  static_assert(NW % KS == 0, "whole row groups");
+  static_assert((RG - 1) * KS * 64 * 64 * 4 <= LDS, "row-group reduction fits in LDS");
 };
 
-template <class ET, int NW, int RG, int NBUF>
-__global__ __launch_bounds__(NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a, int part) {
+__device__ __forceinline__ int dkdv_shape(int live) { return live > 128 ? 8 : live > 64 ? 4 : 2; }
+
+template <class ET, int KS>
+__global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a) {
   using E = Elem<ET>;
-  using S = DkdvShape<NW, RG, NBUF>;
-  constexpr int QC = S::QC, QT = S::QT, STAGE = S::STAGE, KW = S::KW;
+  using S = DkdvShape<KS>;
+  constexpr int NW = S::NW, RG = S::RG, QC = S::QC, QT = S::QT, STAGE = S::STAGE, KW = S::KW;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS];
 
   const Geom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5;
-  const int kslot = wave % S::KS, rg = wave / S::KS;
-  const int unit = part == DKDV_ALL ? KW : 128;  // keys per grid sub-tile
-  const int nsub = g.kv_block / unit;
-  int id = xcd_group(blockIdx.x, gridDim.x, nsub);
-  const int sub = id % nsub;
-  id /= nsub;
+  const int kslot = wave % KS, rg = wave / KS;
+  const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
+  int id = xcd_group(blockIdx.x, gridDim.x, nspan);
+  const int span = id % nspan;
+  id /= nspan;
   const int j = id % g.KVb;
   id /= g.KVb;
   const int hk = id % g.Hkv, b = id / g.Hkv;
 
-  const int kexist = g.kv_exist(b, j);
-  const int k0 = sub * unit;
-  if (k0 >= kexist) return;  // no key of this sub-tile exists
+  const int k0 = span * DKDV_SPAN;
+  const int kend = min(g.kv_exist(b, j), min(g.kv_block, k0 + DKDV_SPAN));  // existing keys < kend
+  if (k0 >= kend) return;
   const int nval = g.kv_val(b, j);
-  const int live = max(0, min(unit, nval - k0));  // live keys of the sub-tile
-  if (part == DKDV_WIDE && live > 0 && live <= 64) return;
-  if (part == DKDV_NARROW && !(live > 0 && live <= 64)) return;
+  const int live = max(0, min(kend, nval) - k0);  // live keys of the span
+  if (dkdv_shape(live) != KS) return;
   const long long krs = g.kv_rs();
   const long long kbase = g.kv_base(b, hk) + (long long)j * g.kv_block * krs;
   const int mykey = k0 + 32 * kslot + (lane & 31);  // key inside the KV block
-  const bool key_live = mykey < nval;
+  const bool key_live = mykey < k0 + live;
 
   f32x16_t dka[4], dva[4];
 #pragma unroll
@@ -180,9 +189,9 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a
 
   if (live > 0) {
     // the work-group's K rows stay in LDS for the whole walk (rows past the
-    // valid keys repeat the last valid one and are masked); V^T columns are
+    // live keys repeat the last live one and are masked); V^T columns are
     // register B operands (lane: key, d = 16ks + 8hl + 0..7)
-    uint8_t* Kt = smem + NBUF * STAGE;
+    uint8_t* Kt = smem + 2 * STAGE;
     const int lastk = min(live, KW) - 1;
     stage_tile<KW, NW>(Kt, wave, lane, [&](int row) {
       return a.k + kbase + (long long)(k0 + min(row, lastk)) * krs;
@@ -193,6 +202,7 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a
     for (int ks = 0; ks < 8; ++ks)
       vr[ks] = key_live ? ldg16(a.v + koff + 16 * ks + 8 * hl) : make_uint4(0, 0, 0, 0);
     const float kmask = key_live ? 0.f : -INFINITY;  // added to the exp2 argument
+    const bool wave_keys = 32 * kslot < live;        // this wave has a live key
     const float c2 = g.scale * LOG2E;
     const long long qrs = g.q_rs();
     const RowOffs ro(lane);
@@ -209,11 +219,18 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a
       stage_tile<QC, NW>(st + QT, wave, lane,
                          [&](int row) { return a.dout + base + min(row, last) * qrs; });
       const long long lb = g.lse_base(b, h) + i * g.q_block + c * QC;
-      if (wave == 0) stage_f32<QC>((float*)(st + 2 * QT), a.lse2 + lb, lane, last);
-      if (wave == NW - 1) stage_f32<QC>((float*)(st + 2 * QT) + QC, a.dr + lb, lane, last);
+      float* fl = reinterpret_cast<float*>(st + 2 * QT);
+      constexpr int NP = (QC + 63) / 64;  // 64-entry pieces of lse2 and of dr
+#pragma unroll
+      for (int pc = 0; pc < NP; ++pc) {
+        if (wave == pc) stage_f32<(QC < 64 ? QC : 64)>(fl + 64 * pc, a.lse2 + lb + 64 * pc, lane, last - 64 * pc);
+        if (wave == NW - 1 - pc)
+          stage_f32<(QC < 64 ? QC : 64)>(fl + QC + 64 * pc, a.dr + lb + 64 * pc, lane, last - 64 * pc);
+      }
     };
 
     auto compute = [&](int buf, int rows_valid) {
+      if (!wave_keys || rows_valid <= rb) return;  // nothing live for this wave
       const uint8_t* Qs = smem + buf * STAGE;
       const uint8_t* Ds = Qs + QT;
       const float* lse2 = reinterpret_cast<const float*>(Qs + 2 * QT);
@@ -319,21 +336,10 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a
           nch = snch;
         }
         const bool has_next = nhh < g.group;
-        const int rows_valid = g.q_exist(b, i) - c * QC;
-        if (NBUF == 2) {
-          if (has_next) stage(buf ^ 1, hk * g.group + nhh, ni, nc);
-          compute(buf, rows_valid);
-          wait_vmem();
-          __syncthreads();
-        } else {
-          compute(0, rows_valid);
-          __syncthreads();
-          if (has_next) {
-            stage(0, hk * g.group + nhh, ni, nc);
-            wait_vmem();
-            __syncthreads();
-          }
-        }
+        if (has_next) stage(buf ^ 1, hk * g.group + nhh, ni, nc);
+        compute(buf, g.q_exist(b, i) - c * QC);
+        wait_vmem();
+        __syncthreads();
         if (!has_next) break;
         hh = nhh;
         e = ne;
@@ -341,49 +347,53 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a
         c = nc;
         i = ni;
         nch = nnch;
-        if (NBUF == 2) buf ^= 1;
+        buf ^= 1;
       }
+    }
+
+    if (RG > 1) {
+      // row groups 1.. hand their sums to row group 0 through LDS, one
+      // accumulator set at a time: [RG-1][KS][64 values][64 lanes] of fp32
+      float* red = reinterpret_cast<float*>(smem);
+      auto reduce = [&](f32x16_t(&acc)[4]) {
+        __syncthreads();
+        if (rg > 0) {
+          float* w = red + ((rg - 1) * KS + kslot) * 4096 + lane;
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w[(mb * 16 + r) * 64] = acc[mb][r];
+        }
+        __syncthreads();
+        if (rg == 0) {
+#pragma unroll
+          for (int g2 = 1; g2 < RG; ++g2) {
+            const float* w = red + ((g2 - 1) * KS + kslot) * 4096 + lane;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[mb][r] += w[(mb * 16 + r) * 64];
+          }
+        }
+      };
+      reduce(dka);
+      reduce(dva);
     }
   }
 
-  int outkey = mykey;
-  bool out_live = key_live;
-  if (RG == 2) {
-    // row group 1 hands its sums to row group 0 through LDS, then writes the
-    // zero gradients of the sub-tile's other (padded) keys
-    // one accumulator set at a time: [KS waves][64 values][64 lanes] of fp32
-    static_assert(S::KS * 64 * 64 * 4 <= S::LDS, "reduction fits in the tiles' LDS");
-    float* red = reinterpret_cast<float*>(smem) + kslot * 64 * 64 + lane;
-    auto reduce = [&](f32x16_t(&acc)[4]) {
-      __syncthreads();
-      if (live > 0 && rg == 1) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) red[(mb * 16 + r) * 64] = acc[mb][r];
-      }
-      __syncthreads();
-      if (live > 0 && rg == 0) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mb][r] += red[(mb * 16 + r) * 64];
-      }
-    };
-    reduce(dka);
-    reduce(dva);
-    if (rg == 1) {
-      outkey = k0 + KW + 32 * kslot + (lane & 31);
-      out_live = false;
-    }
+  // keys of the span past the work-group's KW (absent or padded): zero gradients
+  for (int kk = k0 + KW + (tid >> 4); kk < kend; kk += NW * 4) {
+    const long long o = kbase + (long long)kk * krs + 8 * (tid & 15);
+    stg16(a.dk + o, make_uint4(0, 0, 0, 0));
+    stg16(a.dv + o, make_uint4(0, 0, 0, 0));
   }
 
   // ---- epilogue: dk = scale * dK + dK_c / valid, dv = dV + dV_c / valid ----
-  if (outkey >= kexist || outkey >= k0 + unit) return;
-  const long long koff = kbase + (long long)outkey * krs;
+  if (rg != 0 || mykey >= kend) return;
+  const long long koff = kbase + (long long)mykey * krs;
   const float* dkc = a.dkc ? a.dkc + g.pk(b, hk, j) : nullptr;
   const float* dvc = a.dvc ? a.dvc + g.pk(b, hk, j) : nullptr;
-  const float invn = (out_live && dkc) ? 1.f / (float)nval : 0.f;
+  const float invn = (key_live && dkc) ? 1.f / (float)nval : 0.f;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -392,10 +402,10 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a
       float kx[4], vx[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        kx[u] = out_live ? g.scale * dka[mb][4 * q4 + u] : 0.f;
-        vx[u] = out_live ? dva[mb][4 * q4 + u] : 0.f;
+        kx[u] = key_live ? g.scale * dka[mb][4 * q4 + u] : 0.f;
+        vx[u] = key_live ? dva[mb][4 * q4 + u] : 0.f;
       }
-      if (dkc && out_live) {
+      if (dkc && key_live) {
         const float4 ck = *reinterpret_cast<const float4*>(dkc + d0);
         const float4 cv = *reinterpret_cast<const float4*>(dvc + d0);
         kx[0] += ck.x * invn;
@@ -586,25 +596,22 @@ hipError_t launch_pre_t(const PreArgs& a, hipStream_t st) {
 template <class ET>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
-  const long long tiles = (long long)g.B * g.Hkv * g.KVb;
-  if (tiles == 0) return hipSuccess;
-  if (g.kv_block % 128 == 0) {
-    const unsigned n = (unsigned)(tiles * (g.kv_block / 128));
-    sparse_dkdv_kernel<ET, 4, 1, 2><<<n, 256, 0, st>>>(a, DKDV_WIDE);
-    sparse_dkdv_kernel<ET, 4, 2, 1><<<n, 256, 0, st>>>(a, DKDV_NARROW);
-  } else {
-    sparse_dkdv_kernel<ET, 2, 1, 2><<<(unsigned)(tiles * (g.kv_block / 64)), 128, 0, st>>>(a, DKDV_ALL);
-  }
+  const long long n = (long long)g.B * g.Hkv * g.KVb * ((g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN);
+  if (n == 0) return hipSuccess;
+  sparse_dkdv_kernel<ET, 8><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
+  sparse_dkdv_kernel<ET, 4><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
+  sparse_dkdv_kernel<ET, 2><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
 template <class ET>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
-  const int nw = (g.q_block % 128 == 0) ? 4 : (g.q_block % 64 == 0 ? 2 : 1);
+  const int nw = g.q_block % 256 == 0 ? 8 : g.q_block % 128 == 0 ? 4 : g.q_block % 64 == 0 ? 2 : 1;
   const long long nwg = (long long)g.B * g.Hq * g.Qb * (g.q_block / (32 * nw));
   if (nwg == 0) return hipSuccess;
-  if (nw == 4) sparse_dq_kernel<ET, 4><<<(unsigned)nwg, 256, 0, st>>>(a);
+  if (nw == 8) sparse_dq_kernel<ET, 8><<<(unsigned)nwg, 512, 0, st>>>(a);
+  else if (nw == 4) sparse_dq_kernel<ET, 4><<<(unsigned)nwg, 256, 0, st>>>(a);
   else if (nw == 2) sparse_dq_kernel<ET, 2><<<(unsigned)nwg, 128, 0, st>>>(a);
   else sparse_dq_kernel<ET, 1><<<(unsigned)nwg, 64, 0, st>>>(a);
   return hipGetLastError();

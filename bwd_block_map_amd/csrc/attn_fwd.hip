@@ -220,10 +220,11 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
 template <class ET>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
-  const int nw = (g.q_block % 128 == 0) ? 4 : (g.q_block % 64 == 0 ? 2 : 1);
+  const int nw = g.q_block % 256 == 0 ? 8 : g.q_block % 128 == 0 ? 4 : g.q_block % 64 == 0 ? 2 : 1;
   const long long nwg = (long long)g.B * g.Hq * g.Qb * (g.q_block / (32 * nw));
   if (nwg == 0) return hipSuccess;
-  if (nw == 4) sparse_fwd_kernel<ET, 4><<<(unsigned)nwg, 256, 0, st>>>(a);
+  if (nw == 8) sparse_fwd_kernel<ET, 8><<<(unsigned)nwg, 512, 0, st>>>(a);
+  else if (nw == 4) sparse_fwd_kernel<ET, 4><<<(unsigned)nwg, 256, 0, st>>>(a);
   else if (nw == 2) sparse_fwd_kernel<ET, 2><<<(unsigned)nwg, 128, 0, st>>>(a);
   else sparse_fwd_kernel<ET, 1><<<(unsigned)nwg, 64, 0, st>>>(a);
   return hipGetLastError();
