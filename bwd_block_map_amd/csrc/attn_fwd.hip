@@ -18,6 +18,8 @@
 // comes straight from the row-major V tile through ds_read_b64_tr_b16, in the
 // key order that matches the lane's P values. The chunk loop of a KV block
 // stops after ceil(valid/64) chunks; only a partial last chunk runs the mask.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "lds_tiles.hpp"
 
@@ -31,10 +33,17 @@ constexpr int TILE = KC * HD * 2;  // bytes of one 64-row tile
 template <class ET, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a) {
   using E = Elem<ET>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TILE];  // [stage][K | V]
+  // K and V tiles of the two stages as four distinct LDS objects: with the
+  // stage fixed at compile time the compiler can tell the tiles being filled
+  // from the ones being read, and does not wait for the prefetch before reading
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[TILE];
 
   const Geom& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets the compiler keep wave-level values scalar
   const int hl = lane >> 5, l32 = lane & 31;
 
   const int nsub = g.q_block / (32 * NW);
@@ -55,6 +64,7 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
   const long long qoff = g.q_base(b, h) + (long long)(blk0 + myrow) * qrs;
   const int hk = h / g.group;
   const long long kvb = g.kv_base(b, hk), krs = g.kv_rs();
+  const uint32_t krs_bytes = (uint32_t)(krs * 2);
 
   // this wave's query rows: B operand of S^T = K Q^T (lane: row l32, d = 16ks + 8hl + 0..7)
   uint4 qr[8];
@@ -66,124 +76,157 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
   const int e0 = a.row_ptr[rid], e1 = a.row_ptr[rid + 1];
 
   const float c2 = g.scale * LOG2E;
-  float m_run = -INFINITY, l_run = 0.f;
+  // exp offset of this lane's row in log2 units: it moves only when a chunk's
+  // max exceeds it by more than TAU, so P <= 2^TAU and rescaling is rare
+  float msc = -1e30f;
+  float l_a = 0.f, l_b = 0.f;  // two partial row sums (of the rounded P)
   f32x16_t acc[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
-  const TrLane tl(lane);
+  const RowOffs ro(lane);
+  const TrOffs to(lane);
 
   // global -> LDS for chunk c of KV block j (rows past the valid keys repeat
   // the last valid row: in bounds, and masked out of the softmax)
-  auto stage = [&](int buf, int j, int c, int nval) {
-    const int t0 = j * g.kv_block + c * KC;
+  auto stage = [&](uint8_t* Kd, uint8_t* Vd, int j, int c, int nval) {
+    const long long t0 = kvb + (long long)(j * g.kv_block + c * KC) * krs;
     const int last = nval - c * KC - 1;
-    uint8_t* Ks = smem + buf * 2 * TILE;
-    stage_tile<KC, NW>(Ks, wave, lane, [&](int row) {
-      return a.k + kvb + (long long)(t0 + min(row, last)) * krs;
-    });
-    stage_tile<KC, NW>(Ks + TILE, wave, lane, [&](int row) {
-      return a.v + kvb + (long long)(t0 + min(row, last)) * krs;
-    });
+    stage_rows<KC, NW>(Kd, wave, lane, a.k + t0, krs_bytes, last);
+    stage_rows<KC, NW>(Vd, wave, lane, a.v + t0, krs_bytes, last);
+  };
+  // valid keys of block j, from the raw tile count (INT_MAX without counts)
+  auto raw_val = [&](int j) { return g.kv_valid ? g.kv_valid[j] : 0x7fffffff; };
+  const int kvlen = g.kv_len(b);
+  auto val_of = [&](int j, int raw) { return max(0, min(raw, min(g.kv_block, kvlen - j * g.kv_block))); };
+
+  // walk state: entry e, chunk c of block j with nval valid keys; the block
+  // list is read two entries ahead (col[e+1], col[e+2] and the count of e+1
+  // are in registers), so moving to the next block never waits on a
+  // dependent global load
+  int e = e0, c = 0, j = 0, nval = 0, j1 = 0, r1 = 0, j2 = 0;
+
+  // one chunk: prefetch the next chunk into the other stage, compute this one
+  auto step = [&](auto stage_id) -> bool {
+    constexpr int BUF = decltype(stage_id)::value;
+    const uint8_t* Ks = BUF == 0 ? sK0 : sK1;
+    const uint8_t* Vs = BUF == 0 ? sV0 : sV1;
+    uint8_t* Kn = BUF == 0 ? sK1 : sK0;
+    uint8_t* Vn = BUF == 0 ? sV1 : sV0;
+
+    int ne = e, nc = c + 1, nj = j, nnval = nval, pj1 = j1, pr1 = r1, pj2 = j2;
+    if (nc * KC >= nval) {
+      ne = e + 1;
+      nc = 0;
+      nj = j1;
+      nnval = val_of(j1, r1);
+      pj1 = j2;
+      pr1 = e + 2 < e1 ? raw_val(j2) : 0;  // in flight until the end of this step
+      pj2 = e + 3 < e1 ? a.col[e + 3] : 0;
+    }
+    const bool has_next = ne < e1;
+    if (has_next) stage(Kn, Vn, nj, nc, nnval);
+
+    // ---- S^T = K Q^T (2 x 32 keys by 32 rows) ----
+    f32x16_t s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s0 = E::mfma(ro.at(Ks, 0, ks), qr[ks], s0);
+      s1 = E::mfma(ro.at(Ks, 32, ks), qr[ks], s1);
+    }
+    // lane holds keys 8(r/4) + 4hl + (r%4) (+32 for s1) of its row
+    const int rem = nval - c * KC;
+    if (rem < KC) {
+      const int lim = rem - 4 * hl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + (r & 3);
+        if (kk >= lim) s0[r] = -INFINITY;
+        if (kk + 32 >= lim) s1[r] = -INFINITY;
+      }
+    }
+    // chunk max of the row: a maximum3 tree, then the other lane half
+    float t[11];
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      t[u] = vmax3(s0[3 * u], s0[3 * u + 1], s0[3 * u + 2]);
+      t[5 + u] = vmax3(s1[3 * u], s1[3 * u + 1], s1[3 * u + 2]);
+    }
+    t[10] = vmax(s0[15], s1[15]);
+    float mx = vmax3(vmax3(t[0], t[1], t[2]), vmax3(t[3], t[4], t[5]), vmax3(t[6], t[7], t[8]));
+    mx = xhalf_max(vmax3(mx, t[9], t[10]));
+    constexpr float TAU = 8.f;
+    if (mx * c2 > msc + TAU) {  // move the offset to this chunk's max
+      const float nm = mx * c2;
+      const float alpha = __builtin_amdgcn_exp2f(msc - nm);
+      l_a *= alpha;
+      l_b *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+      msc = nm;
+    }
+
+    // ---- P^T, its row sums, and O^T += V^T P^T: 4 key steps of 16 ----
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x16_t& s = (kt < 2) ? s0 : s1;
+      const int o = 8 * (kt & 1);
+      float p[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[o + u], c2, -msc));
+      const uint4 pb = make_uint4(E::pack(p[0], p[1]), E::pack(p[2], p[3]), E::pack(p[4], p[5]),
+                                  E::pack(p[6], p[7]));
+      l_a = E::sum2(pb.x, l_a);
+      l_b = E::sum2(pb.y, l_b);
+      l_a = E::sum2(pb.z, l_a);
+      l_b = E::sum2(pb.w, l_b);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[mb] = E::mfma(to.at(Vs, 16 * kt, mb), pb, acc[mb]);
+    }
+
+    wait_vmem();
+    // the look-ahead values were loaded into vector registers during this
+    // step; keep them there until the wait above, then make them uniform
+    asm volatile("" : "+v"(pr1), "+v"(pj2));
+    pr1 = __builtin_amdgcn_readfirstlane(pr1);
+    pj2 = __builtin_amdgcn_readfirstlane(pj2);
+    __syncthreads();
+    if (!has_next) return false;
+    e = ne;
+    c = nc;
+    j = nj;
+    nval = nnval;
+    j1 = pj1;
+    r1 = pr1;
+    j2 = pj2;
+    return true;
   };
 
   if (e0 < e1) {
-    int e = e0, c = 0;
-    int j = a.col[e];
-    int nval = g.kv_val(b, j);
-    stage(0, j, 0, nval);
+    j = a.col[e0];
+    nval = val_of(j, raw_val(j));
+    j1 = e0 + 1 < e1 ? a.col[e0 + 1] : 0;
+    r1 = e0 + 1 < e1 ? raw_val(j1) : 0;
+    j2 = e0 + 2 < e1 ? a.col[e0 + 2] : 0;
+    stage(sK0, sV0, j, 0, nval);
     wait_vmem();
     __syncthreads();
-    int buf = 0;
-    while (true) {
-      // the chunk after this one
-      int ne = e, nc = c + 1, nj = j, nnval = nval;
-      if (nc * KC >= nval) {
-        ne = e + 1;
-        nc = 0;
-        if (ne < e1) {
-          nj = a.col[ne];
-          nnval = g.kv_val(b, nj);
-        }
-      }
-      const bool has_next = ne < e1;
-      if (has_next) stage(buf ^ 1, nj, nc, nnval);
-
-      // ---- this chunk: S^T = K Q^T (2 x 32 keys by 32 rows) ----
-      const uint8_t* Ks = smem + buf * 2 * TILE;
-      const uint8_t* Vs = Ks + TILE;
-      f32x16_t s0, s1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s0 = E::mfma(row16(Ks, l32, 2 * ks + hl), qr[ks], s0);
-        s1 = E::mfma(row16(Ks, 32 + l32, 2 * ks + hl), qr[ks], s1);
-      }
-      // lane holds keys 8(r/4) + 4hl + (r%4) (+32 for s1) of its row
-      const int rem = nval - c * KC;
-      if (rem < KC) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= rem) s0[r] = -INFINITY;
-          if (key + 32 >= rem) s1[r] = -INFINITY;
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      mx = xhalf_max(mx);
-      const float mnew = fmaxf(m_run, mx);
-      const float msc = mnew == -INFINITY ? 0.f : mnew * c2;
-      float lsum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, -msc));
-        s1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, -msc));
-        lsum += s0[r] + s1[r];
-      }
-      if (mnew > m_run) {  // rescale only when the running max moved
-        const float alpha = __builtin_amdgcn_exp2f(m_run * c2 - msc);
-        l_run *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
-      }
-      m_run = mnew;
-      l_run += lsum;
-
-      // ---- O^T += V^T P^T: 4 key steps of 16 ----
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const f32x16_t& s = (kt < 2) ? s0 : s1;
-        const int o = 8 * (kt & 1);
-        const uint4 pb = make_uint4(E::pack(s[o + 0], s[o + 1]), E::pack(s[o + 2], s[o + 3]),
-                                    E::pack(s[o + 4], s[o + 5]), E::pack(s[o + 6], s[o + 7]));
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb] = E::mfma(tr_operand(Vs, tl, 16 * kt, mb), pb, acc[mb]);
-      }
-
-      wait_vmem();
-      __syncthreads();
-      if (!has_next) break;
-      e = ne;
-      c = nc;
-      j = nj;
-      nval = nnval;
-      buf ^= 1;
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
     }
   }
 
   // ---- epilogue ----
-  l_run = xhalf_sum(l_run);
+  const float l_run = xhalf_sum(l_a + l_b);
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   if (!row_ok) return;
-  if (hl == 0)
+  if (hl == 0)  // natural-log LSE: (offset + log2 l) * ln 2
     a.lse[g.lse_base(b, h) + blk0 + myrow] =
-        l_run > 0.f ? m_run * g.scale + __logf(l_run) : -INFINITY;
+        l_run > 0.f ? (msc + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f : -INFINITY;
   float gt = 0.f;
   if (a.gate_mode == VSA_GATE_PER_TOKEN)
     gt = E::lo(a.gate[g.gtok_base(b, h) + (long long)(blk0 + myrow) * g.gtok_rs()]);

@@ -36,6 +36,11 @@ struct Elem<bf16_tag> {
     f32x2_t v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
   }
+  // acc + lo + hi of a packed pair, in fp32 (v_dot2c_f32_bf16 against (1, 1))
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p),
+                                           __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+  }
   static __device__ __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
   static __device__ __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 };
@@ -49,6 +54,10 @@ struct Elem<f16_tag> {
   static __device__ __forceinline__ uint32_t pack(float x, float y) {
     f32x2_t v = {x, y};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p),
+                                  __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc, false);
   }
   static __device__ __forceinline__ float lo(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
@@ -138,9 +147,14 @@ __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast
 __device__ __forceinline__ void stg16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // max / sum of a value and its copy in lane l ^ 32
+// Maximum without the NaN quieting of fmaxf (which costs one extra
+// instruction per operand): NaN propagates, v_maximum3_f32 takes three inputs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 __device__ __forceinline__ float xhalf_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -38,6 +38,23 @@ __device__ __forceinline__ void stage_tile(uint8_t* tile, int wave, int lane, F 
   }
 }
 
+// Stage RT rows of a tile whose row r lives at base + min(r, last) * rs_bytes:
+// the base is uniform and each lane adds a 32-bit offset (row < 256, so
+// min(r, last) * rs_bytes stays far below 2^32 for any head count the C ABI
+// accepts), which keeps the address arithmetic to two 24-bit integer ops.
+template <int RT, int NW>
+__device__ __forceinline__ void stage_rows(uint8_t* tile, int wave, int lane, const uint16_t* base,
+                                           uint32_t rs_bytes, int last) {
+  const uint8_t* b8 = reinterpret_cast<const uint8_t*>(base);
+#pragma unroll
+  for (int p = wave; p < RT / 4; p += NW) {
+    const int row = 4 * p + (lane >> 4);
+    const uint32_t c = (uint32_t)((lane & 15) ^ swz(row));
+    const uint32_t off = (uint32_t)__umul24((uint32_t)min(row, last), rs_bytes) + 16u * c;
+    __builtin_amdgcn_global_load_lds((const void*)(b8 + off), (void*)(tile + p * 1024), 16, 0, 0);
+  }
+}
+
 // Stage N <= 64 consecutive fp32 values with one wave instruction: lane i
 // (i < N) writes word i of dst; entries past `last` repeat entry `last`.
 template <int N>
