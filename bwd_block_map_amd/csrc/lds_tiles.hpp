@@ -38,6 +38,30 @@ __device__ __forceinline__ void stage_tile(uint8_t* tile, int wave, int lane, F 
   }
 }
 
+// LDS address (byte offset) of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane i fills lds + 16 i from
+// base + voff. Issued from inline asm so that the compiler does not track it:
+// its own tracking of these loads merges LDS buffers at loop heads and then
+// waits for every prefetch before any LDS read. Callers wait with wait_vm and
+// synchronise with lds_barrier. M0 carries the LDS base; no other instruction
+// in these kernels reads M0, so setting it here clobbers nothing.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "m0", "memory");
+}
+// the same with 4 bytes per lane (lane i fills lds + 4 i)
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+               : "m0", "memory");
+}
+#pragma clang diagnostic pop
+
 // Stage RT rows of a tile whose row r lives at base + min(r, last) * rs_bytes:
 // the base is uniform and each lane adds a 32-bit offset (row < 256, so
 // min(r, last) * rs_bytes stays far below 2^32 for any head count the C ABI
@@ -45,14 +69,33 @@ __device__ __forceinline__ void stage_tile(uint8_t* tile, int wave, int lane, F 
 template <int RT, int NW>
 __device__ __forceinline__ void stage_rows(uint8_t* tile, int wave, int lane, const uint16_t* base,
                                            uint32_t rs_bytes, int last) {
-  const uint8_t* b8 = reinterpret_cast<const uint8_t*>(base);
+  constexpr int P = RT / 4;  // wave instructions of the tile
+  const uint32_t t0 = lds_addr(tile);
 #pragma unroll
-  for (int p = wave; p < RT / 4; p += NW) {
-    const int row = 4 * p + (lane >> 4);
-    const uint32_t c = (uint32_t)((lane & 15) ^ swz(row));
-    const uint32_t off = (uint32_t)__umul24((uint32_t)min(row, last), rs_bytes) + 16u * c;
-    __builtin_amdgcn_global_load_lds((const void*)(b8 + off), (void*)(tile + p * 1024), 16, 0, 0);
+  for (int k = 0; k < (P + NW - 1) / NW; ++k) {
+    const int p = wave + k * NW;
+    if (P % NW == 0 || p < P) {
+      const int row = 4 * p + (lane >> 4);
+      const uint32_t c = (uint32_t)((lane & 15) ^ swz(row));
+      const uint32_t off = (uint32_t)__umul24((uint32_t)min(row, last), rs_bytes) + 16u * c;
+      dma16(base, off, t0 + p * 1024);
+    }
   }
+}
+
+// Direct loads one wave issues for an RT-row tile (when every wave issues the same number).
+template <int RT, int NW>
+constexpr int rows_loads() {
+  static_assert((RT / 4) % NW == 0, "waves issue equal shares");
+  return RT / 4 / NW;
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (loads complete in order; the other counters are left alone).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // Stage N <= 64 consecutive fp32 values with one wave instruction: lane i
@@ -62,6 +105,20 @@ __device__ __forceinline__ void stage_f32(float* dst, const float* src, int lane
   static_assert(N <= 64, "one wave instruction");
   if (lane < N)
     __builtin_amdgcn_global_load_lds((const void*)(src + min(lane, last)), (void*)dst, 4, 0, 0);
+}
+
+// Work-group barrier for LDS tiles filled by direct loads. __syncthreads()
+// carries a release fence that on this target drains every outstanding global
+// load, which would also wait for the chunks prefetched further ahead. Here
+// each wave first retires its own LDS reads and writes (the direct loads it
+// must have landed are waited for by the caller with wait_vm), the empty asm
+// statements keep the compiler from moving memory operations across, and the
+// hardware barrier does the rest.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // all outstanding vector-memory operations (including direct LDS fills) done
