@@ -22,7 +22,7 @@
 //  * dQ: like the forward (Q-owned list, 64-key chunks, S^T and dP^T with
 //    lane = query row); dQ^T += K^T dS^T with K^T staged in LDS.
 #include "kernels.hpp"
-#include "lds_tiles.hpp"
+#include "kv_walk.hpp"
 
 namespace vsa {
 
@@ -427,16 +427,14 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
 // ---------------------------------------------------------------------------
 // dQ (Q-owned)
 // ---------------------------------------------------------------------------
-constexpr int KC = 64;             // keys per chunk
-constexpr int KTILE = KC * HD * 2;
+constexpr int KC = KV_CHUNK;
 
-template <class ET, int NW>
+template <class ET, int NW, int NST>
 __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) {
   using E = Elem<ET>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * KTILE];  // [stage][K | V]
-
   const Geom& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level values stay scalar
   const int hl = lane >> 5, l32 = lane & 31;
   const int nsub = g.q_block / (32 * NW);
   int id = xcd_group(blockIdx.x, gridDim.x, nsub);
@@ -452,9 +450,8 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
   const bool row_ok = myrow < qexist;
   const long long qrs = g.q_rs();
   const long long qoff = g.q_base(b, h) + (long long)(blk0 + myrow) * qrs;
-  const int hk = h / g.group;
-  const long long kvb = g.kv_base(b, hk), krs = g.kv_rs();
 
+  // this wave's Q and dO rows: B operands (lane: row l32, d = 16ks + 8hl + 0..7)
   uint4 qr[8], dor[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -465,7 +462,8 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
   const float lse2 = row_ok ? a.lse2[lrow] : INFINITY;
   const float drv = row_ok ? a.dr[lrow] : 0.f;
   const float c2 = g.scale * LOG2E;
-  const TrLane tl(lane);
+  const RowOffs ro(lane);
+  const TrOffs to(lane);
 
   f32x16_t acc[4];
 #pragma unroll
@@ -474,86 +472,44 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
 
   const long long rid = ((long long)b * g.Hq + h) * g.Qb + i;
-  const int e0 = a.row_ptr[rid], e1 = a.row_ptr[rid + 1];
+  const int e0 = a.row_ptr[rid];
+  const int cnt = a.row_ptr[rid + 1] - e0;
 
-  auto stage = [&](int buf, int j, int c, int nval) {
-    const int t0 = j * g.kv_block + c * KC;
-    const int last = nval - c * KC - 1;
-    uint8_t* Ks = smem + buf * 2 * KTILE;
-    stage_tile<KC, NW>(Ks, wave, lane, [&](int row) {
-      return a.k + kvb + (long long)(t0 + min(row, last)) * krs;
-    });
-    stage_tile<KC, NW>(Ks + KTILE, wave, lane, [&](int row) {
-      return a.v + kvb + (long long)(t0 + min(row, last)) * krs;
-    });
-  };
-
-  if (e0 < e1) {
-    int e = e0, c = 0;
-    int j = a.col[e];
-    int nval = g.kv_val(b, j);
-    stage(0, j, 0, nval);
-    wait_vmem();
-    __syncthreads();
-    int buf = 0;
-    while (true) {
-      int ne = e, nc = c + 1, nj = j, nnval = nval;
-      if (nc * KC >= nval) {
-        ne = e + 1;
-        nc = 0;
-        if (ne < e1) {
-          nj = a.col[ne];
-          nnval = g.kv_val(b, nj);
-        }
-      }
-      const bool has_next = ne < e1;
-      if (has_next) stage(buf ^ 1, nj, nc, nnval);
-
-      const uint8_t* Ks = smem + buf * 2 * KTILE;
-      const uint8_t* Vs = Ks + KTILE;
-      f32x16_t s0, s1, p0, p1;
+  walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, cnt, a.k, a.v, wave, lane,
+                   [&](const uint8_t* Ks, const uint8_t* Vs, int rem) {
+    // per half of 32 keys: S^T = K Q^T, dP^T = V dO^T, dS = P * (dP - D), then
+    // dQ^T += K^T dS^T over its two key steps of 16
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s0[r] = s1[r] = p0[r] = p1[r] = 0.f;
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16_t sv, pv;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = pv[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        s0 = E::mfma(row16(Ks, l32, 2 * ks + hl), qr[ks], s0);
-        s1 = E::mfma(row16(Ks, 32 + l32, 2 * ks + hl), qr[ks], s1);
-        p0 = E::mfma(row16(Vs, l32, 2 * ks + hl), dor[ks], p0);
-        p1 = E::mfma(row16(Vs, 32 + l32, 2 * ks + hl), dor[ks], p1);
+        sv = E::mfma(ro.at(Ks, 32 * hf, ks), qr[ks], sv);
+        pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
       }
-      const int rem = nval - c * KC;
+      // lane holds keys 32hf + 8(r/4) + 4hl + (r%4) of its row; keys past the
+      // valid ones get P = 0 through a -inf exponent
+      if (rem < KC) {
+        const int lim = rem - 32 * hf - 4 * hl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float a0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, -lse2));
-        float a1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, -lse2));
-        if (rem < KC) {
-          const int key = 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= rem) a0 = 0.f;
-          if (key + 32 >= rem) a1 = 0.f;
-        }
-        s0[r] = a0 * (p0[r] - drv);
-        s1[r] = a1 * (p1[r] - drv);
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) >= lim) sv[r] = -INFINITY;
       }
-      // dQ^T += K^T dS^T (key steps of 16)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const f32x16_t& s = (kt < 2) ? s0 : s1;
-        const int o = 8 * (kt & 1);
-        const uint4 pb = make_uint4(E::pack(s[o], s[o + 1]), E::pack(s[o + 2], s[o + 3]),
-                                    E::pack(s[o + 4], s[o + 5]), E::pack(s[o + 6], s[o + 7]));
+      for (int r = 0; r < 16; ++r)
+        sv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c2, -lse2)) * (pv[r] - drv);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb] = E::mfma(tr_operand(Ks, tl, 16 * kt, mb), pb, acc[mb]);
+      for (int kt = 0; kt < 2; ++kt) {
+        const int o = 8 * kt;
+        const uint4 pb = make_uint4(E::pack(sv[o], sv[o + 1]), E::pack(sv[o + 2], sv[o + 3]),
+                                    E::pack(sv[o + 4], sv[o + 5]), E::pack(sv[o + 6], sv[o + 7]));
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = E::mfma(to.at(Ks, 32 * hf + 16 * kt, mb), pb, acc[mb]);
       }
-      wait_vmem();
-      __syncthreads();
-      if (!has_next) break;
-      e = ne;
-      c = nc;
-      j = nj;
-      nval = nnval;
-      buf ^= 1;
     }
-  }
+  });
 
   if (!row_ok) return;
   const float* dqc = nullptr;
@@ -610,10 +566,10 @@ hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int nw = g.q_block % 256 == 0 ? 8 : g.q_block % 128 == 0 ? 4 : g.q_block % 64 == 0 ? 2 : 1;
   const long long nwg = (long long)g.B * g.Hq * g.Qb * (g.q_block / (32 * nw));
   if (nwg == 0) return hipSuccess;
-  if (nw == 8) sparse_dq_kernel<ET, 8><<<(unsigned)nwg, 512, 0, st>>>(a);
-  else if (nw == 4) sparse_dq_kernel<ET, 4><<<(unsigned)nwg, 256, 0, st>>>(a);
-  else if (nw == 2) sparse_dq_kernel<ET, 2><<<(unsigned)nwg, 128, 0, st>>>(a);
-  else sparse_dq_kernel<ET, 1><<<(unsigned)nwg, 64, 0, st>>>(a);
+  if (nw == 8) sparse_dq_kernel<ET, 8, 4><<<(unsigned)nwg, 512, 0, st>>>(a);
+  else if (nw == 4) sparse_dq_kernel<ET, 4, 2><<<(unsigned)nwg, 256, 0, st>>>(a);
+  else if (nw == 2) sparse_dq_kernel<ET, 2, 2><<<(unsigned)nwg, 128, 0, st>>>(a);
+  else sparse_dq_kernel<ET, 1, 2><<<(unsigned)nwg, 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

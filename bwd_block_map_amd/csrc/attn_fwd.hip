@@ -18,40 +18,18 @@
 // comes straight from the row-major V tile through ds_read_b64_tr_b16, in the
 // key order that matches the lane's P values. The chunk loop of a KV block
 // stops after ceil(valid/64) chunks; only a partial last chunk runs the mask.
-#include <type_traits>
-
 #include "kernels.hpp"
-#include "lds_tiles.hpp"
+#include "kv_walk.hpp"
 
 namespace vsa {
 
 namespace {
 
-constexpr int KC = 64;             // keys per chunk
-constexpr int TILE = KC * HD * 2;  // bytes of one 64-row tile
-constexpr int LIST_CAP = 1024;     // block-list entries held in LDS at a time
-
-template <int I>
-using Slot = std::integral_constant<int, I>;
+constexpr int KC = KV_CHUNK;
 
 template <class ET, int NW, int NST>
 __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a) {
   using E = Elem<ET>;
-  static_assert(NST == 2 || NST == 4, "stage ring of 2 or 4");
-  // K and V tiles of the NST stages as distinct LDS objects: with the stage
-  // fixed at compile time the compiler can tell the tiles being filled from
-  // the ones being read, and does not wait for the prefetch before reading
-  __shared__ __attribute__((aligned(1024))) uint8_t sK0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sK1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sK2[NST > 2 ? TILE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV2[NST > 2 ? TILE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sK3[NST > 2 ? TILE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sV3[NST > 2 ? TILE : 16];
-  __shared__ int lst_j[LIST_CAP];  // a page of this row's block list: block and valid keys
-  __shared__ int lst_v[LIST_CAP];
-
   const Geom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level values stay scalar
@@ -73,9 +51,6 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
   const bool row_ok = myrow < qexist;
   const long long qrs = g.q_rs();
   const long long qoff = g.q_base(b, h) + (long long)(blk0 + myrow) * qrs;
-  const int hk = h / g.group;
-  const long long kvb = g.kv_base(b, hk), krs = g.kv_rs();
-  const uint32_t krs_bytes = (uint32_t)(krs * 2);
 
   // this wave's query rows: B operand of S^T = K Q^T (lane: row l32, d = 16ks + 8hl + 0..7)
   uint4 qr[8];
@@ -100,177 +75,69 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
   const RowOffs ro(lane);
   const TrOffs to(lane);
 
-  // ---- the block list, a page of LIST_CAP entries at a time, in LDS ----
-  const int kvlen = g.kv_len(b);
-  auto load_page = [&](int base) {
-    for (int t = tid; t < LIST_CAP && base + t < cnt; t += NW * 64) {
-      const int j = a.col[e0 + base + t];
-      const int ex = max(0, min(g.kv_block, kvlen - j * g.kv_block));
-      lst_j[t] = j;
-      lst_v[t] = g.kv_valid ? min(g.kv_valid[j], ex) : ex;
+  walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, cnt, a.k, a.v, wave, lane,
+                   [&](const uint8_t* Ks, const uint8_t* Vs, int rem) {
+    // ---- S^T = K Q^T (2 x 32 keys by 32 rows) ----
+    f32x16_t s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s0 = E::mfma(ro.at(Ks, 0, ks), qr[ks], s0);
+      s1 = E::mfma(ro.at(Ks, 32, ks), qr[ks], s1);
     }
-  };
-  if (cnt == 0) goto epilogue;
-  load_page(0);
-  wait_vm<0>();  // the query rows and the list page have landed
-  __syncthreads();
-
-  {
-    // stager: the next chunk to load (entry se of the list, chunk sc of block sj)
-    int se = 0, sc = 0, page = 0;
-    int sj = lst_j[0], snv = lst_v[0];
-    bool more = true;
-    auto advance = [&]() {
-      if (++sc * KC < snv) return;
-      sc = 0;
-      if (++se >= cnt) {
-        more = false;
-        return;
-      }
-      if (se - page >= LIST_CAP) {  // next page (only for lists longer than LIST_CAP)
-        __syncthreads();
-        page = se;
-        load_page(page);
-        __syncthreads();
-      }
-      sj = lst_j[se - page];
-      snv = lst_v[se - page];
-    };
-    // per slot: whether it holds a chunk, and that chunk's number of valid keys
-    bool have[NST];
-    int rem[NST];
-    auto tileK = [&](auto sid) -> uint8_t* {
-      constexpr int S = decltype(sid)::value;
-      if constexpr (S == 0) return sK0;
-      else if constexpr (S == 1) return sK1;
-      else if constexpr (S == 2) return sK2;
-      else return sK3;
-    };
-    auto tileV = [&](auto sid) -> uint8_t* {
-      constexpr int S = decltype(sid)::value;
-      if constexpr (S == 0) return sV0;
-      else if constexpr (S == 1) return sV1;
-      else if constexpr (S == 2) return sV2;
-      else return sV3;
-    };
-    // load the stager's chunk into slot sid (rows past the valid keys repeat
-    // the last valid row: in bounds, and masked out of the softmax)
-    auto fill = [&](auto sid) {
-      constexpr int S = decltype(sid)::value;
-      have[S] = more;
-      if (!more) return;
-      const long long t0 = kvb + (long long)(sj * g.kv_block + sc * KC) * krs;
-      const int left = snv - sc * KC;
-      rem[S] = left;
-      stage_rows<KC, NW>(tileK(sid), wave, lane, a.k + t0, krs_bytes, left - 1);
-      stage_rows<KC, NW>(tileV(sid), wave, lane, a.v + t0, krs_bytes, left - 1);
-      advance();
-    };
-    constexpr int LPC = 2 * rows_loads<KC, NW>();  // direct loads per chunk and wave
-
-    // one chunk: refill the slot freed last step, compute slot sid, wait for the next
-    auto step = [&](auto sid) -> bool {
-      constexpr int S = decltype(sid)::value;
-      fill(Slot<(S + NST - 1) % NST>{});
-      const uint8_t* Ks = tileK(sid);
-      const uint8_t* Vs = tileV(sid);
-
-      // ---- S^T = K Q^T (2 x 32 keys by 32 rows) ----
-      f32x16_t s0, s1;
+    // lane holds keys 8(r/4) + 4hl + (r%4) (+32 for s1) of its row
+    if (rem < KC) {
+      const int lim = rem - 4 * hl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s0 = E::mfma(ro.at(Ks, 0, ks), qr[ks], s0);
-        s1 = E::mfma(ro.at(Ks, 32, ks), qr[ks], s1);
-      }
-      // lane holds keys 8(r/4) + 4hl + (r%4) (+32 for s1) of its row
-      if (rem[S] < KC) {
-        const int lim = rem[S] - 4 * hl;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 8 * (r >> 2) + (r & 3);
-          if (kk >= lim) s0[r] = -INFINITY;
-          if (kk + 32 >= lim) s1[r] = -INFINITY;
-        }
-      }
-      // chunk max of the row: a maximum3 tree, then the other lane half
-      float t[11];
-#pragma unroll
-      for (int u = 0; u < 5; ++u) {
-        t[u] = vmax3(s0[3 * u], s0[3 * u + 1], s0[3 * u + 2]);
-        t[5 + u] = vmax3(s1[3 * u], s1[3 * u + 1], s1[3 * u + 2]);
-      }
-      t[10] = vmax(s0[15], s1[15]);
-      float mx = vmax3(vmax3(t[0], t[1], t[2]), vmax3(t[3], t[4], t[5]), vmax3(t[6], t[7], t[8]));
-      mx = xhalf_max(vmax3(mx, t[9], t[10]));
-      constexpr float TAU = 8.f;
-      if (mx * c2 > msc + TAU) {  // move the offset to this chunk's max
-        const float nm = mx * c2;
-        const float alpha = __builtin_amdgcn_exp2f(msc - nm);
-        l_a *= alpha;
-        l_b *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
-        msc = nm;
-      }
-
-      // ---- P^T, its row sums, and O^T += V^T P^T: 4 key steps of 16 ----
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        f32x16_t& sv = (kt < 2) ? s0 : s1;
-        const int o = 8 * (kt & 1);
-        float pv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pv[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[o + u], c2, -msc));
-        const uint4 pb = make_uint4(E::pack(pv[0], pv[1]), E::pack(pv[2], pv[3]), E::pack(pv[4], pv[5]),
-                                    E::pack(pv[6], pv[7]));
-        l_a = E::sum2(pb.x, l_a);
-        l_b = E::sum2(pb.y, l_b);
-        l_a = E::sum2(pb.z, l_a);
-        l_b = E::sum2(pb.w, l_b);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb] = E::mfma(to.at(Vs, 16 * kt, mb), pb, acc[mb]);
-      }
-
-      // the next slot's chunk must have landed; later chunks may stay in flight
-      if constexpr (NST == 4) {
-        const int later = (int)have[(S + 2) % NST] + (int)have[(S + 3) % NST];
-        if (later == 2) wait_vm<2 * LPC>();
-        else if (later == 1) wait_vm<LPC>();
-        else wait_vm<0>();
-      } else {
-        wait_vm<0>();
-      }
-      lds_barrier();
-      return have[(S + 1) % NST];
-    };
-
-    // prologue: the first NST - 1 chunks in flight
-    fill(Slot<0>{});
-    if constexpr (NST == 4) {
-      fill(Slot<1>{});
-      fill(Slot<2>{});
-      const int later = (int)have[1] + (int)have[2];
-      if (later == 2) wait_vm<2 * LPC>();
-      else if (later == 1) wait_vm<LPC>();
-      else wait_vm<0>();
-    } else {
-      wait_vm<0>();
-    }
-    lds_barrier();
-    if constexpr (NST == 4) {
-      while (step(Slot<0>{}) && step(Slot<1>{}) && step(Slot<2>{}) && step(Slot<3>{})) {
-      }
-    } else {
-      while (step(Slot<0>{}) && step(Slot<1>{})) {
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + (r & 3);
+        if (kk >= lim) s0[r] = -INFINITY;
+        if (kk + 32 >= lim) s1[r] = -INFINITY;
       }
     }
-  }
+    // chunk max of the row: a maximum3 tree, then the other lane half
+    float t[11];
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      t[u] = vmax3(s0[3 * u], s0[3 * u + 1], s0[3 * u + 2]);
+      t[5 + u] = vmax3(s1[3 * u], s1[3 * u + 1], s1[3 * u + 2]);
+    }
+    t[10] = vmax(s0[15], s1[15]);
+    float mx = vmax3(vmax3(t[0], t[1], t[2]), vmax3(t[3], t[4], t[5]), vmax3(t[6], t[7], t[8]));
+    mx = xhalf_max(vmax3(mx, t[9], t[10]));
+    constexpr float TAU = 8.f;
+    if (mx * c2 > msc + TAU) {  // move the offset to this chunk's max
+      const float nm = mx * c2;
+      const float alpha = __builtin_amdgcn_exp2f(msc - nm);
+      l_a *= alpha;
+      l_b *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+      msc = nm;
+    }
 
-epilogue:
+    // ---- P^T, its row sums, and O^T += V^T P^T: 4 key steps of 16 ----
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x16_t& sv = (kt < 2) ? s0 : s1;
+      const int o = 8 * (kt & 1);
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[o + u], c2, -msc));
+      const uint4 pb = make_uint4(E::pack(pv[0], pv[1]), E::pack(pv[2], pv[3]), E::pack(pv[4], pv[5]),
+                                  E::pack(pv[6], pv[7]));
+      l_a = E::sum2(pb.x, l_a);
+      l_b = E::sum2(pb.y, l_b);
+      l_a = E::sum2(pb.z, l_a);
+      l_b = E::sum2(pb.w, l_b);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[mb] = E::mfma(to.at(Vs, 16 * kt, mb), pb, acc[mb]);
+    }
+  });
+
   const float l_run = xhalf_sum(l_a + l_b);
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   if (!row_ok) return;
