@@ -133,20 +133,29 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
 // Each row group takes 32 rows of a chunk; the row groups' sums are added
 // through LDS at the end. One launch per shape; a work-group whose span has
 // another shape returns at once.
+//
+// Q / dO chunks (with the chunk rows' lse2 and D terms) go global -> LDS with
+// counted direct loads into a ring of NST slots, so NST - 1 chunks are in
+// flight while one is computed; the KV-owned list of the current head sits in
+// LDS a page at a time.
 constexpr int DKDV_NW = 8;
 constexpr int DKDV_SPAN = 256;
+constexpr int DKDV_LIST_CAP = 1024;
 
 template <int KS>
 struct DkdvShape {
   static constexpr int NW = DKDV_NW;
-  static constexpr int RG = NW / KS;                  // row groups
-  static constexpr int KW = 32 * KS;                  // keys of the work-group
-  static constexpr int QC = 32 * RG;                  // query rows per chunk
-  static constexpr int QT = QC * HD * 2;              // bytes of a QC-row tile
-  static constexpr int STAGE = 2 * QT + 2 * QC * 4;   // Q | dO | lse2 | dr
-  static constexpr int LDS = 2 * STAGE + KW * HD * 2;  // two stages, then the K tile
-  static_assert(NW % KS == 0, "whole row groups");
-  static_assert((RG - 1) * KS * 64 * 64 * 4 <= LDS, "row-group reduction fits in LDS");
+  static constexpr int RG = NW / KS;                 // row groups
+  static constexpr int KW = 32 * KS;                 // keys of the work-group
+  static constexpr int QC = 32 * RG;                 // query rows per chunk
+  static constexpr int QT = QC * HD * 2;             // bytes of a QC-row tile
+  static constexpr int STAGE = 2 * QT + 2 * QC * 4;  // Q | dO | lse2 | dr
+  static constexpr int NST = KS == 8 ? 4 : KS == 4 ? 3 : 2;  // ring slots (LDS budget)
+  // direct loads per chunk and wave: Q and dO rows, then its own rows' lse2 and dr
+  static constexpr int LPC = 2 * (QC / 4 / NW) + 2;
+  static_assert(NW % KS == 0 && (QC / 4) % NW == 0, "whole row groups, equal load shares");
+  static_assert((RG - 1) * KS * 64 * 64 * 4 <= NST * STAGE, "row-group reduction fits in the ring");
+  static_assert(STAGE % 256 == 0, "slots keep the 256-byte row alignment");
 };
 
 __device__ __forceinline__ int dkdv_shape(int live) { return live > 128 ? 8 : live > 64 ? 4 : 2; }
@@ -156,10 +165,14 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
   using E = Elem<ET>;
   using S = DkdvShape<KS>;
   constexpr int NW = S::NW, RG = S::RG, QC = S::QC, QT = S::QT, STAGE = S::STAGE, KW = S::KW;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS];
+  constexpr int NST = S::NST, LPC = S::LPC;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NST][STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t Kt[KW * HD * 2];
+  __shared__ int lst_i[DKDV_LIST_CAP];
 
   const Geom& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level values stay scalar
   const int hl = lane >> 5;
   const int kslot = wave % KS, rg = wave / KS;
   const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
@@ -191,11 +204,8 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
     // the work-group's K rows stay in LDS for the whole walk (rows past the
     // live keys repeat the last live one and are masked); V^T columns are
     // register B operands (lane: key, d = 16ks + 8hl + 0..7)
-    uint8_t* Kt = smem + 2 * STAGE;
-    const int lastk = min(live, KW) - 1;
-    stage_tile<KW, NW>(Kt, wave, lane, [&](int row) {
-      return a.k + kbase + (long long)(k0 + min(row, lastk)) * krs;
-    });
+    stage_rows<KW, NW>(Kt, wave, lane, a.k + kbase + (long long)k0 * krs, (uint32_t)(krs * 2),
+                       min(live, KW) - 1);
     uint4 vr[8];
     const long long koff = kbase + (long long)mykey * krs;
 #pragma unroll
@@ -205,43 +215,88 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
     const bool wave_keys = 32 * kslot < live;        // this wave has a live key
     const float c2 = g.scale * LOG2E;
     const long long qrs = g.q_rs();
+    const uint32_t qrs_bytes = (uint32_t)(qrs * 2);
     const RowOffs ro(lane);
     const TrOffs to(lane);
     const int rb = 32 * rg;  // this wave's rows inside a chunk
+    const int qlen = g.q_len(b);
 
-    // one chunk = (head h, Q block i, rows QC*c ..); rows past the block repeat
-    // its last row (in bounds) and are masked in the compute
-    auto stage = [&](int buf, int h, int i, int c) {
-      const int last = g.q_exist(b, i) - c * QC - 1;
-      const long long base = g.q_base(b, h) + (long long)(i * g.q_block + c * QC) * qrs;
-      uint8_t* st = smem + buf * STAGE;
-      stage_tile<QC, NW>(st, wave, lane, [&](int row) { return a.q + base + min(row, last) * qrs; });
-      stage_tile<QC, NW>(st + QT, wave, lane,
-                         [&](int row) { return a.dout + base + min(row, last) * qrs; });
-      const long long lb = g.lse_base(b, h) + i * g.q_block + c * QC;
-      float* fl = reinterpret_cast<float*>(st + 2 * QT);
-      constexpr int NP = (QC + 63) / 64;  // 64-entry pieces of lse2 and of dr
-#pragma unroll
-      for (int pc = 0; pc < NP; ++pc) {
-        if (wave == pc) stage_f32<(QC < 64 ? QC : 64)>(fl + 64 * pc, a.lse2 + lb + 64 * pc, lane, last - 64 * pc);
-        if (wave == NW - 1 - pc)
-          stage_f32<(QC < 64 ? QC : 64)>(fl + QC + 64 * pc, a.dr + lb + 64 * pc, lane, last - 64 * pc);
+    // ---- the list walker: heads of the group, their KV-owned entries, row chunks ----
+    int hh = 0, e0 = 0, cnt = 0, page = 0;  // current head's CSR row and list page
+    auto load_head = [&](int hx) {  // first list page of head hx (all waves; drains loads)
+      const long long r = ((long long)b * g.Hq + hk * g.group + hx) * g.KVb + j;
+      e0 = a.row_ptr[r];
+      cnt = a.row_ptr[r + 1] - e0;
+      page = 0;
+      __syncthreads();
+      for (int t = tid; t < DKDV_LIST_CAP && t < cnt; t += NW * 64) lst_i[t] = a.col[e0 + t];
+      __syncthreads();
+    };
+    int se = 0, sc = 0, si = 0, sqe = 0;  // stager: entry, chunk, Q block, its rows
+    bool more = true;
+    auto settle = [&]() {  // from entry se of head hh, find the next entry (skipping empty heads)
+      while (se >= cnt) {
+        if (++hh >= g.group) {
+          more = false;
+          return;
+        }
+        load_head(hh);
+        se = 0;
+      }
+      if (se - page >= DKDV_LIST_CAP) {  // next page (only for lists longer than the cap)
+        __syncthreads();
+        page = se;
+        for (int t = tid; t < DKDV_LIST_CAP && page + t < cnt; t += NW * 64) lst_i[t] = a.col[e0 + page + t];
+        __syncthreads();
+      }
+      si = lst_i[se - page];
+      sqe = max(0, min(g.q_block, qlen - si * g.q_block));  // >= 1 for a listed Q block
+    };
+    load_head(0);
+    settle();
+
+    // per slot, 8 bits of `slots`: valid rows of its chunk (1 .. QC), 0 if empty
+    uint32_t slots = 0;
+    auto fill = [&](int s) {
+      slots &= ~(0xFFu << (8 * s));
+      if (!more) return;
+      const int h = hk * g.group + hh;
+      const int left = sqe - sc * QC;  // rows of the block from this chunk on
+      const int last = left - 1;
+      slots |= (uint32_t)min(left, QC) << (8 * s);
+      const long long base = g.q_base(b, h) + (long long)(si * g.q_block + sc * QC) * qrs;
+      const long long lb = g.lse_base(b, h) + si * g.q_block + sc * QC + rb;
+      uint8_t* st = ring[s];
+      stage_rows<QC, NW>(st, wave, lane, a.q + base, qrs_bytes, last);
+      stage_rows<QC, NW>(st + QT, wave, lane, a.dout + base, qrs_bytes, last);
+      // this wave's 32 rows of lse2 and dr (waves of one row group load the same values)
+      const uint32_t loff = 4u * (uint32_t)min(lane, max(0, last - rb));
+      const uint32_t lds_l = lds_addr(st + 2 * QT) + 4 * rb;
+      if (lane < 32) {
+        dma4(a.lse2 + lb, loff, lds_l);
+        dma4(a.dr + lb, loff, lds_l + 4 * QC);
+      }
+      if (++sc * QC >= sqe) {
+        sc = 0;
+        ++se;
+        settle();
       }
     };
+    auto rem_of = [&](int s) { return (int)((slots >> (8 * s)) & 0xFFu); };
 
-    auto compute = [&](int buf, int rows_valid) {
-      if (!wave_keys || rows_valid <= rb) return;  // nothing live for this wave
-      const uint8_t* Qs = smem + buf * STAGE;
+    // one chunk: S = Q K^T and dP = dO V^T, then P and dS, then
+    // dV^T += dO^T P and dK^T += Q^T dS
+    auto compute = [&](const uint8_t* Qs, int rows_valid) {
       const uint8_t* Ds = Qs + QT;
       const float* lse2 = reinterpret_cast<const float*>(Qs + 2 * QT);
       const float* drs = lse2 + QC;
-      // S = Q K^T and dP = dO V^T (rows rb + 8(r/4) + 4hl + r%4, key column)
-      f32x16_t s, dp;
+      // rows rb + 8(r/4) + 4hl + r%4, key column
+      f32x16_t sv, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        s = E::mfma(ro.at(Qs, rb, ks), ro.at(Kt, 32 * kslot, ks), s);
+        sv = E::mfma(ro.at(Qs, rb, ks), ro.at(Kt, 32 * kslot, ks), sv);
         dp = E::mfma(ro.at(Ds, rb, ks), vr[ks], dp);
       }
       const bool partial = rows_valid < rb + 32;  // rows past the Q block get P = 0
@@ -249,33 +304,26 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
       for (int q4 = 0; q4 < 4; ++q4) {
         const float4 l4 = *reinterpret_cast<const float4*>(lse2 + rb + 8 * q4 + 4 * hl);
         const float4 d4 = *reinterpret_cast<const float4*>(drs + rb + 8 * q4 + 4 * hl);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
         if (partial) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = 4 * q4 + u;
-            const float l = rb + 8 * q4 + 4 * hl + u >= rows_valid ? INFINITY : lv[u];
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -l) + kmask);
-            s[r] = p;
-            dp[r] = p * (dp[r] - dv[u]);
-          }
-        } else {
+          for (int u = 0; u < 4; ++u)
+            if (rb + 8 * q4 + 4 * hl + u >= rows_valid) lv[u] = INFINITY;
+        }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = 4 * q4 + u;
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -lv[u]) + kmask);
-            s[r] = p;
-            dp[r] = p * (dp[r] - dv[u]);
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * q4 + u;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c2, -lv[u]) + kmask);
+          sv[r] = p;
+          dp[r] = p * (dp[r] - dv[u]);
         }
       }
-      // dV^T += dO^T P, dK^T += Q^T dS (row steps of 16)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int o = 8 * kt;
-        const uint4 pp = make_uint4(E::pack(s[o], s[o + 1]), E::pack(s[o + 2], s[o + 3]),
-                                    E::pack(s[o + 4], s[o + 5]), E::pack(s[o + 6], s[o + 7]));
+        const uint4 pp = make_uint4(E::pack(sv[o], sv[o + 1]), E::pack(sv[o + 2], sv[o + 3]),
+                                    E::pack(sv[o + 4], sv[o + 5]), E::pack(sv[o + 6], sv[o + 7]));
         const uint4 ps = make_uint4(E::pack(dp[o], dp[o + 1]), E::pack(dp[o + 2], dp[o + 3]),
                                     E::pack(dp[o + 4], dp[o + 5]), E::pack(dp[o + 6], dp[o + 7]));
 #pragma unroll
@@ -285,76 +333,40 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
         }
       }
     };
-
-    // walk (head in group, KV-owned entry, row chunk)
-    int hh = 0, e = 0, e1 = 0, c = 0, i = 0, nch = 0;
-    auto row_of = [&](int hx) { return ((long long)b * g.Hq + hk * g.group + hx) * g.KVb + j; };
-    auto settle = [&]() {  // advance (hh, e) to the next entry with rows, from the current one
-      while (hh < g.group) {
-        if (e < e1) {
-          i = a.col[e];
-          nch = (g.q_exist(b, i) + QC - 1) / QC;
-          if (nch > 0) return;
-          ++e;
-          continue;
-        }
-        ++hh;
-        if (hh < g.group) {
-          const long long r = row_of(hh);
-          e = a.row_ptr[r];
-          e1 = a.row_ptr[r + 1];
-        }
-      }
+    // does this wave have work in a chunk with `rows` valid rows
+    auto busy = [&](int rows) { return wave_keys && rows > rb; };
+    // the chunk of slot s1 must have landed; the chunks loaded after it may
+    // stay in flight
+    auto wait_chunk = [&](int s1) {  // s1: slot of chunk n + 1
+      int later = 0;
+#pragma unroll
+      for (int k = 1; k < NST - 1; ++k) later += rem_of((s1 + k) % NST) != 0;
+      if (NST >= 4 && later >= 2) wait_vm<(NST >= 4 ? 2 : 0) * LPC>();
+      else if (NST >= 3 && later >= 1) wait_vm<(NST >= 3 ? 1 : 0) * LPC>();
+      else wait_vm<0>();
     };
-    {
-      const long long r = row_of(0);
-      e = a.row_ptr[r];
-      e1 = a.row_ptr[r + 1];
-      settle();
-    }
-    if (hh < g.group) {
-      stage(0, hk * g.group + hh, i, 0);
-      wait_vmem();
-      __syncthreads();
-      int buf = 0;
-      while (true) {
-        int nhh = hh, ne = e, ne1 = e1, nc = c + 1, ni = i, nnch = nch;
-        if (nc >= nch) {
-          const int shh = hh, se = e, se1 = e1, si = i, snch = nch;
-          ++e;
-          nc = 0;
-          settle();
-          nhh = hh;
-          ne = e;
-          ne1 = e1;
-          ni = i;
-          nnch = nch;
-          hh = shh;
-          e = se;
-          e1 = se1;
-          i = si;
-          nch = snch;
-        }
-        const bool has_next = nhh < g.group;
-        if (has_next) stage(buf ^ 1, hk * g.group + nhh, ni, nc);
-        compute(buf, g.q_exist(b, i) - c * QC);
-        wait_vmem();
-        __syncthreads();
-        if (!has_next) break;
-        hh = nhh;
-        e = ne;
-        e1 = ne1;
-        c = nc;
-        i = ni;
-        nch = nnch;
-        buf ^= 1;
+    auto next = [&](int s) { return s == NST - 1 ? 0 : s + 1; };
+
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < NST - 1; ++s) fill(s);
+      wait_vm<0>();  // the K tile, V columns and the first slot's rows
+      lds_barrier();
+      for (int s = 0;;) {
+        fill(s == 0 ? NST - 1 : s - 1);  // the slot freed by the previous step
+        const int rows = rem_of(s);
+        if (busy(rows)) compute(ring[s], rows);
+        s = next(s);
+        wait_chunk(s);
+        lds_barrier();
+        if (rem_of(s) == 0) break;
       }
     }
 
     if (RG > 1) {
-      // row groups 1.. hand their sums to row group 0 through LDS, one
-      // accumulator set at a time: [RG-1][KS][64 values][64 lanes] of fp32
-      float* red = reinterpret_cast<float*>(smem);
+      // row groups 1.. hand their sums to row group 0 through the (now idle)
+      // ring, one accumulator set at a time: [RG-1][KS][64 values][64 lanes]
+      float* red = reinterpret_cast<float*>(&ring[0][0]);
       auto reduce = [&](f32x16_t(&acc)[4]) {
         __syncthreads();
         if (rg > 0) {

@@ -51,13 +51,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // in these kernels reads M0, so setting it here clobbers nothing.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// base and lds are wave-uniform; readfirstlane states that to the compiler
+// (it folds away when they already live in scalar registers)
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(base)),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
                : "m0", "memory");
 }
 // the same with 4 bytes per lane (lane i fills lds + 4 i)
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(base)),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
                : "m0", "memory");
 }
 #pragma clang diagnostic pop
