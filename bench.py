@@ -142,6 +142,98 @@ def cpu_baseline(case, gpu_map_rows_seed=0, target_s=15.0):
     }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
+CSRC = os.path.join(ROOT, "bwd_block_map_amd", "csrc")
+# rocprofv3 kernel names of each stage (the dK/dV stage is three launches)
+STAGE_KERNELS = {"sparse_fwd": "sparse_fwd_kernel", "sparse_dkdv": "sparse_dkdv_kernel",
+                 "sparse_dq": "sparse_dq_kernel"}
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources: a traffic figure is only reported for
+    the kernels it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _counter_rows(path, counter):
+    """(kernel name, dispatch id) -> counter value (KiB) from a rocprofv3 counter CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                out[key] = out.get(key, 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_bytes, workload, command):
+    """Turn a FETCH_SIZE pass and a WRITE_SIZE pass (one bench run each, with a
+    copy probe of copy_bytes) into HBM bytes per stage launch. Each counter is
+    scaled by what it reads for the copy kernel, which moves copy_bytes in and
+    copy_bytes out."""
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+
+    def copy_kib(rows):
+        vals = [v for (n, _), v in rows.items() if "copyBuffer" in n or "copy_kernel" in n]
+        return max(vals) if vals else None
+
+    kib = copy_bytes / 1024.0
+    cf, cw = copy_kib(fetch), copy_kib(write)
+    if not cf or not cw:
+        raise SystemExit("no copy kernel found in the counter files (run bench.py with --copy-probe)")
+    ff, fw = kib / cf, kib / cw
+
+    def per_launch(rows, pattern):
+        vals = [v for (n, _), v in rows.items() if pattern in n]
+        n_disp = len(vals)
+        return (sum(vals) / n_disp if n_disp else 0.0), n_disp
+
+    stages = {}
+    for stage, pat in STAGE_KERNELS.items():
+        # per-kernel means, summed over the distinct kernels of the stage
+        names = sorted({n for (n, _) in fetch if pat in n})
+        b_f = b_w = 0.0
+        for n in names:
+            vf = [v for (m, _), v in fetch.items() if m == n]
+            vw = [v for (m, _), v in write.items() if m == n]
+            b_f += (sum(vf) / len(vf)) * ff * 1024.0 if vf else 0.0
+            b_w += (sum(vw) / len(vw)) * fw * 1024.0 if vw else 0.0
+        stages[stage] = {"fetch_bytes": b_f, "write_bytes": b_w, "bytes": b_f + b_w,
+                         "kernels": len(names)}
+    out = {"workload": workload, "command": command, "source_hash": kernel_source_hash(),
+           "copy_probe_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": ff, "write_scale": fw, "stages": stages,
+           "note": "HBM bytes per stage launch (the dK/dV stage sums its three launches); "
+                   "FETCH_SIZE and WRITE_SIZE are scaled by what they read for a plain "
+                   "copy of copy_probe_bytes"}
+    path = TRAFFIC_FILE.format(workload=workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out["stages"], indent=1))
+    print(f"wrote {path}")
+
+
+def stage_traffic(workload, stage):
+    """Measured HBM bytes per launch of a stage, or None when no measurement
+    exists or the kernels changed since it was taken."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t["stages"].get(stage, {}).get("bytes")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,7 +242,18 @@ def main():
     ap.add_argument("--workload", default="c5_vsa256_720p_gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="after timing, copy BYTES on the device once (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "passes (FETCH_SIZE, WRITE_SIZE) of a --copy-probe run, and exit")
+    ap.add_argument("--traffic-command", default="",
+                    help="the profiling command, recorded with --summarize-traffic")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
+                          args.copy_probe, args.workload, args.traffic_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(sharding by head groups is described in DESIGN.md)", file=sys.stderr)
@@ -221,7 +324,10 @@ def main():
     achieved = kflops[dom] / (dom_ms * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stage_traffic(case.name, dom),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                "copy-calibrated; null if not measured on these kernels)",
                 "ms_per_launch": round(dom_ms, 3)}
 
     fwd_t = fwd_flops / (fwd_ms * 1e-3) / 1e12
@@ -246,6 +352,12 @@ def main():
                           for k, v in per_kernel.items()},
         "roofline": roofline,
     }
+    if args.copy_probe > 0:  # a plain copy of known size, for counter calibration
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(case, target_s=args.cpu_seconds)
