@@ -297,3 +297,8 @@ class Buffers:
         self.map = None
         if p.topk > 0:
             self.map = torch.empty((p.B, p.Hq, p.Qb, p.KVb), dtype=torch.uint8, device=dev)
+
+
+# PyTorch entry points (autograd over vsa_fwd / vsa_bwd)
+from .torch_api import (attention, block_sparse_attn, video_sparse_attn,  # noqa: E402
+                        video_sparse_attn_bshd)
