@@ -11,16 +11,17 @@
 // gfx950 design.
 //  * bwd_pre: one work-group per (b, h, Q block); coalesced 16-byte loads of
 //    dO and O_sel, 16-lane shuffles for the row dot products; with a gate it
-//    also sums gate * dO over the tile (LDS) and forms dgate.
-//  * dK/dV: one work-group = NW waves x 32 keys of one KV block; K and V of
-//    the wave's keys stay in registers as MFMA B operands for S = Q K^T and
-//    dP = dO V^T (lane = key column, 16 query rows per lane); the Q heads of
-//    the group and the Q blocks of the KV-owned list are walked in chunks of
-//    32 rows, staged in LDS both row-major (for the d contractions) and
-//    transposed (for the row contractions dV^T += dO^T P, dK^T += Q^T dS).
-//    Accumulators stay in registers; one plain store per element at the end.
-//  * dQ: like the forward (Q-owned list, 64-key chunks, S^T and dP^T with
-//    lane = query row); dQ^T += K^T dS^T with K^T staged in LDS.
+//    also sums gate * dO over the tile (LDS) and forms dgate; it also writes
+//    lse * log2(e) for the exp2-based recomputation of P.
+//  * dK/dV: one 8-wave work-group per span of up to 256 keys of a KV block, in
+//    one of three shapes picked by the span's live keys (below). The K tile
+//    stays in LDS, V^T columns and the dK^T / dV^T accumulators in registers;
+//    the heads of the group and the Q blocks of the KV-owned list are walked
+//    in row chunks that arrive in LDS through a ring of direct loads. No
+//    atomics: one plain store per element at the end.
+//  * dQ: like the forward (Q-owned list, 64-key chunks through the shared
+//    K/V ring walker, S^T and dP^T with lane = query row); dQ^T += K^T dS^T
+//    with K^T read transposed from the K tile.
 #include "kernels.hpp"
 #include "kv_walk.hpp"
 
