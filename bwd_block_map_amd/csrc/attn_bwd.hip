@@ -169,6 +169,9 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
   constexpr int NST = S::NST, LPC = S::LPC;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NST][STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t Kt[KW * HD * 2];
+  // the V^T columns d >= 16 VREG live in LDS, not in registers: [ks - VREG][key][lane half]
+  constexpr int VREG = 6;
+  __shared__ uint4 Vx[(8 - VREG) * KW * 2];
   __shared__ int lst_i[DKDV_LIST_CAP];
 
   const Geom& g = a.g;
@@ -207,11 +210,16 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
     // register B operands (lane: key, d = 16ks + 8hl + 0..7)
     stage_rows<KW, NW>(Kt, wave, lane, a.k + kbase + (long long)k0 * krs, (uint32_t)(krs * 2),
                        min(live, KW) - 1);
-    uint4 vr[8];
+    uint4 vr[VREG];
     const long long koff = kbase + (long long)mykey * krs;
+    const int vx = (32 * kslot + (lane & 31)) * 2 + hl;  // this lane's slot in Vx
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      vr[ks] = key_live ? ldg16(a.v + koff + 16 * ks + 8 * hl) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks >= VREG && rg != 0) continue;  // row group 0 stores the shared columns
+      const uint4 v = key_live ? ldg16(a.v + koff + 16 * ks + 8 * hl) : make_uint4(0, 0, 0, 0);
+      if (ks < VREG) vr[ks] = v;
+      else Vx[(ks - VREG) * KW * 2 + vx] = v;
+    }
     const float kmask = key_live ? 0.f : -INFINITY;  // added to the exp2 argument
     const bool wave_keys = 32 * kslot < live;        // this wave has a live key
     const float c2 = g.scale * LOG2E;
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         sv = E::mfma(ro.at(Qs, rb, ks), ro.at(Kt, 32 * kslot, ks), sv);
-        dp = E::mfma(ro.at(Ds, rb, ks), vr[ks], dp);
+        dp = E::mfma(ro.at(Ds, rb, ks), ks < VREG ? vr[ks] : Vx[(ks - VREG) * KW * 2 + vx], dp);
       }
       const bool partial = rows_valid < rb + 32;  // rows past the Q block get P = 0
 #pragma unroll
