@@ -220,7 +220,6 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
       if (ks < VREG) vr[ks] = v;
       else Vx[(ks - VREG) * KW * 2 + vx] = v;
     }
-    const float kmask = key_live ? 0.f : -INFINITY;  // added to the exp2 argument
     const bool wave_keys = 32 * kslot < live;        // this wave has a live key
     const float c2 = g.scale * LOG2E;
     const long long qrs = g.q_rs();
@@ -231,17 +230,23 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
     const int qlen = g.q_len(b);
 
     // ---- the list walker: heads of the group, their KV-owned entries, row chunks ----
+    // A chunk's loads need only two running offsets (of its row 0 in q / dout
+    // and in lse2 / dr), so a fill is a few scalar adds and the direct loads.
     int hh = 0, e0 = 0, cnt = 0, page = 0;  // current head's CSR row and list page
     auto load_head = [&](int hx) {  // first list page of head hx (all waves; drains loads)
       const long long r = ((long long)b * g.Hq + hk * g.group + hx) * g.KVb + j;
-      e0 = a.row_ptr[r];
-      cnt = a.row_ptr[r + 1] - e0;
+      // uniform, and kept scalar: everything the fills derive from them stays scalar
+      e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[r]);
+      cnt = __builtin_amdgcn_readfirstlane(a.row_ptr[r + 1]) - e0;
       page = 0;
       __syncthreads();
       for (int t = tid; t < DKDV_LIST_CAP && t < cnt; t += NW * 64) lst_i[t] = a.col[e0 + t];
       __syncthreads();
     };
-    int se = 0, sc = 0, si = 0, sqe = 0;  // stager: entry, chunk, Q block, its rows
+    // stager: list entry se, rows of its Q block from the next chunk on, and
+    // the element offsets of the next chunk's row 0 in q / dout and lse2 / dr
+    int se = 0, left = 0;
+    long long cq = 0, cl = 0;
     bool more = true;
     auto settle = [&]() {  // from entry se of head hh, find the next entry (skipping empty heads)
       while (se >= cnt) {
@@ -258,35 +263,39 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
         for (int t = tid; t < DKDV_LIST_CAP && page + t < cnt; t += NW * 64) lst_i[t] = a.col[e0 + page + t];
         __syncthreads();
       }
-      si = lst_i[se - page];
-      sqe = max(0, min(g.q_block, qlen - si * g.q_block));  // >= 1 for a listed Q block
+      const int si = __builtin_amdgcn_readfirstlane(lst_i[se - page]);
+      left = max(0, min(g.q_block, qlen - si * g.q_block));  // >= 1 for a listed Q block
+      const int h = hk * g.group + hh;
+      const long long r0 = (long long)si * g.q_block;
+      cq = uniform_i64(g.q_base(b, h) + r0 * qrs);
+      cl = uniform_i64(g.lse_base(b, h) + r0 + rb);
     };
     load_head(0);
     settle();
 
     // per slot, 8 bits of `slots`: valid rows of its chunk (1 .. QC), 0 if empty
     uint32_t slots = 0;
+    const long long qstep = (long long)QC * qrs;
     auto fill = [&](int s) {
       slots &= ~(0xFFu << (8 * s));
       if (!more) return;
-      const int h = hk * g.group + hh;
-      const int left = sqe - sc * QC;  // rows of the block from this chunk on
-      const int last = left - 1;
-      slots |= (uint32_t)min(left, QC) << (8 * s);
-      const long long base = g.q_base(b, h) + (long long)(si * g.q_block + sc * QC) * qrs;
-      const long long lb = g.lse_base(b, h) + si * g.q_block + sc * QC + rb;
+      const int last = min(left, QC) - 1;  // rows past it repeat it
+      slots |= (uint32_t)(last + 1) << (8 * s);
       uint8_t* st = ring[s];
-      stage_rows<QC, NW>(st, wave, lane, a.q + base, qrs_bytes, last);
-      stage_rows<QC, NW>(st + QT, wave, lane, a.dout + base, qrs_bytes, last);
+      stage_rows<QC, NW>(st, wave, lane, a.q + cq, qrs_bytes, last);
+      stage_rows<QC, NW>(st + QT, wave, lane, a.dout + cq, qrs_bytes, last);
       // this wave's 32 rows of lse2 and dr (waves of one row group load the same values)
       const uint32_t loff = 4u * (uint32_t)min(lane, max(0, last - rb));
       const uint32_t lds_l = lds_addr(st + 2 * QT) + 4 * rb;
       if (lane < 32) {
-        dma4(a.lse2 + lb, loff, lds_l);
-        dma4(a.dr + lb, loff, lds_l + 4 * QC);
+        dma4(a.lse2 + cl, loff, lds_l);
+        dma4(a.dr + cl, loff, lds_l + 4 * QC);
       }
-      if (++sc * QC >= sqe) {
-        sc = 0;
+      left -= QC;
+      if (left > 0) {
+        cq += qstep;
+        cl += QC;
+      } else {
         ++se;
         settle();
       }
@@ -323,7 +332,9 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * q4 + u;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c2, -lv[u]) + kmask);
+          // a key past the live ones only feeds its own dK / dV column, which
+          // the epilogue writes as zero, so it needs no mask here
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c2, -lv[u]));
           sv[r] = p;
           dp[r] = p * (dp[r] - dv[u]);
         }
@@ -493,8 +504,8 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
     for (int r = 0; r < 16; ++r) acc[mb][r] = 0.f;
 
   const long long rid = ((long long)b * g.Hq + h) * g.Qb + i;
-  const int e0 = a.row_ptr[rid];
-  const int cnt = a.row_ptr[rid + 1] - e0;
+  const int e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[rid]);  // uniform: the walk stays scalar
+  const int cnt = __builtin_amdgcn_readfirstlane(a.row_ptr[rid + 1]) - e0;
 
   walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, cnt, a.k, a.v, wave, lane,
                    [&](const uint8_t* Ks, const uint8_t* Vs, int rem) {

@@ -59,8 +59,8 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
     qr[ks] = row_ok ? ldg16(a.q + qoff + 16 * ks + 8 * hl) : make_uint4(0, 0, 0, 0);
 
   const long long rid = ((long long)b * g.Hq + h) * g.Qb + i;
-  const int e0 = a.row_ptr[rid];
-  const int cnt = a.row_ptr[rid + 1] - e0;
+  const int e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[rid]);  // uniform: the walk stays scalar
+  const int cnt = __builtin_amdgcn_readfirstlane(a.row_ptr[rid + 1]) - e0;
 
   const float c2 = g.scale * LOG2E;
   // exp offset of this lane's row in log2 units: it moves only when a chunk's

@@ -34,7 +34,7 @@ __device__ __forceinline__ void walk_kv(const Geom& g, int b, int hk, const int3
   if (cnt <= 0) return;
 
   const int tid = wave * 64 + lane;
-  const long long kvb = g.kv_base(b, hk), krs = g.kv_rs();
+  const long long kvb = uniform_i64(g.kv_base(b, hk)), krs = g.kv_rs();
   const uint32_t krs_bytes = (uint32_t)(krs * 2);
   const int kvlen = g.kv_len(b);
   auto load_page = [&](int base) {
@@ -49,13 +49,25 @@ __device__ __forceinline__ void walk_kv(const Geom& g, int b, int hk, const int3
   wait_vm<0>();  // the caller's loads and the list page have landed
   __syncthreads();
 
-  // stager: the next chunk to load (entry se of the list, chunk sc of block sj)
-  int se = 0, sc = 0, page = 0;
-  int sj = lst_j[0], snv = lst_v[0];
+  // stager: the next chunk to load: entry se of the list, `left` keys of its
+  // block from that chunk on, and the element offset of the chunk's row 0.
+  // All of it is wave-uniform and kept scalar, so a fill is a few scalar adds
+  // and the direct loads.
+  int se = 0, page = 0, left = 0;
+  long long cur = 0;
   bool more = true;
+  auto enter = [&]() {  // entry se (on the current page) becomes the stager's block
+    const int j = __builtin_amdgcn_readfirstlane(lst_j[se - page]);
+    left = __builtin_amdgcn_readfirstlane(lst_v[se - page]);  // >= 1 for a listed block
+    cur = uniform_i64(kvb + (long long)j * g.kv_block * krs);
+  };
+  enter();
   auto advance = [&]() {
-    if (++sc * KV_CHUNK < snv) return;
-    sc = 0;
+    left -= KV_CHUNK;
+    if (left > 0) {
+      cur += (long long)KV_CHUNK * krs;
+      return;
+    }
     if (++se >= cnt) {
       more = false;
       return;
@@ -66,19 +78,16 @@ __device__ __forceinline__ void walk_kv(const Geom& g, int b, int hk, const int3
       load_page(page);
       __syncthreads();
     }
-    sj = lst_j[se - page];
-    snv = lst_v[se - page];
+    enter();
   };
   // per slot, 8 bits of `slots`: valid keys of its chunk (1 .. 64), 0 if empty
   uint32_t slots = 0;
   auto fill = [&](int s) {
     slots &= ~(0xFFu << (8 * s));
     if (!more) return;
-    const long long t0 = kvb + (long long)(sj * g.kv_block + sc * KV_CHUNK) * krs;
-    const int left = snv - sc * KV_CHUNK;  // keys of the block from this chunk on
     slots |= (uint32_t)min(left, KV_CHUNK) << (8 * s);
-    stage_rows<KV_CHUNK, NW>(ring[s][0], wave, lane, kp + t0, krs_bytes, left - 1);
-    stage_rows<KV_CHUNK, NW>(ring[s][1], wave, lane, vp + t0, krs_bytes, left - 1);
+    stage_rows<KV_CHUNK, NW>(ring[s][0], wave, lane, kp + cur, krs_bytes, left - 1);
+    stage_rows<KV_CHUNK, NW>(ring[s][1], wave, lane, vp + cur, krs_bytes, left - 1);
     advance();
   };
   auto rem_of = [&](int s) { return (int)((slots >> (8 * s)) & 0xFFu); };

@@ -59,6 +59,13 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
+// a wave-uniform 64-bit integer, stated as such (keeps derived values scalar)
+__device__ __forceinline__ long long uniform_i64(long long x) {
+  const uint64_t v = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (long long)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(base)),
                "s"(__builtin_amdgcn_readfirstlane(lds))
