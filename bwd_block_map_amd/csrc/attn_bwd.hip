@@ -244,7 +244,7 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
       __syncthreads();
     };
     // stager: list entry se, rows of its Q block from the next chunk on, and
-    // the element offsets of the next chunk's row 0 in q / dout and lse2 / dr
+    // the element offsets of the next chunk's row 0 in q / dout and in lse2 / dr
     int se = 0, left = 0;
     long long cq = 0, cl = 0;
     bool more = true;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
       const int h = hk * g.group + hh;
       const long long r0 = (long long)si * g.q_block;
       cq = uniform_i64(g.q_base(b, h) + r0 * qrs);
-      cl = uniform_i64(g.lse_base(b, h) + r0 + rb);
+      cl = uniform_i64(g.lse_base(b, h) + r0);
     };
     load_head(0);
     settle();
@@ -284,8 +284,9 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
       uint8_t* st = ring[s];
       stage_rows<QC, NW>(st, wave, lane, a.q + cq, qrs_bytes, last);
       stage_rows<QC, NW>(st + QT, wave, lane, a.dout + cq, qrs_bytes, last);
-      // this wave's 32 rows of lse2 and dr (waves of one row group load the same values)
-      const uint32_t loff = 4u * (uint32_t)min(lane, max(0, last - rb));
+      // this wave's 32 rows of lse2 and dr (waves of one row group load the same
+      // values); rows past the chunk's last repeat it, so no load leaves the block
+      const uint32_t loff = 4u * (uint32_t)min(rb + lane, last);
       const uint32_t lds_l = lds_addr(st + 2 * QT) + 4 * rb;
       if (lane < 32) {
         dma4(a.lse2 + cl, loff, lds_l);
@@ -468,7 +469,7 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level values stay scalar
   const int hl = lane >> 5, l32 = lane & 31;
-  const int nsub = g.q_block / (32 * NW);
+  const int nsub = max(1, g.q_block / (32 * NW));  // Q blocks of 8 or 16 rows: one wave
   int id = xcd_group(blockIdx.x, gridDim.x, nsub);
   const int sub = id % nsub;
   id /= nsub;
@@ -596,7 +597,7 @@ template <class ET>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int nw = g.q_block % 256 == 0 ? 8 : g.q_block % 128 == 0 ? 4 : g.q_block % 64 == 0 ? 2 : 1;
-  const long long nwg = (long long)g.B * g.Hq * g.Qb * (g.q_block / (32 * nw));
+  const long long nwg = (long long)g.B * g.Hq * g.Qb * max(1, g.q_block / (32 * nw));
   if (nwg == 0) return hipSuccess;
   if (nw == 8) sparse_dq_kernel<ET, 8, 4><<<(unsigned)nwg, 512, 0, st>>>(a);
   else if (nw == 4) sparse_dq_kernel<ET, 4, 2><<<(unsigned)nwg, 256, 0, st>>>(a);

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level values stay scalar
   const int hl = lane >> 5, l32 = lane & 31;
 
-  const int nsub = g.q_block / (32 * NW);
+  const int nsub = max(1, g.q_block / (32 * NW));  // Q blocks of 8 or 16 rows: one wave
   int id = xcd_group(blockIdx.x, gridDim.x, nsub);
   const int sub = id % nsub;
   id /= nsub;
@@ -181,7 +181,7 @@ template <class ET>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int nw = g.q_block % 256 == 0 ? 8 : g.q_block % 128 == 0 ? 4 : g.q_block % 64 == 0 ? 2 : 1;
-  const long long nwg = (long long)g.B * g.Hq * g.Qb * (g.q_block / (32 * nw));
+  const long long nwg = (long long)g.B * g.Hq * g.Qb * max(1, g.q_block / (32 * nw));
   if (nwg == 0) return hipSuccess;
   if (nw == 8) sparse_fwd_kernel<ET, 8, 4><<<(unsigned)nwg, 512, 0, st>>>(a);
   else if (nw == 4) sparse_fwd_kernel<ET, 4, 2><<<(unsigned)nwg, 256, 0, st>>>(a);

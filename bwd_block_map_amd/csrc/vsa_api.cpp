@@ -243,8 +243,9 @@ int validate(const vsa_problem* p) {
   if (p->D != vsa::HD) return fail(VSA_ERR_UNSUPPORTED, "head dimension %d: this build has D=128", p->D);
   if (p->q_block < 1 || p->kv_block < 1)
     return fail(VSA_ERR_INVALID_ARG, "q_block and kv_block must be positive");
-  if (p->q_block % 32 != 0 || p->kv_block % 64 != 0)
-    return fail(VSA_ERR_UNSUPPORTED, "q_block must be a multiple of 32 and kv_block of 64 (got %d, %d)",
+  if ((p->q_block % 32 != 0 && p->q_block != 8 && p->q_block != 16) || p->kv_block % 64 != 0)
+    return fail(VSA_ERR_UNSUPPORTED,
+                "q_block must be 8, 16 or a multiple of 32 and kv_block a multiple of 64 (got %d, %d)",
                 p->q_block, p->kv_block);
   if (p->Sq < 0 || p->Skv < 0) return fail(VSA_ERR_INVALID_ARG, "Sq and Skv must be >= 0");
   if (!(p->scale > 0.f) || !std::isfinite(p->scale))

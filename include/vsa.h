@@ -84,7 +84,8 @@ enum vsa_gate_mode {
  *                 reads KV head h / (Hq / Hkv)
  *   Sq, Skv       rows per batch entry (TND: total packed tokens Tq, Tkv)
  *   D             head dimension (this build: 128)
- *   q_block       rows per Q block, a multiple of 32
+ *   q_block       rows per Q block: 8, 16 or a multiple of 32 (8 and 16 run one
+ *                 32-row wave per block, with the rows past the block idle)
  *   kv_block      keys per KV block, a multiple of 64
  *   Qb, KVb       blocks per batch entry: ceil(Sq/q_block), ceil(Skv/kv_block)
  *                 (TND: of the longest sequence)

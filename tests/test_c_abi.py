@@ -45,6 +45,9 @@ def test_validate_accepts_the_workload_shapes():
                            gate_mode="per_token"))
     vsa.vsa_validate(_prob(dtype=torch.float16, B=2, Hq=8, Hkv=8, Sq=4096, Skv=4096,
                            q_block=128, kv_block=128))
+    # the Ascend page's [8, 128] block shape, and [16, 128]
+    vsa.vsa_validate(_prob(Sq=256, Skv=256, q_block=8, kv_block=128))
+    vsa.vsa_validate(_prob(Sq=256, Skv=256, q_block=16, kv_block=128))
 
 
 def _code(p):
@@ -64,6 +67,7 @@ def test_validate_rejects_bad_problems_with_messages():
     assert _code(_prob(Hq=3, Hkv=2))[0] == vsa.ERR_INVALID_ARG
     assert _code(_prob(D=64))[0] == vsa.ERR_UNSUPPORTED
     assert _code(_prob(q_block=48))[0] == vsa.ERR_UNSUPPORTED
+    assert _code(_prob(Sq=240, q_block=24))[0] == vsa.ERR_UNSUPPORTED
     assert _code(_prob(scale=float("nan")))[0] == vsa.ERR_INVALID_ARG
     assert _code(_prob(scale=-1.0))[0] == vsa.ERR_INVALID_ARG
     assert _code(_prob(topk=-1))[0] == vsa.ERR_INVALID_ARG

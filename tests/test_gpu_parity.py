@@ -81,6 +81,8 @@ SMALL = [
     ("p3_bnsd_fp16", {}),
     ("p3_bnsd_bf16", {}),
     ("p3_bnsd_sparse32", {}),
+    ("p3_bnsd_q8", {}),
+    ("p3_bnsd_q16", {}),
     ("p3_tnd_full", {}),
     ("p3_tnd_sparse", {}),
     ("p3_tnd_single", {}),
@@ -88,6 +90,7 @@ SMALL = [
     ("p3_tnd_group4", {}),
     ("p3_tnd_mqa", {}),
     ("p3_tnd_tail64", {}),
+    ("p3_tnd_q8", {}),
     ("c3_tnd_gqa", {}),
     ("c3_tnd_gqa_page", {}),
 ]
@@ -107,7 +110,7 @@ def test_fwd_bwd_parity_small(name, kw):
 
 def _index_cases():
     for n in ("c1_vsa256_tiny", "c2_bnsd_mha", "c3_tnd_gqa", "c3_tnd_gqa_page", "p3_tnd_uneven",
-              "p3_bnsd_sparse32", "p3_tnd_tail64"):
+              "p3_bnsd_sparse32", "p3_tnd_tail64", "p3_bnsd_q8", "p3_tnd_q8"):
         yield make_case(n)
     # empty KV tiles, an all-zero row and a 3-D (batch-shared) map
     yield build_case("idx_empty", B=2, Hq=2, D=128, q_block=64, kv_block=64,
@@ -216,6 +219,15 @@ def test_ragged_tails_and_q_block_64():
                       q_block=64, kv_block=128, Sq=300, Skv=333, map_kind="bernoulli",
                       map_p=0.5, seed=17)
     _compare_case(case, run_case(case), oracle.Oracle(case, np.float32))
+
+
+def test_ragged_tails_and_q_blocks_8_and_16():
+    for qb in (8, 16):
+        case = build_case(f"ragged_q{qb}", dtype="bf16", layout="bshd", B=2, Hq=4, Hkv=2, D=128,
+                          q_block=qb, kv_block=128, Sq=100, Skv=333, map_kind="bernoulli",
+                          map_p=0.4, seed=19 + qb)
+        _say(f"[ragged q_block={qb}]")
+        _compare_case(case, run_case(case), oracle.Oracle(case, np.float32))
 
 
 def test_c2_full_size_sampled_heads():

@@ -367,6 +367,9 @@ CASES: Dict[str, Callable[..., Case]] = {
     "p3_bnsd_fp16": _p3_bnsd("p3_bnsd_fp16", "fp16", 32, (128, 128), False),
     "p3_bnsd_bf16": _p3_bnsd("p3_bnsd_bf16", "bf16", 32, (128, 128), False),
     "p3_bnsd_sparse32": _p3_bnsd("p3_bnsd_sparse32", "fp16", 256, (32, 128), True),
+    # the Ascend page's multi-block sparse scenario, block_shape [8, 128], and [16, 128]
+    "p3_bnsd_q8": _p3_bnsd("p3_bnsd_q8", "fp16", 256, (8, 128), True),
+    "p3_bnsd_q16": _p3_bnsd("p3_bnsd_q16", "bf16", 256, (16, 128), True),
     "p3_tnd_full": _p3_tnd("p3_tnd_full", 12, 3, _PAGE_Q_LENS, _PAGE_KV_LENS, full=True),
     "p3_tnd_sparse": _p3_tnd("p3_tnd_sparse", 12, 3, _PAGE_Q_LENS, _PAGE_KV_LENS),
     "p3_tnd_single": _p3_tnd("p3_tnd_single", 4, 2, [127], [191], full=True),
@@ -374,6 +377,7 @@ CASES: Dict[str, Callable[..., Case]] = {
     "p3_tnd_group4": _p3_tnd("p3_tnd_group4", 8, 2, [96, 137], [111, 259]),
     "p3_tnd_mqa": _p3_tnd("p3_tnd_mqa", 8, 1, [65, 130], [129, 33]),
     "p3_tnd_tail64": _p3_tnd("p3_tnd_tail64", 4, 2, [65, 127, 3], [129, 11, 64], block=(64, 128)),
+    "p3_tnd_q8": _p3_tnd("p3_tnd_q8", 4, 2, [65, 127, 3, 30], [129, 11, 64, 200], block=(8, 128)),
 }
 
 
