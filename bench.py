@@ -144,7 +144,7 @@ def cpu_baseline(case, gpu_map_rows_seed=0, target_s=15.0):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
 CSRC = os.path.join(ROOT, "bwd_block_map_amd", "csrc")
-# rocprofv3 kernel names of each stage (the dK/dV stage is three launches)
+# rocprofv3 kernel names of each stage
 STAGE_KERNELS = {"sparse_fwd": "sparse_fwd_kernel", "sparse_dkdv": "sparse_dkdv_kernel",
                  "sparse_dq": "sparse_dq_kernel"}
 
@@ -211,7 +211,7 @@ def summarize_traffic(fetch_csv, write_csv, copy_bytes, workload, command):
     out = {"workload": workload, "command": command, "source_hash": kernel_source_hash(),
            "copy_probe_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale": ff, "write_scale": fw, "stages": stages,
-           "note": "HBM bytes per stage launch (the dK/dV stage sums its three launches); "
+           "note": "HBM bytes per stage launch; "
                    "FETCH_SIZE and WRITE_SIZE are scaled by what they read for a plain "
                    "copy of copy_probe_bytes"}
     path = TRAFFIC_FILE.format(workload=workload)

@@ -132,8 +132,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
 //   KS = 4 key slots x 2 row groups (128 keys, 64-row chunks)
 //   KS = 2 key slots x 4 row groups ( 64 keys, 128-row chunks)
 // Each row group takes 32 rows of a chunk; the row groups' sums are added
-// through LDS at the end. One launch per shape; a work-group whose span has
-// another shape returns at once.
+// through LDS at the end. One launch covers all three shapes: each work-group
+// runs the shape of its own span.
 //
 // Q / dO chunks (with the chunk rows' lse2 and D terms) go global -> LDS with
 // counted direct loads into a ring of NST slots, so NST - 1 chunks are in
@@ -161,38 +161,41 @@ struct DkdvShape {
 
 __device__ __forceinline__ int dkdv_shape(int live) { return live > 128 ? 8 : live > 64 ? 4 : 2; }
 
+// LDS of one shape, carved from the kernel's buffer: the Q/dO ring, the K
+// tile, the V^T columns d >= 16 DKDV_VREG ([ks - VREG][key][lane half]; the
+// registers do not hold all eight) and the list page
+constexpr int DKDV_VREG = 6;
+template <int KS>
+struct DkdvLds {
+  using S = DkdvShape<KS>;
+  static constexpr int KT = (S::NST * S::STAGE + 1023) / 1024 * 1024;
+  static constexpr int VX = KT + S::KW * HD * 2;
+  static constexpr int LST = VX + (8 - DKDV_VREG) * S::KW * 2 * 16;
+  static constexpr int BYTES = LST + DKDV_LIST_CAP * 4;
+};
+constexpr int imax(int x, int y) { return x > y ? x : y; }
+constexpr int DKDV_LDS = imax(DkdvLds<8>::BYTES, imax(DkdvLds<4>::BYTES, DkdvLds<2>::BYTES));
+static_assert(DKDV_LDS <= 160 * 1024, "dK/dV LDS budget");
+
+// dK / dV of keys k0 .. kend-1 of KV block j (live keys: the first `live`)
 template <class ET, int KS>
-__global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a) {
+__device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b, int hk, int j,
+                                          int k0, int kend, int nval, int live) {
   using E = Elem<ET>;
   using S = DkdvShape<KS>;
+  using L = DkdvLds<KS>;
   constexpr int NW = S::NW, RG = S::RG, QC = S::QC, QT = S::QT, STAGE = S::STAGE, KW = S::KW;
-  constexpr int NST = S::NST, LPC = S::LPC;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NST][STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t Kt[KW * HD * 2];
-  // the V^T columns d >= 16 VREG live in LDS, not in registers: [ks - VREG][key][lane half]
-  constexpr int VREG = 6;
-  __shared__ uint4 Vx[(8 - VREG) * KW * 2];
-  __shared__ int lst_i[DKDV_LIST_CAP];
+  constexpr int NST = S::NST, LPC = S::LPC, VREG = DKDV_VREG;
+  uint8_t* const ring = smem;  // slot s at ring + s * STAGE
+  uint8_t* const Kt = smem + L::KT;
+  uint4* const Vx = reinterpret_cast<uint4*>(smem + L::VX);
+  int* const lst_i = reinterpret_cast<int*>(smem + L::LST);
 
   const Geom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level values stay scalar
   const int hl = lane >> 5;
   const int kslot = wave % KS, rg = wave / KS;
-  const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
-  int id = xcd_group(blockIdx.x, gridDim.x, nspan);
-  const int span = id % nspan;
-  id /= nspan;
-  const int j = id % g.KVb;
-  id /= g.KVb;
-  const int hk = id % g.Hkv, b = id / g.Hkv;
-
-  const int k0 = span * DKDV_SPAN;
-  const int kend = min(g.kv_exist(b, j), min(g.kv_block, k0 + DKDV_SPAN));  // existing keys < kend
-  if (k0 >= kend) return;
-  const int nval = g.kv_val(b, j);
-  const int live = max(0, min(kend, nval) - k0);  // live keys of the span
-  if (dkdv_shape(live) != KS) return;
   const long long krs = g.kv_rs();
   const long long kbase = g.kv_base(b, hk) + (long long)j * g.kv_block * krs;
   const int mykey = k0 + 32 * kslot + (lane & 31);  // key inside the KV block
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
       if (!more) return;
       const int last = min(left, QC) - 1;  // rows past it repeat it
       slots |= (uint32_t)(last + 1) << (8 * s);
-      uint8_t* st = ring[s];
+      uint8_t* st = ring + s * STAGE;
       stage_rows<QC, NW>(st, wave, lane, a.q + cq, qrs_bytes, last);
       stage_rows<QC, NW>(st + QT, wave, lane, a.dout + cq, qrs_bytes, last);
       // this wave's 32 rows of lse2 and dr (waves of one row group load the same
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
       for (int s = 0;;) {
         fill(s == 0 ? NST - 1 : s - 1);  // the slot freed by the previous step
         const int rows = rem_of(s);
-        if (busy(rows)) compute(ring[s], rows);
+        if (busy(rows)) compute(ring + s * STAGE, rows);
         s = next(s);
         wait_chunk(s);
         lds_barrier();
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
     if (RG > 1) {
       // row groups 1.. hand their sums to row group 0 through the (now idle)
       // ring, one accumulator set at a time: [RG-1][KS][64 values][64 lanes]
-      float* red = reinterpret_cast<float*>(&ring[0][0]);
+      float* red = reinterpret_cast<float*>(ring);
       auto reduce = [&](f32x16_t(&acc)[4]) {
         __syncthreads();
         if (rg > 0) {
@@ -455,6 +458,31 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
       *reinterpret_cast<uint2*>(a.dv + koff + d0) =
           make_uint2(E::pack(vx[0], vx[1]), E::pack(vx[2], vx[3]));
     }
+}
+
+// One launch for all three shapes: each work-group picks its span's shape, so
+// the memory-bound 64-key spans of partial tiles run next to the MFMA-bound
+// 256-key spans instead of after them.
+template <class ET>
+__global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DKDV_LDS];
+  const Geom& g = a.g;
+  const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
+  int id = xcd_group(blockIdx.x, gridDim.x, nspan);
+  const int span = id % nspan;
+  id /= nspan;
+  const int j = id % g.KVb;
+  id /= g.KVb;
+  const int hk = id % g.Hkv, b = id / g.Hkv;
+  const int k0 = span * DKDV_SPAN;
+  const int kend = min(g.kv_exist(b, j), min(g.kv_block, k0 + DKDV_SPAN));  // existing keys < kend
+  if (k0 >= kend) return;
+  const int nval = g.kv_val(b, j);
+  const int live = max(0, min(kend, nval) - k0);  // live keys of the span
+  const int shape = dkdv_shape(live);
+  if (shape == 8) dkdv_span<ET, 8>(a, smem, b, hk, j, k0, kend, nval, live);
+  else if (shape == 4) dkdv_span<ET, 4>(a, smem, b, hk, j, k0, kend, nval, live);
+  else dkdv_span<ET, 2>(a, smem, b, hk, j, k0, kend, nval, live);
 }
 
 // ---------------------------------------------------------------------------
@@ -587,9 +615,7 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const long long n = (long long)g.B * g.Hkv * g.KVb * ((g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN);
   if (n == 0) return hipSuccess;
-  sparse_dkdv_kernel<ET, 8><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
-  sparse_dkdv_kernel<ET, 4><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
-  sparse_dkdv_kernel<ET, 2><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
+  sparse_dkdv_kernel<ET><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
