@@ -68,15 +68,26 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 }
 
 // Coarse scores for CR Q tiles, then (optionally) top-k -> map bytes and the
-// coarse attention O_c / lse_c. Dynamic LDS: sc[CR][KVb], qcs[CR][HD], hist[4][256].
-__global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int CR, int want_topk,
-                                                         int want_gate) {
+// coarse attention O_c / lse_c. Dynamic LDS: sc[CR][KVb], qcs[CR][HD],
+// hist[4][256] and a staging tile of CT pooled K (transposed) or V rows. The
+// pooled K and V rows are streamed through the tile with coalesced loads; every
+// score and every O_c element keeps its sequential accumulation order over d
+// (scores) and over the KV tiles (O_c).
+constexpr int CT = 64;               // pooled rows per staging tile
+constexpr int CT_LD = CT + 1;        // padded row of the transposed K tile
+constexpr int TILE_FLOATS = HD * CT_LD;
+constexpr int TILE_LOADS = CT * HD / 4 / 256;  // 16-byte loads per thread for one tile
+// CR is a template argument: with a run-time row count every "r < CR" test
+// becomes a branch around one FMA and serialises the LDS reads behind it.
+template <int CR>
+__global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int want_topk, int want_gate) {
   extern __shared__ float dsm[];
   const Geom& g = a.g;
   const int KVb = g.KVb;
   float* sc = dsm;
   float* qcs = sc + CR * KVb;
   int* hist = reinterpret_cast<int*>(qcs + CR * HD);
+  float* tile = reinterpret_cast<float*>(hist + 4 * 256);
   const int nrb = (g.Qb + CR - 1) / CR;
   int id = blockIdx.x;
   const int rb = id % nrb;
@@ -84,38 +95,53 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
   const int h = id % g.Hq, b = id / g.Hq;
   const int hk = h / g.group;
   const int i0 = rb * CR, nr = min(CR, g.Qb - i0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   for (int t = tid; t < CR * HD; t += 256) {
     const int r = t / HD, d = t % HD;
     qcs[t] = r < nr ? a.qc[g.pq(b, h, i0 + r) + d] : 0.f;
   }
   __syncthreads();
-  // scores: one KV tile per thread at a time
-  for (int j = tid; j < KVb; j += 256) {
-    const bool valid = g.kv_val(b, j) > 0;
-    float acc[16];
+  // scores, CT KV tiles at a time: the tiles' pooled K rows are staged
+  // transposed (tile[d][j]); thread (wave w, lane j) forms rows w, w+4, .. of
+  // column j, accumulating over d in order
+  for (int j0 = 0; j0 < KVb; j0 += CT) {
+    __syncthreads();  // the previous tile is consumed
+    float4 kv[TILE_LOADS];  // all loads of the tile in flight at once
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    if (valid) {
-      const float4* kp = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j));
-      for (int d4 = 0; d4 < HD / 4; ++d4) {
-        const float4 kv = kp[d4];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (r < CR) {
-            const float4 qv = *reinterpret_cast<const float4*>(qcs + r * HD + 4 * d4);
-            acc[r] = __builtin_fmaf(qv.x, kv.x, acc[r]);
-            acc[r] = __builtin_fmaf(qv.y, kv.y, acc[r]);
-            acc[r] = __builtin_fmaf(qv.z, kv.z, acc[r]);
-            acc[r] = __builtin_fmaf(qv.w, kv.w, acc[r]);
-          }
-        }
-      }
+    for (int k = 0; k < TILE_LOADS; ++k) {
+      const int t = tid + 256 * k, jj = t / (HD / 4), d4 = t % (HD / 4), j = min(j0 + jj, KVb - 1);
+      kv[k] = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j))[d4];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (r < CR) sc[r * KVb + j] = valid ? g.scale * acc[r] : -INFINITY;
+    for (int k = 0; k < TILE_LOADS; ++k) {
+      const int t = tid + 256 * k, jj = t / (HD / 4), d4 = t % (HD / 4);
+      tile[(4 * d4 + 0) * CT_LD + jj] = kv[k].x;
+      tile[(4 * d4 + 1) * CT_LD + jj] = kv[k].y;
+      tile[(4 * d4 + 2) * CT_LD + jj] = kv[k].z;
+      tile[(4 * d4 + 3) * CT_LD + jj] = kv[k].w;
+    }
+    __syncthreads();
+    // rows wave + 4u, u < RU (all of them exist when CR is a multiple of 4)
+    constexpr int RU = (CR + 3) / 4;
+    const int j = j0 + lane;
+    float acc[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) acc[u] = 0.f;
+    if (CR % 4 == 0 || wave < CR) {
+#pragma unroll 8
+      for (int d = 0; d < HD; ++d) {
+        const float kv = tile[d * CT_LD + lane];
+#pragma unroll
+        for (int u = 0; u < RU; ++u) acc[u] = __builtin_fmaf(qcs[(wave + 4 * u) * HD + d], kv, acc[u]);
+      }
+      if (j < KVb) {
+        const bool valid = g.kv_val(b, j) > 0;
+#pragma unroll
+        for (int u = 0; u < RU; ++u) sc[(wave + 4 * u) * KVb + j] = valid ? g.scale * acc[u] : -INFINITY;
+      }
+    }
   }
   __syncthreads();
 
@@ -217,18 +243,31 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
       if (lane == 0) a.lse_c[((long long)b * g.Hq + h) * g.Qb + i0 + r] = l > 0.f ? m + __logf(l) : -INFINITY;
     }
     __syncthreads();
-    // O_c[r][d] = sum_j P[r][j] V_c[j][d]
+    // O_c[r][d] = sum_j P[r][j] V_c[j][d], CT pooled V rows at a time (tile[j][d])
     const int d = tid & (HD - 1), half = tid >> 7;
     float acc[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-    const float* vcb = a.vc + g.pk(b, hk, 0) + d;
-    for (int j = 0; j < KVb; ++j) {
-      const float v = vcb[(long long)j * HD];
+    for (int j0 = 0; j0 < KVb; j0 += CT) {
+      __syncthreads();  // the previous tile is consumed
+      float4 vv[TILE_LOADS];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = half * 8 + u;
-        if (r < CR) acc[u] = __builtin_fmaf(sc[r * KVb + j], v, acc[u]);
+      for (int k = 0; k < TILE_LOADS; ++k) {
+        const int t = tid + 256 * k, jj = t / (HD / 4), d4 = t % (HD / 4), j = min(j0 + jj, KVb - 1);
+        vv[k] = reinterpret_cast<const float4*>(a.vc + g.pk(b, hk, j))[d4];
+      }
+#pragma unroll
+      for (int k = 0; k < TILE_LOADS; ++k) reinterpret_cast<float4*>(tile)[tid + 256 * k] = vv[k];
+      __syncthreads();
+      const int nj = min(CT, KVb - j0);
+      if (CR == 16 || half * 8 < CR) {
+#pragma unroll 4
+        for (int jj = 0; jj < nj; ++jj) {
+          const float v = tile[jj * HD + d];
+#pragma unroll
+          for (int u = 0; u < (CR < 8 ? CR : 8); ++u)
+            acc[u] = __builtin_fmaf(sc[(half * 8 + u) * KVb + j0 + jj], v, acc[u]);
+        }
       }
     }
 #pragma unroll
@@ -375,8 +414,8 @@ __global__ void zero_kernel(uint8_t* p, size_t n) {
 }  // namespace
 
 int coarse_rows_per_block(int KVb) {
-  // scores [CR][KVb] + qc [CR][HD] + 4 histograms must fit in 160 KiB
-  const long long budget = 160 * 1024 - 4 * 256 * 4;
+  // scores [CR][KVb] + qc [CR][HD] + 4 histograms + the staging tile must fit in 160 KiB
+  const long long budget = 160 * 1024 - 4 * 256 * 4 - TILE_FLOATS * 4;
   int cr = 16;
   while (cr > 1 && (long long)cr * (KVb + HD) * 4 > budget) cr >>= 1;
   return cr;
@@ -404,8 +443,15 @@ hipError_t launch_coarse_fwd(const CoarseArgs& a, bool want_topk, bool want_gate
   const int cr = coarse_rows_per_block(g.KVb);
   const long long n = (long long)g.B * g.Hq * ((g.Qb + cr - 1) / cr);
   if (n == 0) return hipSuccess;
-  const size_t lds = ((size_t)cr * (g.KVb + HD) + 4 * 256) * 4;
-  coarse_fwd_kernel<<<(unsigned)n, 256, lds, st>>>(a, cr, want_topk ? 1 : 0, want_gate ? 1 : 0);
+  const size_t lds = ((size_t)cr * (g.KVb + HD) + 4 * 256 + TILE_FLOATS) * 4;
+  const int tk = want_topk ? 1 : 0, gt = want_gate ? 1 : 0;
+  switch (cr) {
+    case 16: coarse_fwd_kernel<16><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
+    case 8: coarse_fwd_kernel<8><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
+    case 4: coarse_fwd_kernel<4><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
+    case 2: coarse_fwd_kernel<2><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
+    default: coarse_fwd_kernel<1><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
+  }
   return hipGetLastError();
 }
 
