@@ -279,8 +279,13 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
 }
 
 // Coarse backward, row form: P_c, dS_c for CR2 rows (kept in workspace for the
-// column pass) and dQ_c = scale dS_c K_c.
+// column pass) and dQ_c = scale dS_c K_c. The pooled K and V rows stream
+// through an LDS tile (transposed for the scores, row-major for dQ_c) with all
+// loads of a tile in flight.
 constexpr int CR2 = 8;
+constexpr int CT2 = 32;       // pooled rows per staging tile
+constexpr int CT2_LD = CT2 + 1;
+constexpr int TILE2_FLOATS = 2 * HD * CT2_LD;  // K^T | V^T
 __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a) {
   extern __shared__ float dsm[];
   const Geom& g = a.g;
@@ -290,6 +295,7 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a
   float* qcs = dS + CR2 * KVb;    // [CR2][HD]
   float* dos = qcs + CR2 * HD;    // [CR2][HD]
   float* lsc = dos + CR2 * HD;    // [CR2]
+  float* tile = lsc + CR2;        // TILE2_FLOATS
   const int nrb = (g.Qb + CR2 - 1) / CR2;
   int id = blockIdx.x;
   const int rb = id % nrb;
@@ -297,75 +303,105 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a
   const int h = id % g.Hq, b = id / g.Hq;
   const int hk = h / g.group;
   const int i0 = rb * CR2, nr = min(CR2, g.Qb - i0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int t = tid; t < CR2 * HD; t += 256) {
     const int r = t / HD, d = t % HD;
     qcs[t] = r < nr ? a.qc[g.pq(b, h, i0 + r) + d] : 0.f;
     dos[t] = r < nr ? a.doc[g.pq(b, h, i0 + r) + d] : 0.f;
   }
   if (tid < CR2) lsc[tid] = tid < nr ? a.lse_c[((long long)b * g.Hq + h) * g.Qb + i0 + tid] : -INFINITY;
-  __syncthreads();
-  for (int j = tid; j < KVb; j += 256) {
-    const bool valid = g.kv_val(b, j) > 0;
-    float cs[CR2], dp[CR2];
+  // scores and dP_c, CT2 KV tiles at a time: thread = (row 2 wave + lane / 32, column lane % 32)
+  const int r = 2 * wave + (lane >> 5), jj = lane & 31;
+  constexpr int LOADS = 2 * CT2 * HD / 4 / 256;
+  for (int j0 = 0; j0 < KVb; j0 += CT2) {
+    __syncthreads();  // the previous tile is consumed (and the rows above are loaded)
+    float4 x[LOADS];
 #pragma unroll
-    for (int r = 0; r < CR2; ++r) cs[r] = dp[r] = 0.f;
-    if (valid) {
-      const float4* kp = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j));
-      const float4* vp = reinterpret_cast<const float4*>(a.vc + g.pk(b, hk, j));
-      for (int d4 = 0; d4 < HD / 4; ++d4) {
-        const float4 kv = kp[d4], vv = vp[d4];
-#pragma unroll
-        for (int r = 0; r < CR2; ++r) {
-          const float4 qv = *reinterpret_cast<const float4*>(qcs + r * HD + 4 * d4);
-          const float4 ov = *reinterpret_cast<const float4*>(dos + r * HD + 4 * d4);
-          cs[r] += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
-          dp[r] += ov.x * vv.x + ov.y * vv.y + ov.z * vv.z + ov.w * vv.w;
-        }
-      }
+    for (int k = 0; k < LOADS; ++k) {
+      const int t = tid + 256 * k, arr = t / (CT2 * HD / 4), rem = t % (CT2 * HD / 4);
+      const int j = min(j0 + rem / (HD / 4), KVb - 1), d4 = rem % (HD / 4);
+      x[k] = reinterpret_cast<const float4*>((arr ? a.vc : a.kc) + g.pk(b, hk, j))[d4];
     }
 #pragma unroll
-    for (int r = 0; r < CR2; ++r) {
-      const float p = (valid && lsc[r] != -INFINITY) ? __expf(g.scale * cs[r] - lsc[r]) : 0.f;
+    for (int k = 0; k < LOADS; ++k) {
+      const int t = tid + 256 * k, arr = t / (CT2 * HD / 4), rem = t % (CT2 * HD / 4);
+      const int jt = rem / (HD / 4), d4 = rem % (HD / 4);
+      float* tt = tile + arr * HD * CT2_LD;
+      tt[(4 * d4 + 0) * CT2_LD + jt] = x[k].x;
+      tt[(4 * d4 + 1) * CT2_LD + jt] = x[k].y;
+      tt[(4 * d4 + 2) * CT2_LD + jt] = x[k].z;
+      tt[(4 * d4 + 3) * CT2_LD + jt] = x[k].w;
+    }
+    __syncthreads();
+    float cs = 0.f, dp = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < HD; ++d) {
+      cs = __builtin_fmaf(qcs[r * HD + d], tile[d * CT2_LD + jj], cs);
+      dp = __builtin_fmaf(dos[r * HD + d], tile[HD * CT2_LD + d * CT2_LD + jj], dp);
+    }
+    const int j = j0 + jj;
+    if (j < KVb) {
+      const bool valid = g.kv_val(b, j) > 0;
+      const float p = (valid && lsc[r] != -INFINITY) ? __expf(g.scale * cs - lsc[r]) : 0.f;
       P[r * KVb + j] = p;
-      dS[r * KVb + j] = p == 0.f ? 0.f : dp[r];
+      dS[r * KVb + j] = p == 0.f ? 0.f : dp;
     }
   }
   __syncthreads();
-  for (int r = wave; r < nr; r += 4) {
+  for (int rr = wave; rr < nr; rr += 4) {
     float s = 0.f;
-    for (int j = lane; j < KVb; j += 64) s += P[r * KVb + j] * dS[r * KVb + j];
+    for (int j = lane; j < KVb; j += 64) s += P[rr * KVb + j] * dS[rr * KVb + j];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    const long long ro = (((long long)b * g.Hq + h) * g.Qb + i0 + r) * KVb;
+    const long long ro = (((long long)b * g.Hq + h) * g.Qb + i0 + rr) * KVb;
     for (int j = lane; j < KVb; j += 64) {
-      const float p = P[r * KVb + j];
-      const float ds = p * (dS[r * KVb + j] - s);
-      dS[r * KVb + j] = ds;
+      const float p = P[rr * KVb + j];
+      const float ds = p * (dS[rr * KVb + j] - s);
+      dS[rr * KVb + j] = ds;
       a.dss[ro + j] = ds;
       a.ps[ro + j] = p;
     }
   }
-  __syncthreads();
+  // dQ_c[r][d] = scale sum_j dS_c[r][j] K_c[j][d], CT2 pooled K rows at a time (tile[j][d])
   const int d = tid & (HD - 1), half = tid >> 7;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const float* kcb = a.kc + g.pk(b, hk, 0) + d;
-  for (int j = 0; j < KVb; ++j) {
-    const float kv = kcb[(long long)j * HD];
+  constexpr int KLOADS = CT2 * HD / 4 / 256;
+  for (int j0 = 0; j0 < KVb; j0 += CT2) {
+    __syncthreads();  // dS is final / the previous tile is consumed
+    float4 x[KLOADS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = __builtin_fmaf(dS[(half * 4 + u) * KVb + j], kv, acc[u]);
+    for (int k = 0; k < KLOADS; ++k) {
+      const int t = tid + 256 * k, j = min(j0 + t / (HD / 4), KVb - 1), d4 = t % (HD / 4);
+      x[k] = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j))[d4];
+    }
+#pragma unroll
+    for (int k = 0; k < KLOADS; ++k) reinterpret_cast<float4*>(tile)[tid + 256 * k] = x[k];
+    __syncthreads();
+    const int nj = min(CT2, KVb - j0);
+#pragma unroll 4
+    for (int jt = 0; jt < nj; ++jt) {
+      const float kv = tile[jt * HD + d];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[u] = __builtin_fmaf(dS[(half * 4 + u) * KVb + j0 + jt], kv, acc[u]);
+    }
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int r = half * 4 + u;
-    if (r < nr) a.dqc[g.pq(b, h, i0 + r) + d] = g.scale * acc[u];
+    const int rr = half * 4 + u;
+    if (rr < nr) a.dqc[g.pq(b, h, i0 + rr) + d] = g.scale * acc[u];
   }
 }
 
 // Coarse backward, column form: dK_c = scale sum dS_c^T Q_c, dV_c = sum P_c^T dO_c
-// over the Q heads of the group (16 KV tiles per work-group, thread = (d, 8 tiles)).
+// over the Q heads of the group (16 KV tiles per work-group, thread = (d, 8
+// tiles)). The Q tiles' pooled rows and this block's dS_c / P_c columns are
+// staged in LDS CI tiles at a time, all loads of a stage in flight.
 constexpr int CC = 16;
+constexpr int CI = 32;
 __global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(const CoarseArgs a) {
+  __shared__ float4 qo[2][CI][HD / 4];  // q_c | dO_c rows
+  __shared__ float pd[2][CI][CC];       // dS_c | P_c of this block's columns
   const Geom& g = a.g;
   const int KVb = g.KVb;
   const int ncb = (KVb + CC - 1) / CC;
@@ -378,17 +414,40 @@ __global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(const CoarseArgs a
   float dk[8], dv[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) dk[u] = dv[u] = 0.f;
+  constexpr int QLOADS = 2 * CI * HD / 4 / 256, PLOADS = 2 * CI * CC / 256;
   for (int hh = 0; hh < g.group; ++hh) {
     const int h = hk * g.group + hh;
-    for (int i = 0; i < g.Qb; ++i) {
-      const float q = a.qc[g.pq(b, h, i) + d];
-      const float o = a.doc[g.pq(b, h, i) + d];
-      const long long ro = (((long long)b * g.Hq + h) * g.Qb + i) * KVb;
+    for (int i0 = 0; i0 < g.Qb; i0 += CI) {
+      float4 x[QLOADS];
+      float y[PLOADS];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (j0 + u < KVb) {
-          dk[u] = __builtin_fmaf(a.dss[ro + j0 + u], q, dk[u]);
-          dv[u] = __builtin_fmaf(a.ps[ro + j0 + u], o, dv[u]);
+      for (int k = 0; k < QLOADS; ++k) {
+        const int t = tid + 256 * k, arr = t / (CI * HD / 4), rem = t % (CI * HD / 4);
+        const int i = min(i0 + rem / (HD / 4), g.Qb - 1), d4 = rem % (HD / 4);
+        x[k] = reinterpret_cast<const float4*>((arr ? a.doc : a.qc) + g.pq(b, h, i))[d4];
+      }
+#pragma unroll
+      for (int k = 0; k < PLOADS; ++k) {
+        const int t = tid + 256 * k, arr = t / (CI * CC), rem = t % (CI * CC);
+        const int i = min(i0 + rem / CC, g.Qb - 1), j = cb * CC + rem % CC;
+        const long long ro = (((long long)b * g.Hq + h) * g.Qb + i) * KVb;
+        y[k] = j < KVb ? (arr ? a.ps : a.dss)[ro + j] : 0.f;
+      }
+      __syncthreads();  // the previous stage is consumed
+#pragma unroll
+      for (int k = 0; k < QLOADS; ++k) (&qo[0][0][0])[tid + 256 * k] = x[k];
+#pragma unroll
+      for (int k = 0; k < PLOADS; ++k) (&pd[0][0][0])[tid + 256 * k] = y[k];
+      __syncthreads();
+      const int ni = min(CI, g.Qb - i0);
+      const float* qrow = reinterpret_cast<const float*>(&qo[0][0][0]);
+      const float* orow = reinterpret_cast<const float*>(&qo[1][0][0]);
+      for (int ii = 0; ii < ni; ++ii) {
+        const float q = qrow[ii * HD + d], o = orow[ii * HD + d];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          dk[u] = __builtin_fmaf(pd[0][ii][half * 8 + u], q, dk[u]);
+          dv[u] = __builtin_fmaf(pd[1][ii][half * 8 + u], o, dv[u]);
         }
       }
     }
@@ -412,6 +471,10 @@ __global__ void zero_kernel(uint8_t* p, size_t n) {
 }
 
 }  // namespace
+
+size_t coarse_bwd_lds(int KVb) {
+  return ((size_t)2 * CR2 * KVb + 2 * CR2 * HD + CR2 + TILE2_FLOATS) * 4;
+}
 
 int coarse_rows_per_block(int KVb) {
   // scores [CR][KVb] + qc [CR][HD] + 4 histograms + the staging tile must fit in 160 KiB
@@ -460,7 +523,7 @@ hipError_t launch_coarse_bwd(const CoarseArgs& a, hipStream_t st) {
   const long long nr = (long long)g.B * g.Hq * ((g.Qb + CR2 - 1) / CR2);
   const long long nc = (long long)g.B * g.Hkv * ((g.KVb + CC - 1) / CC);
   if (nr == 0 || nc == 0) return hipSuccess;
-  const size_t lds = ((size_t)2 * CR2 * g.KVb + 2 * CR2 * HD + CR2) * 4;
+  const size_t lds = coarse_bwd_lds(g.KVb);
   coarse_bwd_rows_kernel<<<(unsigned)nr, 256, lds, st>>>(a);
   coarse_bwd_cols_kernel<<<(unsigned)nc, 256, 0, st>>>(a);
   return hipGetLastError();

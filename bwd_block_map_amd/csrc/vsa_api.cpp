@@ -15,6 +15,7 @@
 
 namespace vsa {
 int coarse_rows_per_block(int KVb);
+size_t coarse_bwd_lds(int KVb);
 }
 
 namespace {
@@ -278,7 +279,7 @@ int validate(const vsa_problem* p) {
   if (rows_total(p) >= (1LL << 31)) return fail(VSA_ERR_UNSUPPORTED, "B*Hq*Sq must stay below 2^31");
   if (is_video(p) && vsa::coarse_rows_per_block(p->KVb) < 1)
     return fail(VSA_ERR_UNSUPPORTED, "KVb %d too large for the coarse kernels", p->KVb);
-  if (p->gate_mode != VSA_GATE_NONE && ((size_t)2 * 8 * p->KVb + 2 * 8 * 128 + 8) * 4 > 160 * 1024)
+  if (p->gate_mode != VSA_GATE_NONE && vsa::coarse_bwd_lds(p->KVb) > 160 * 1024)
     return fail(VSA_ERR_UNSUPPORTED, "KVb %d too large for the compression backward", p->KVb);
   return VSA_OK;
 }
