@@ -173,6 +173,77 @@ def _counter_rows(path, counter):
     return out
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_{workload}.txt")
+PMC_COUNTERS = ("SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_VALU_MFMA_BUSY_CYCLES "
+                "SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VMEM GRBM_GUI_ACTIVE")
+
+
+def summarize_counters(counter_csv, agent_csv, workload, command):
+    """Per-kernel MFMA use from one rocprofv3 --pmc pass (PMC_COUNTERS) over a
+    bench step: executed MFMA work (every MFMA here is a 32x32x16 one, 32768
+    flop), the share of cycles the MFMA pipes were busy, the sustained clock,
+    instruction mix per MFMA and, for the sparse stages, HBM GB/s from the
+    traffic file. Durations are the counter run's own dispatch timestamps."""
+    import csv
+    import re
+    agent = next(a for a in csv.DictReader(open(agent_csv)) if a.get("Name", "").startswith("gfx"))
+    n_xcc, n_simd = int(agent["Num_Xcc"]), int(agent["Simd_Count"])
+    per = {}
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            if "vsa" not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "c": {}})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    agg = {}
+    for d in per.values():
+        n = re.sub(r"\(.*$", "", d["name"].replace("vsa::(anonymous namespace)::", "").replace("void ", ""))
+        a = agg.setdefault(n, {"n": 0, "s": 0.0, "c": {}})
+        a["n"] += 1
+        a["s"] += d["s"]
+        for c, v in d["c"].items():
+            a["c"][c] = a["c"].get(c, 0.0) + v
+    traffic = {}
+    tpath = TRAFFIC_FILE.format(workload=workload)
+    if os.path.exists(tpath):
+        tr = json.load(open(tpath))
+        if tr.get("source_hash") == kernel_source_hash():
+            traffic = tr["stages"]
+    lines = [f"# rocprofv3 counter summary, {workload}",
+             f"# command: {command}",
+             f"# counters: {PMC_COUNTERS}",
+             "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs): the share of",
+             "# cycles the MFMA pipes worked; clock = GRBM_GUI_ACTIVE / XCDs / duration (the",
+             "# sustained engine clock during the kernel); executed TFLOP/s counts every issued",
+             "# MFMA (padding included), % of 2.5 PF against the dense bf16 peak at 2.4 GHz.",
+             "# HBM GB/s: FETCH_SIZE + WRITE_SIZE bytes per launch (traffic file) / duration.",
+             "",
+             f"{'kernel':44s} {'calls':>5s} {'ms':>8s} {'GHz':>5s} {'exec TF/s':>9s} {'%2.5PF':>6s} "
+             f"{'MFMA busy':>9s} {'VALU/MFMA':>9s} {'LDS/MFMA':>8s} {'SALU/MFMA':>9s} {'HBM GB/s':>8s}"]
+    for n, a in sorted(agg.items(), key=lambda kv: -kv[1]["s"]):
+        c, k = a["c"], a["n"]
+        sec = a["s"] / k
+        mf = c.get("SQ_INSTS_MFMA", 0.0) / k
+        grbm = c.get("GRBM_GUI_ACTIVE", 0.0) / k
+        ghz = grbm / n_xcc / sec * 1e-9 if sec > 0 else 0.0
+        tf = mf * 32768 / sec * 1e-12 if sec > 0 else 0.0
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / k / (grbm / n_xcc * n_simd) if grbm else 0.0
+        ratio = (lambda x: f"{c.get(x, 0.0) / k / mf:9.2f}" if mf else f"{'-':>9s}")
+        gbs = "-"
+        for stage, pat in STAGE_KERNELS.items():
+            if pat in n and stage in traffic:
+                gbs = f"{traffic[stage]['bytes'] / sec * 1e-9:8.0f}"
+        lines.append(f"{n[:44]:44s} {k:5d} {sec * 1e3:8.2f} {ghz:5.2f} {tf:9.1f} {100 * tf / 2500:6.1f} "
+                     f"{100 * busy:8.1f}% {ratio('SQ_INSTS_VALU')} {ratio('SQ_INSTS_LDS')[1:]} "
+                     f"{ratio('SQ_INSTS_SALU')} {gbs:>8s}")
+    path = COUNTERS_FILE.format(workload=workload)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    print(f"wrote {path}")
+
+
 def summarize_traffic(fetch_csv, write_csv, copy_bytes, workload, command):
     """Turn a FETCH_SIZE pass and a WRITE_SIZE pass (one bench run each, with a
     copy probe of copy_bytes) into HBM bytes per stage launch. Each counter is
@@ -247,9 +318,18 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "passes (FETCH_SIZE, WRITE_SIZE) of a --copy-probe run, and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_CSV", "AGENT_CSV"),
+                    help="write profiles/counters_<workload>.txt from one rocprofv3 --pmc pass "
+                         "over the counters in PMC_COUNTERS, and exit")
+    ap.add_argument("--counters-command", default="",
+                    help="the profiling command, recorded with --summarize-counters")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command, recorded with --summarize-traffic")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
+                           args.counters_command)
+        return
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
                           args.copy_probe, args.workload, args.traffic_command)
