@@ -23,21 +23,6 @@ __device__ __forceinline__ uint32_t toff(int r, int c) {
   return (uint32_t)(r * 256 + ((c ^ swz(r)) << 4));
 }
 
-// Stage RT rows into a tile with direct 16-byte global->LDS loads. Each wave
-// instruction fills 4 rows (1 KiB); lane l writes physical chunk l & 15 of
-// row 4p + (l >> 4), so it fetches logical chunk (l & 15) ^ swz(row).
-// src(row) returns the global address of element 0 of that tile row.
-template <int RT, int NW, class F>
-__device__ __forceinline__ void stage_tile(uint8_t* tile, int wave, int lane, F src) {
-#pragma unroll
-  for (int p = wave; p < RT / 4; p += NW) {
-    const int row = 4 * p + (lane >> 4);
-    const int c = (lane & 15) ^ swz(row);
-    __builtin_amdgcn_global_load_lds((const void*)(src(row) + 8 * c), (void*)(tile + p * 1024), 16,
-                                     0, 0);
-  }
-}
-
 // LDS address (byte offset) of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -115,15 +100,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Stage N <= 64 consecutive fp32 values with one wave instruction: lane i
-// (i < N) writes word i of dst; entries past `last` repeat entry `last`.
-template <int N>
-__device__ __forceinline__ void stage_f32(float* dst, const float* src, int lane, int last) {
-  static_assert(N <= 64, "one wave instruction");
-  if (lane < N)
-    __builtin_amdgcn_global_load_lds((const void*)(src + min(lane, last)), (void*)dst, 4, 0, 0);
-}
-
 // Work-group barrier for LDS tiles filled by direct loads. __syncthreads()
 // carries a release fence that on this target drains every outstanding global
 // load, which would also wait for the chunks prefetched further ahead. Here
@@ -136,14 +112,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// all outstanding vector-memory operations (including direct LDS fills) done
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
-
-// Row-wise MFMA operand: lane reads 8 elements (16 B) of row r, chunk c.
-__device__ __forceinline__ uint4 row16(const uint8_t* tile, int r, int c) {
-  return *reinterpret_cast<const uint4*>(tile + toff(r, c));
 }
 
 // Per-lane byte offsets of the row-wise operand reads. A wave reads rows
@@ -183,13 +151,6 @@ struct TrLane {
     half = 8u * (uint32_t)(i & 1);
   }
 };
-
-__device__ __forceinline__ uint4 tr_operand(const uint8_t* tile, const TrLane& t, int rb, int mb) {
-  const int r = rb + (int)t.row_off, c = 4 * mb + t.c_off;
-  const uint2 lo = tr8(tile, toff(r, c) + t.half);
-  const uint2 hi = tr8(tile, toff(r + 8, c) + t.half);
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
 
 // Per-lane byte offsets of the transposed operand reads: rows rb + {0..15}
 // with rb a multiple of 16, so for each (low / high row group, mb) the offset
