@@ -178,6 +178,13 @@ PMC_COUNTERS = ("SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_VALU_
                 "SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VMEM GRBM_GUI_ACTIVE")
 
 
+def _short_kernel(name):
+    """A kernel's name without argument lists and namespaces, as the summaries print it."""
+    import re
+    n = name.replace("vsa::(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*$", "", n)
+
+
 def summarize_counters(counter_csv, agent_csv, workload, command):
     """Per-kernel MFMA use from one rocprofv3 --pmc pass (PMC_COUNTERS) over a
     bench step: executed MFMA work (every MFMA here is a 32x32x16 one, 32768
@@ -198,7 +205,7 @@ def summarize_counters(counter_csv, agent_csv, workload, command):
             d["s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
     agg = {}
     for d in per.values():
-        n = re.sub(r"\(.*$", "", d["name"].replace("vsa::(anonymous namespace)::", "").replace("void ", ""))
+        n = _short_kernel(d["name"])
         a = agg.setdefault(n, {"n": 0, "s": 0.0, "c": {}})
         a["n"] += 1
         a["s"] += d["s"]
@@ -209,15 +216,17 @@ def summarize_counters(counter_csv, agent_csv, workload, command):
     if os.path.exists(tpath):
         tr = json.load(open(tpath))
         if tr.get("source_hash") == kernel_source_hash():
-            traffic = tr["stages"]
-    lines = [f"# rocprofv3 counter summary, {workload}",
+            traffic = tr.get("kernels", {})
+    lines = [f"# rocprofv3 counter summary, {workload} ({agent['Name']}: {agent['Cu_Count']} CUs, "
+             f"{n_simd} SIMDs, {n_xcc} XCDs)",
              f"# command: {command}",
              f"# counters: {PMC_COUNTERS}",
              "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs): the share of",
              "# cycles the MFMA pipes worked; clock = GRBM_GUI_ACTIVE / XCDs / duration (the",
              "# sustained engine clock during the kernel); executed TFLOP/s counts every issued",
              "# MFMA (padding included), % of 2.5 PF against the dense bf16 peak at 2.4 GHz.",
-             "# HBM GB/s: FETCH_SIZE + WRITE_SIZE bytes per launch (traffic file) / duration.",
+             "# HBM GB/s: FETCH_SIZE + WRITE_SIZE bytes per launch (traffic file, copy-calibrated)",
+             "# / duration.",
              "",
              f"{'kernel':44s} {'calls':>5s} {'ms':>8s} {'GHz':>5s} {'exec TF/s':>9s} {'%2.5PF':>6s} "
              f"{'MFMA busy':>9s} {'VALU/MFMA':>9s} {'LDS/MFMA':>8s} {'SALU/MFMA':>9s} {'HBM GB/s':>8s}"]
@@ -230,10 +239,7 @@ def summarize_counters(counter_csv, agent_csv, workload, command):
         tf = mf * 32768 / sec * 1e-12 if sec > 0 else 0.0
         busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / k / (grbm / n_xcc * n_simd) if grbm else 0.0
         ratio = (lambda x: f"{c.get(x, 0.0) / k / mf:9.2f}" if mf else f"{'-':>9s}")
-        gbs = "-"
-        for stage, pat in STAGE_KERNELS.items():
-            if pat in n and stage in traffic:
-                gbs = f"{traffic[stage]['bytes'] / sec * 1e-9:8.0f}"
+        gbs = f"{traffic[n]['bytes'] / sec * 1e-9:8.0f}" if n in traffic and sec > 0 else "-"
         lines.append(f"{n[:44]:44s} {k:5d} {sec * 1e3:8.2f} {ghz:5.2f} {tf:9.1f} {100 * tf / 2500:6.1f} "
                      f"{100 * busy:8.1f}% {ratio('SQ_INSTS_VALU')} {ratio('SQ_INSTS_LDS')[1:]} "
                      f"{ratio('SQ_INSTS_SALU')} {gbs:>8s}")
@@ -279,9 +285,18 @@ def summarize_traffic(fetch_csv, write_csv, copy_bytes, workload, command):
             b_w += (sum(vw) / len(vw)) * fw * 1024.0 if vw else 0.0
         stages[stage] = {"fetch_bytes": b_f, "write_bytes": b_w, "bytes": b_f + b_w,
                          "kernels": len(names)}
+    # every kernel of the library, per launch (pooling, index, coarse, ... too)
+    kernels = {}
+    for n in sorted({n for (n, _) in fetch if "vsa" in n}):
+        vf = [v for (m, _), v in fetch.items() if m == n]
+        vw = [v for (m, _), v in write.items() if m == n]
+        b_f = (sum(vf) / len(vf)) * ff * 1024.0
+        b_w = (sum(vw) / len(vw)) * fw * 1024.0 if vw else 0.0
+        kernels[_short_kernel(n)] = {"fetch_bytes": b_f, "write_bytes": b_w, "bytes": b_f + b_w,
+                                     "launches": len(vf)}
     out = {"workload": workload, "command": command, "source_hash": kernel_source_hash(),
            "copy_probe_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
-           "fetch_scale": ff, "write_scale": fw, "stages": stages,
+           "fetch_scale": ff, "write_scale": fw, "stages": stages, "kernels": kernels,
            "note": "HBM bytes per stage launch; "
                    "FETCH_SIZE and WRITE_SIZE are scaled by what they read for a plain "
                    "copy of copy_probe_bytes"}
@@ -390,8 +405,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     prof = vsa.vsa_profile_end()
-    fwd_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
-    bwd_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
+    fwd_all = [a.elapsed_time(b) for a, b, _ in ev]
+    bwd_all = [b.elapsed_time(c) for _, b, c in ev]
+    fwd_ms, bwd_ms = float(np.median(fwd_all)), float(np.median(bwd_all))
     step_ms = wall * 1e3 / args.steps
     log(f"[bench] timed {args.steps} steps: fwd {fwd_ms:.2f} ms, bwd {bwd_ms:.2f} ms")
 
@@ -423,6 +439,7 @@ def main():
                    "gate": case.gate_mode, "tokens_valid": int(np.sum(case.q_var))
                    if case.q_var is not None else case.Sq},
         "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+        "fwd_ms_min": round(float(min(fwd_all)), 3), "bwd_ms_min": round(float(min(bwd_all)), 3),
         "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2),
         "fwd_frac_of_peak": round(fwd_t / PEAK_BF16_TFLOPS, 4),
         "bwd_frac_of_peak": round(bwd_t / PEAK_BF16_TFLOPS, 4),
