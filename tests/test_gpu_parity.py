@@ -230,6 +230,21 @@ def test_ragged_tails_and_q_blocks_8_and_16():
         _compare_case(case, run_case(case), oracle.Oracle(case, np.float32))
 
 
+def test_block_lists_longer_than_one_page():
+    """More than 1024 selected blocks per row: the Q-owned walk (forward, dQ)
+    and the KV-owned walk (dK/dV) page their block lists through LDS; GQA makes
+    dK/dV walk a second head after the first one's pages."""
+    cases = [
+        build_case("long_kv_list", dtype="bf16", layout="bhsd", B=1, Hq=2, Hkv=1, D=128,
+                   q_block=256, kv_block=64, Sq=256, Skv=64 * 1040, map_kind="ones", seed=23),
+        build_case("long_q_list", dtype="fp16", layout="bshd", B=1, Hq=2, Hkv=1, D=128,
+                   q_block=32, kv_block=64, Sq=32 * 1040, Skv=128, map_kind="ones", seed=29),
+    ]
+    for case in cases:
+        _say(f"[{case.name}] Qb={case.Qb} KVb={case.KVb}")
+        _compare_case(case, run_case(case), oracle.Oracle(case, np.float32))
+
+
 def test_c2_full_size_sampled_heads():
     """BNSD S=4096 at its full size; the oracle evaluates two whole heads."""
     case = make_case("c2_bnsd_mha")
