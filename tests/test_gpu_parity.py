@@ -233,12 +233,14 @@ def test_ragged_tails_and_q_blocks_8_and_16():
 def test_video_tiles_with_shared_kv_heads():
     """Pooled-score top-k and the gated compression branch with 4 query heads
     on 2 KV heads: coarse scores per query head against the shared pooled K,
-    dK_c / dV_c and the sparse dK / dV summed over each KV head's group."""
-    for gate in ("per_token", "per_element"):
-        case = build_case(f"video_gqa_{gate}", dtype="bf16", layout="bshd", B=1, Hq=4, Hkv=2,
-                          D=128, q_var=[256, 256, 97, 256], kv_var=[256, 64, 256, 173, 16],
-                          topk=3, map_kind="none", gate_mode=gate, gate_kind="sigmoid",
-                          seed=31)
+    dK_c / dV_c and the sparse dK / dV summed over each KV head's group; also
+    two batch entries in fp16 (a map per batch entry)."""
+    for dtype, layout, B, gate in (("bf16", "bshd", 1, "per_token"), ("bf16", "bshd", 1, "per_element"),
+                                   ("fp16", "bhsd", 2, "per_token")):
+        case = build_case(f"video_gqa_{dtype}_{layout}_b{B}_{gate}", dtype=dtype, layout=layout, B=B,
+                          Hq=4, Hkv=2, D=128, q_var=[256, 256, 97, 256],
+                          kv_var=[256, 64, 256, 173, 16], topk=3, map_kind="none", gate_mode=gate,
+                          gate_kind="sigmoid", seed=31)
         _say(f"[{case.name}]")
         res = run_case(case)
         orc = oracle.Oracle(case, np.float32)
