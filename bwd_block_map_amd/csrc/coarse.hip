@@ -279,13 +279,11 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
 }
 
 // Coarse backward, row form: P_c, dS_c for CR2 rows (kept in workspace for the
-// column pass) and dQ_c = scale dS_c K_c. The pooled K and V rows stream
-// through an LDS tile (transposed for the scores, row-major for dQ_c) with all
-// loads of a tile in flight.
+// column pass) and dQ_c = scale dS_c K_c. For dQ_c the pooled K rows stream
+// through an LDS tile with all loads of a tile in flight.
 constexpr int CR2 = 8;
-constexpr int CT2 = 32;       // pooled rows per staging tile
-constexpr int CT2_LD = CT2 + 1;
-constexpr int TILE2_FLOATS = 2 * HD * CT2_LD;  // K^T | V^T
+constexpr int CT2 = 32;                  // pooled K rows per staging tile
+constexpr int TILE2_FLOATS = CT2 * HD;
 __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a) {
   extern __shared__ float dsm[];
   const Geom& g = a.g;
@@ -295,7 +293,7 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a
   float* qcs = dS + CR2 * KVb;    // [CR2][HD]
   float* dos = qcs + CR2 * HD;    // [CR2][HD]
   float* lsc = dos + CR2 * HD;    // [CR2]
-  float* tile = lsc + CR2;        // TILE2_FLOATS
+  float* tile = lsc + CR2;        // [CT2][HD]
   const int nrb = (g.Qb + CR2 - 1) / CR2;
   int id = blockIdx.x;
   const int rb = id % nrb;
@@ -311,41 +309,31 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a
     dos[t] = r < nr ? a.doc[g.pq(b, h, i0 + r) + d] : 0.f;
   }
   if (tid < CR2) lsc[tid] = tid < nr ? a.lse_c[((long long)b * g.Hq + h) * g.Qb + i0 + tid] : -INFINITY;
-  // scores and dP_c, CT2 KV tiles at a time: thread = (row 2 wave + lane / 32, column lane % 32)
-  const int r = 2 * wave + (lane >> 5), jj = lane & 31;
-  constexpr int LOADS = 2 * CT2 * HD / 4 / 256;
-  for (int j0 = 0; j0 < KVb; j0 += CT2) {
-    __syncthreads();  // the previous tile is consumed (and the rows above are loaded)
-    float4 x[LOADS];
+  __syncthreads();
+  for (int j = tid; j < KVb; j += 256) {
+    const bool valid = g.kv_val(b, j) > 0;
+    float cs[CR2], dp[CR2];
 #pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
-      const int t = tid + 256 * k, arr = t / (CT2 * HD / 4), rem = t % (CT2 * HD / 4);
-      const int j = min(j0 + rem / (HD / 4), KVb - 1), d4 = rem % (HD / 4);
-      x[k] = reinterpret_cast<const float4*>((arr ? a.vc : a.kc) + g.pk(b, hk, j))[d4];
+    for (int r = 0; r < CR2; ++r) cs[r] = dp[r] = 0.f;
+    if (valid) {
+      const float4* kp = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j));
+      const float4* vp = reinterpret_cast<const float4*>(a.vc + g.pk(b, hk, j));
+      for (int d4 = 0; d4 < HD / 4; ++d4) {
+        const float4 kv = kp[d4], vv = vp[d4];
+#pragma unroll
+        for (int r = 0; r < CR2; ++r) {
+          const float4 qv = *reinterpret_cast<const float4*>(qcs + r * HD + 4 * d4);
+          const float4 ov = *reinterpret_cast<const float4*>(dos + r * HD + 4 * d4);
+          cs[r] += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
+          dp[r] += ov.x * vv.x + ov.y * vv.y + ov.z * vv.z + ov.w * vv.w;
+        }
+      }
     }
 #pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
-      const int t = tid + 256 * k, arr = t / (CT2 * HD / 4), rem = t % (CT2 * HD / 4);
-      const int jt = rem / (HD / 4), d4 = rem % (HD / 4);
-      float* tt = tile + arr * HD * CT2_LD;
-      tt[(4 * d4 + 0) * CT2_LD + jt] = x[k].x;
-      tt[(4 * d4 + 1) * CT2_LD + jt] = x[k].y;
-      tt[(4 * d4 + 2) * CT2_LD + jt] = x[k].z;
-      tt[(4 * d4 + 3) * CT2_LD + jt] = x[k].w;
-    }
-    __syncthreads();
-    float cs = 0.f, dp = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < HD; ++d) {
-      cs = __builtin_fmaf(qcs[r * HD + d], tile[d * CT2_LD + jj], cs);
-      dp = __builtin_fmaf(dos[r * HD + d], tile[HD * CT2_LD + d * CT2_LD + jj], dp);
-    }
-    const int j = j0 + jj;
-    if (j < KVb) {
-      const bool valid = g.kv_val(b, j) > 0;
-      const float p = (valid && lsc[r] != -INFINITY) ? __expf(g.scale * cs - lsc[r]) : 0.f;
+    for (int r = 0; r < CR2; ++r) {
+      const float p = (valid && lsc[r] != -INFINITY) ? __expf(g.scale * cs[r] - lsc[r]) : 0.f;
       P[r * KVb + j] = p;
-      dS[r * KVb + j] = p == 0.f ? 0.f : dp;
+      dS[r * KVb + j] = p == 0.f ? 0.f : dp[r];
     }
   }
   __syncthreads();
