@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -284,6 +285,40 @@ int validate(const vsa_problem* p) {
   return VSA_OK;
 }
 
+// A pointer a kernel may dereference: device or managed memory, or pinned host
+// memory with a device mapping. A plain host pointer (which would fault the
+// GPU) is rejected here, before any launch.
+bool device_accessible(const void* ptr) {
+  hipPointerAttribute_t a{};
+  const hipError_t e = hipPointerGetAttributes(&a, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // an unregistered pointer is an answer, not a pending error
+    return false;
+  }
+  return a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged ||
+         (a.type == hipMemoryTypeHost && a.devicePointer != nullptr);
+}
+
+struct Arg {
+  const void* ptr;
+  const char* name;
+};
+
+// every non-NULL pointer of a compute call, the problem's own ones included
+int check_device(const vsa_problem* p, std::initializer_list<Arg> args) {
+  const Arg own[] = {{p->q_valid, "q_valid"},
+                     {p->kv_valid, "kv_valid"},
+                     {p->cu_seqlens_q, "cu_seqlens_q"},
+                     {p->cu_seqlens_kv, "cu_seqlens_kv"}};
+  for (const Arg& a : own)
+    if (a.ptr && !device_accessible(a.ptr))
+      return fail(VSA_ERR_INVALID_ARG, "%s must be a device tensor", a.name);
+  for (const Arg& a : args)
+    if (a.ptr && !device_accessible(a.ptr))
+      return fail(VSA_ERR_INVALID_ARG, "%s must be a device tensor", a.name);
+  return VSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -323,6 +358,8 @@ int block_map_to_index(const vsa_problem* p, const uint8_t* block_map, int kv_ow
   if (!row_ptr || (!col_idx && col_capacity > 0))
     return fail(VSA_ERR_INVALID_ARG, "row_ptr / col_idx must be device buffers");
   if (col_capacity < 0) return fail(VSA_ERR_INVALID_ARG, "col_capacity must be >= 0");
+  if (int c = check_device(p, {{block_map, "block_map"}, {row_ptr, "row_ptr"}, {col_idx, "col_idx"}}))
+    return c;
   const vsa::Geom g = make_geom(p);
   hipError_t e;
   {
@@ -356,6 +393,9 @@ int vsa_fwd(const vsa_problem* p, const void* q, const void* k, const void* v, u
   if (saved && saved_bytes < need_saved)
     return fail(VSA_ERR_WORKSPACE, "saved state: %zu bytes needed, %zu given", need_saved,
                 saved_bytes);
+  if (int c = check_device(p, {{q, "q"}, {k, "k"}, {v, "v"}, {block_map, "block_map"}, {gate, "gate"},
+                               {out, "out"}, {lse, "lse"}, {saved, "saved"}, {ws, "ws"}}))
+    return c;
   hipStream_t st = (hipStream_t)stream;
   const FwdWs w = carve_fwd(p, ws, nullptr);
   const Saved s = saved ? carve_saved(p, saved, nullptr) : Saved{};
@@ -449,6 +489,10 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
     return fail(VSA_ERR_WORKSPACE, "saved state: %zu bytes needed, %zu given", need_saved, saved_bytes);
   if (ws_bytes < need_ws || (!ws && need_ws))
     return fail(VSA_ERR_WORKSPACE, "backward workspace: %zu bytes needed, %zu given", need_ws, ws_bytes);
+  if (int c = check_device(p, {{q, "q"}, {k, "k"}, {v, "v"}, {gate, "gate"}, {dout, "dout"},
+                               {out, "out"}, {lse, "lse"}, {saved, "saved"}, {dq, "dq"}, {dk, "dk"},
+                               {dv, "dv"}, {dgate, "dgate"}, {ws, "ws"}}))
+    return c;
   hipStream_t st = (hipStream_t)stream;
   const long long qn = q_elems(p);
   const long long kn = p->layout == VSA_TND ? (long long)p->Skv * p->Hkv * p->D

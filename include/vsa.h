@@ -27,6 +27,12 @@
  *  - Return value: VSA_OK or one of the VSA_ERR_* codes. Argument errors are
  *    detected on the host before anything is launched; vsa_last_error() then
  *    returns a message (thread-local, valid until the next call on the thread).
+ *    The compute calls (block_map_to_index, vsa_fwd, vsa_bwd) check every
+ *    non-NULL pointer they are given, the problem's valid-count and
+ *    cu_seqlens arrays included, with hipPointerGetAttributes: device or
+ *    managed memory, or pinned host memory with a device mapping, is accepted;
+ *    a plain host pointer gives VSA_ERR_INVALID_ARG ("<name> must be a device
+ *    tensor").
  *  - Layouts of q-shaped tensors (q, out, dout, dq, per-element gate):
  *      VSA_BHSD [B, Hq, Sq, D], VSA_BSHD [B, Sq, Hq, D], VSA_TND [Tq, Hq, D];
  *    kv-shaped tensors (k, v, dk, dv) have Hkv heads and Skv (Tkv) rows.

@@ -248,6 +248,37 @@ def test_video_tiles_with_shared_kv_heads():
         _compare_case(case, res, orc)
 
 
+def test_host_pointers_are_rejected_before_any_launch():
+    """The C ABI itself (not only the Python wrapper) refuses a plain host
+    pointer for a tensor or for a valid-count array, with INVALID_ARG."""
+    import ctypes as C
+    case = make_case("c1_vsa256_tiny")
+    d = device_inputs(case)
+    p = problem_for(case, d)
+    buf = vsa.Buffers(p, d["q"], training=True)
+    bmap = d["map"] if case.topk == 0 else buf.map
+    assert case.gate_mode == "none"
+    host_q = d["q"].cpu()
+    L = vsa.lib()
+
+    def fwd(prob, q):
+        return L.vsa_fwd(prob.ref, C.c_void_p(q.data_ptr()), C.c_void_p(d["k"].data_ptr()),
+                         C.c_void_p(d["v"].data_ptr()), C.c_void_p(bmap.data_ptr()), None,
+                         C.c_void_p(buf.out.data_ptr()), C.c_void_p(buf.lse.data_ptr()),
+                         C.c_void_p(buf.saved.data_ptr()), C.c_size_t(buf.saved.numel()),
+                         C.c_void_p(buf.ws_fwd.data_ptr()), C.c_size_t(buf.ws_fwd.numel()),
+                         C.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+    assert fwd(p, host_q) == vsa.ERR_INVALID_ARG
+    assert vsa.vsa_last_error() == "q must be a device tensor"
+    host_kv = d["kv_valid"].cpu()
+    p2 = problem_for(case, dict(d, kv_valid=host_kv))
+    assert fwd(p2, d["q"]) == vsa.ERR_INVALID_ARG
+    assert vsa.vsa_last_error() == "kv_valid must be a device tensor"
+    assert fwd(p, d["q"]) == vsa.OK  # the same call with device memory runs
+    torch.cuda.synchronize()
+
+
 def test_block_lists_longer_than_one_page():
     """More than 1024 selected blocks per row: the Q-owned walk (forward, dQ)
     and the KV-owned walk (dK/dV) page their block lists through LDS; GQA makes
