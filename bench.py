@@ -250,6 +250,30 @@ def summarize_counters(counter_csv, agent_csv, workload, command):
     print(f"wrote {path}")
 
 
+KERNELS_FILE = os.path.join(ROOT, "profiles", "kernels_{workload}.txt")
+
+
+def summarize_trace(db_path, workload, command):
+    """Per-kernel calls, mean and total duration from a rocprofv3 --kernel-trace
+    results database, as a short text table."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = list(db.execute("select name, count(*), sum(duration), avg(duration) from kernels "
+                           "group by name order by sum(duration) desc"))
+    total = sum(r[2] for r in rows) or 1
+    lines = [f"# rocprofv3 kernel-trace summary, {workload}", f"# command: {command}", "",
+             f"{'kernel':62s} {'calls':>5s} {'avg_ms':>10s} {'total_ms':>10s} {'pct':>6s}"]
+    for name, calls, tot, avg in rows:
+        n = _short_kernel(name)
+        n = "torch: " + n[len("at::"):] if n.startswith("at::") else n
+        lines.append(f"{n[:62]:62s} {calls:5d} {avg / 1e6:10.3f} {tot / 1e6:10.3f} {100 * tot / total:6.2f}")
+    path = KERNELS_FILE.format(workload=workload)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    print(f"wrote {path}")
+
+
 def summarize_traffic(fetch_csv, write_csv, copy_bytes, workload, command):
     """Turn a FETCH_SIZE pass and a WRITE_SIZE pass (one bench run each, with a
     copy probe of copy_bytes) into HBM bytes per stage launch. Each counter is
@@ -336,11 +360,19 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("COUNTER_CSV", "AGENT_CSV"),
                     help="write profiles/counters_<workload>.txt from one rocprofv3 --pmc pass "
                          "over the counters in PMC_COUNTERS, and exit")
+    ap.add_argument("--summarize-trace", metavar="RESULTS_DB",
+                    help="write profiles/kernels_<workload>.txt from a rocprofv3 --kernel-trace "
+                         "results database, and exit")
+    ap.add_argument("--trace-command", default="",
+                    help="the profiling command, recorded with --summarize-trace")
     ap.add_argument("--counters-command", default="",
                     help="the profiling command, recorded with --summarize-counters")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command, recorded with --summarize-traffic")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.trace_command)
+        return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
                            args.counters_command)
