@@ -48,6 +48,9 @@ def test_validate_accepts_the_workload_shapes():
     # the Ascend page's [8, 128] block shape, and [16, 128]
     vsa.vsa_validate(_prob(Sq=256, Skv=256, q_block=8, kv_block=128))
     vsa.vsa_validate(_prob(Sq=256, Skv=256, q_block=16, kv_block=128))
+    # KV blocks of any multiple of 64 keys, Q blocks of any multiple of 32 rows
+    for qb, kb in [(64, 64), (96, 192), (32, 320), (128, 512)]:
+        vsa.vsa_validate(_prob(Sq=1024, Skv=1024, q_block=qb, kv_block=kb))
 
 
 def _code(p):

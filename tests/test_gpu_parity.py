@@ -91,6 +91,10 @@ SMALL = [
     ("p3_tnd_mqa", {}),
     ("p3_tnd_tail64", {}),
     ("p3_tnd_q8", {}),
+    ("p3_bnsd_kv64", {}),
+    ("p3_tnd_kv192", {}),
+    ("p3_tnd_kv320", {}),
+    ("p3_bnsd_kv512", {}),
     ("c3_tnd_gqa", {}),
     ("c3_tnd_gqa_page", {}),
 ]

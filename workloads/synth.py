@@ -378,6 +378,13 @@ CASES: Dict[str, Callable[..., Case]] = {
     "p3_tnd_mqa": _p3_tnd("p3_tnd_mqa", 8, 1, [65, 130], [129, 33]),
     "p3_tnd_tail64": _p3_tnd("p3_tnd_tail64", 4, 2, [65, 127, 3], [129, 11, 64], block=(64, 128)),
     "p3_tnd_q8": _p3_tnd("p3_tnd_q8", 4, 2, [65, 127, 3, 30], [129, 11, 64, 200], block=(8, 128)),
+    # KV blocks other than 128 / 256: one 64-key chunk per block; 192 keys with
+    # 96-row Q blocks (three 32-row waves per block); 320 keys (a dK/dV span of
+    # 256 keys plus one of 64); 512 keys (two full spans)
+    "p3_bnsd_kv64": _p3_bnsd("p3_bnsd_kv64", "bf16", 512, (64, 64), True),
+    "p3_tnd_kv192": _p3_tnd("p3_tnd_kv192", 4, 2, [65, 300, 7], [129, 500, 400], block=(96, 192)),
+    "p3_tnd_kv320": _p3_tnd("p3_tnd_kv320", 4, 1, [33, 250, 700], [321, 640, 650], block=(32, 320)),
+    "p3_bnsd_kv512": _p3_bnsd("p3_bnsd_kv512", "fp16", 1024, (128, 512), False),
 }
 
 
