@@ -350,10 +350,16 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
                                     E::pack(sv[o + 4], sv[o + 5]), E::pack(sv[o + 6], sv[o + 7]));
         const uint4 ps = make_uint4(E::pack(dp[o], dp[o + 1]), E::pack(dp[o + 2], dp[o + 3]),
                                     E::pack(dp[o + 4], dp[o + 5]), E::pack(dp[o + 6], dp[o + 7]));
+        uint4 nv = to.at(Ds, rb + 16 * kt, 0), nk = to.at(Qs, rb + 16 * kt, 0);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-          dva[mb] = E::mfma(to.at(Ds, rb + 16 * kt, mb), pp, dva[mb]);
-          dka[mb] = E::mfma(to.at(Qs, rb + 16 * kt, mb), ps, dka[mb]);
+          const uint4 cv = nv, ck = nk;
+          if (mb < 3) {  // the next step's operands are read before this step's MFMAs
+            nv = to.at(Ds, rb + 16 * kt, mb + 1);
+            nk = to.at(Qs, rb + 16 * kt, mb + 1);
+          }
+          dva[mb] = E::mfma(cv, pp, dva[mb]);
+          dka[mb] = E::mfma(ck, ps, dka[mb]);
         }
       }
     };
