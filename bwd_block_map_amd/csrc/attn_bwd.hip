@@ -316,10 +316,19 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       f32x16_t sv, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
+      uint4 nq = ro.at(Qs, rb, 0), nk = ro.at(Kt, 32 * kslot, 0), nd = ro.at(Ds, rb, 0);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sv = E::mfma(ro.at(Qs, rb, ks), ro.at(Kt, 32 * kslot, ks), sv);
-        dp = E::mfma(ro.at(Ds, rb, ks), ks < VREG ? vr[ks] : Vx[(ks - VREG) * KW * 2 + vx], dp);
+        const uint4 cq = nq, ck = nk, cd = nd;
+        if (ks < 7) {  // the next step's operands are read before this step's MFMAs
+          nq = ro.at(Qs, rb, ks + 1);
+          nk = ro.at(Kt, 32 * kslot, ks + 1);
+          nd = ro.at(Ds, rb, ks + 1);
+        }
+        // keeps the scheduler from sinking those reads back next to their use
+        __builtin_amdgcn_sched_barrier(0);
+        sv = E::mfma(cq, ck, sv);
+        dp = E::mfma(cd, ks < VREG ? vr[ks] : Vx[(ks - VREG) * KW * 2 + vx], dp);
       }
       const bool partial = rows_valid < rb + 32;  // rows past the Q block get P = 0
 #pragma unroll
