@@ -253,7 +253,9 @@ def vsa_bwd(p: Problem, q, k, v, gate, dout, out, lse, saved, dq, dk, dv, dgate,
         _check_tensors(p, q, k, v, gate, qlike=(("dout", dout), ("out", out), ("dq", dq)),
                        kvlike=(("dk", dk), ("dv", dv)), lse=lse)
         if dgate is not None:
-            _expect(dgate, gate.numel(), "dgate")
+            if gate is None:
+                raise ValueError("dgate needs the gate it is the gradient of")
+            _expect(dgate, gate.numel(), "dgate", gate.dtype)
     _check(lib().vsa_bwd(
         p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(dout), _ptr(out), _ptr(lse),
         _ptr(saved), C.c_size_t(0 if saved is None else saved.numel() * saved.element_size()),
