@@ -65,9 +65,10 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
 #pragma clang diagnostic pop
 
 // Stage RT rows of a tile whose row r lives at base + min(r, last) * rs_bytes:
-// the base is uniform and each lane adds a 32-bit offset (row < 256, so
-// min(r, last) * rs_bytes stays far below 2^32 for any head count the C ABI
-// accepts), which keeps the address arithmetic to two 24-bit integer ops.
+// the base is uniform and each lane adds a 32-bit offset computed with a 24-bit
+// multiply (row < 256; the C ABI keeps a row stride below 2^24 bytes, fewer
+// than 65536 heads in the token-major layouts, so the offset stays below 2^32),
+// which keeps the address arithmetic to two 24-bit integer ops.
 template <int RT, int NW>
 __device__ __forceinline__ void stage_rows(uint8_t* tile, int wave, int lane, const uint16_t* base,
                                            uint32_t rs_bytes, int last) {

@@ -275,6 +275,11 @@ int validate(const vsa_problem* p) {
       return fail(VSA_ERR_INVALID_ARG, "Qb/KVb must be ceil(S/block): got %d/%d, want %lld/%lld",
                   p->Qb, p->KVb, ceil_div(p->Sq, p->q_block), ceil_div(p->Skv, p->kv_block));
   }
+  // tiles are staged with 24-bit row offsets: a row stride (heads x 256 B in the
+  // token-major layouts) must stay below 2^24 bytes
+  if (p->layout != VSA_BHSD && (p->Hq >= 65536 || p->Hkv >= 65536))
+    return fail(VSA_ERR_UNSUPPORTED, "BSHD and TND need fewer than 65536 heads (Hq=%d Hkv=%d)",
+                p->Hq, p->Hkv);
   if ((long long)p->B * p->Hq * p->Qb * std::max(p->KVb, 1) >= (1LL << 31))
     return fail(VSA_ERR_UNSUPPORTED, "B*Hq*Qb*KVb must stay below 2^31");
   if (rows_total(p) >= (1LL << 31)) return fail(VSA_ERR_UNSUPPORTED, "B*Hq*Sq must stay below 2^31");

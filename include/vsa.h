@@ -143,7 +143,11 @@ int vsa_abi_version(void);
 
 /* Host-only check of a problem (no device access). Messages for the cases
  * the pages name: "actual_seq_lengths must be specified",
- * "actual_seq_lengths_kv must be specified" (TND without cu_seqlens_q / _kv). */
+ * "actual_seq_lengths_kv must be specified" (TND without cu_seqlens_q / _kv).
+ * Limits of this build (VSA_ERR_UNSUPPORTED): D = 128; q_block 8, 16 or a
+ * multiple of 32, kv_block a multiple of 64; fewer than 65536 heads in BSHD and
+ * TND (row offsets of the tile loads are 24-bit); B*Hq*Qb*KVb and B*Hq*Sq below
+ * 2^31; KVb small enough for the coarse kernels' LDS when top-k or a gate is on. */
 int vsa_validate(const vsa_problem* p);
 
 /*

@@ -68,6 +68,9 @@ def test_validate_rejects_bad_problems_with_messages():
                        q_block=128, kv_block=128, cu_seqlens_q=fake))
     assert c == vsa.ERR_INVALID_ARG and m == "actual_seq_lengths_kv must be specified"
     assert _code(_prob(Hq=3, Hkv=2))[0] == vsa.ERR_INVALID_ARG
+    # 24-bit row offsets of the tile loads: token-major rows of 65536 heads are too long
+    c, m = _code(_prob(layout="bshd", Hq=65536, Hkv=65536, Sq=256, Skv=256))
+    assert c == vsa.ERR_UNSUPPORTED and "65536 heads" in m
     assert _code(_prob(D=64))[0] == vsa.ERR_UNSUPPORTED
     assert _code(_prob(q_block=48))[0] == vsa.ERR_UNSUPPORTED
     assert _code(_prob(Sq=240, q_block=24))[0] == vsa.ERR_UNSUPPORTED
