@@ -146,12 +146,12 @@ struct Geom {
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void stg16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
-// max / sum of a value and its copy in lane l ^ 32
 // Maximum without the NaN quieting of fmaxf (which costs one extra
 // instruction per operand): NaN propagates, v_maximum3_f32 takes three inputs.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
+// max / sum of a value and its copy in lane l ^ 32
 __device__ __forceinline__ float xhalf_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
