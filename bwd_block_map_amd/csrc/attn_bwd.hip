@@ -152,12 +152,22 @@ struct DkdvShape {
   static constexpr int QT = QC * HD * 2;             // bytes of a QC-row tile
   static constexpr int STAGE = 2 * QT + 2 * QC * 4;  // Q | dO | lse2 | dr
   static constexpr int NST = KS == 8 ? 4 : KS == 4 ? 3 : 2;  // ring slots (LDS budget)
-  // direct loads per chunk and wave: Q and dO rows, then its own rows' lse2 and dr
-  static constexpr int LPC = 2 * (QC / 4 / NW) + 2;
+  // direct loads per chunk and wave: Q and dO rows; the first wave of each row
+  // group also loads the group's lse2 and dr
+  static constexpr int LPC_ROWS = 2 * (QC / 4 / NW);
+  static constexpr int LPC = LPC_ROWS + 2;
   static_assert(NW % KS == 0 && (QC / 4) % NW == 0, "whole row groups, equal load shares");
   static_assert((RG - 1) * KS * 64 * 64 * 4 <= NST * STAGE, "row-group reduction fits in the ring");
   static_assert(STAGE % 256 == 0, "slots keep the 256-byte row alignment");
 };
+
+// wait until at most `later` chunks of L direct loads each are outstanding
+template <int NST, int L>
+__device__ __forceinline__ void wait_later(int later) {
+  if (NST >= 4 && later >= 2) wait_vm<(NST >= 4 ? 2 : 0) * L>();
+  else if (NST >= 3 && later >= 1) wait_vm<(NST >= 3 ? 1 : 0) * L>();
+  else wait_vm<0>();
+}
 
 __device__ __forceinline__ int dkdv_shape(int live) { return live > 128 ? 8 : live > 64 ? 4 : 2; }
 
@@ -185,7 +195,7 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
   using S = DkdvShape<KS>;
   using L = DkdvLds<KS>;
   constexpr int NW = S::NW, RG = S::RG, QC = S::QC, QT = S::QT, STAGE = S::STAGE, KW = S::KW;
-  constexpr int NST = S::NST, LPC = S::LPC, VREG = DKDV_VREG;
+  constexpr int NST = S::NST, LPC = S::LPC, LPC_ROWS = S::LPC_ROWS, VREG = DKDV_VREG;
   uint8_t* const ring = smem;  // slot s at ring + s * STAGE
   uint8_t* const Kt = smem + L::KT;
   uint4* const Vx = reinterpret_cast<uint4*>(smem + L::VX);
@@ -287,11 +297,11 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       uint8_t* st = ring + s * STAGE;
       stage_rows<QC, NW>(st, wave, lane, a.q + cq, qrs_bytes, last);
       stage_rows<QC, NW>(st + QT, wave, lane, a.dout + cq, qrs_bytes, last);
-      // this wave's 32 rows of lse2 and dr (waves of one row group load the same
-      // values); rows past the chunk's last repeat it, so no load leaves the block
+      // the row group's 32 rows of lse2 and dr, loaded by its first wave; rows
+      // past the chunk's last repeat it, so no load leaves the block
       const uint32_t loff = 4u * (uint32_t)min(rb + lane, last);
       const uint32_t lds_l = lds_addr(st + 2 * QT) + 4 * rb;
-      if (lane < 32) {
+      if (kslot == 0 && lane < 32) {
         dma4(a.lse2 + cl, loff, lds_l);
         dma4(a.dr + cl, loff, lds_l + 4 * QC);
       }
@@ -380,9 +390,8 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       int later = 0;
 #pragma unroll
       for (int k = 1; k < NST - 1; ++k) later += rem_of((s1 + k) % NST) != 0;
-      if (NST >= 4 && later >= 2) wait_vm<(NST >= 4 ? 2 : 0) * LPC>();
-      else if (NST >= 3 && later >= 1) wait_vm<(NST >= 3 ? 1 : 0) * LPC>();
-      else wait_vm<0>();
+      if (kslot == 0) wait_later<NST, LPC>(later);
+      else wait_later<NST, LPC_ROWS>(later);
     };
     auto next = [&](int s) { return s == NST - 1 ? 0 : s + 1; };
 
