@@ -75,8 +75,35 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
   const RowOffs ro(lane);
   const TrOffs to(lane);
 
+  // All-zero query rows (video callers zero the padded slots of partial
+  // tiles). Rows of one Q block with equal query values (here: all zero, of
+  // either sign) go through identical arithmetic over the same block list, so
+  // they get identical outputs. The lowest wave whose 32 rows are all zero
+  // runs the general path; the work-group's other all-zero waves skip the
+  // chunk arithmetic and copy its accumulators, row sum and exp offset at the
+  // end.
+  __shared__ int zflag[NW];
+  __shared__ float zacc[HD + 2];
+  uint32_t nzq = 0;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) nzq |= (qr[ks].x | qr[ks].y | qr[ks].z | qr[ks].w) & 0x7fff7fffu;
+  const bool zwave = __ballot(nzq != 0) == 0ull;
+  if (lane == 0) zflag[wave] = zwave;
+  __syncthreads();
+  int zfirst = NW, nzw = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int f = zflag[w];
+    if (f && zfirst == NW) zfirst = w;
+    nzw += f;
+  }
+  zfirst = __builtin_amdgcn_readfirstlane(zfirst);
+  const bool zshare = __builtin_amdgcn_readfirstlane(nzw) > 1;  // uniform over the work-group
+  const bool zlead = zwave && wave == zfirst, zskip = zwave && wave != zfirst;
+
   walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, cnt, a.k, a.v, wave, lane,
                    [&](const uint8_t* Ks, const uint8_t* Vs, int rem) {
+    if (zskip) return;
     // ---- S^T = K Q^T (2 x 32 keys by 32 rows) ----
     f32x16_t s0, s1;
 #pragma unroll
@@ -138,7 +165,28 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
     }
   });
 
-  const float l_run = xhalf_sum(l_a + l_b);
+  float l_run = xhalf_sum(l_a + l_b);
+  if (zshare) {  // every row of the leading all-zero wave holds the shared result
+    if (zlead && l32 == 0) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zacc[32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3)] = acc[mb][r];
+      if (hl == 0) {
+        zacc[HD] = l_run;
+        zacc[HD + 1] = msc;
+      }
+    }
+    __syncthreads();
+    if (zskip) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][r] = zacc[32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3)];
+      l_run = zacc[HD];
+      msc = zacc[HD + 1];
+    }
+  }
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   if (!row_ok) return;
   if (hl == 0)  // natural-log LSE: (offset + log2 l) * ln 2

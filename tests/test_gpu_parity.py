@@ -180,6 +180,28 @@ def _as_bshd(case):
     return b
 
 
+def test_zero_query_rows_of_a_block_share_one_output():
+    """Padded slots of partial video tiles hold zero queries. Such rows go
+    through identical arithmetic, so every one of them in a block has the same
+    output and LSE, whether its wave computed it or copied it from the block's
+    leading all-zero wave (the 61-valid tile: rows 61-63 are computed in a
+    wave with live rows, rows 64-255 by one wave and copied to five). The
+    oracle comparison of the same case is in test_fwd_bwd_parity_small."""
+    for layout in ("bhsd", "bshd"):
+        case = make_case("p1_partial_q", layout=layout)
+        res = run_case(case, backward=False)
+        out = res["out"] if layout == "bhsd" else res["out"].transpose(0, 2, 1, 3)
+        lse = res["lse"]
+        for i, qv in enumerate(case.q_var.tolist()):
+            if qv == 256:
+                continue
+            rows = slice(i * 256 + qv, (i + 1) * 256)
+            o, l = out[:, :, rows], lse[:, :, rows]
+            assert np.array_equal(o, np.broadcast_to(o[:, :, :1], o.shape)), (layout, i)
+            assert np.array_equal(l, np.broadcast_to(l[:, :, :1], l.shape)), (layout, i)
+            assert np.isfinite(l).all()
+
+
 def test_bhsd_and_bshd_are_bit_identical():
     a = make_case("p1_gated", layout="bhsd")
     b = _as_bshd(a)
