@@ -47,6 +47,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
   const int tid = threadIdx.x, slot = tid >> 4, dg = tid & 15;
   const long long qrs = g.q_rs(), qb = g.q_base(b, h);
   const bool gated = a.gate_mode != VSA_GATE_NONE;
+  // 32-row groups of the block with a row whose q or dO is not zero
+  __shared__ uint32_t live_groups;
+  if (tid == 0) live_groups = 0;
+  __syncthreads();
+  uint32_t lg = 0;
   float gacc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) gacc[u] = 0.f;
@@ -60,6 +65,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
     const long long off = qb + (long long)(blk0 + s) * qrs + 8 * dg;
     const uint4 dv = ldg16(a.dout + off);
     const uint4 ov = ldg16(a.osel + off);
+    const uint4 qv = ldg16(a.q + off);
+    // a row is live when one of its 16 lanes sees a non-zero q or dO element
+    // (either sign of zero counts as zero); the wave holds rows 4w .. 4w+3
+    const uint32_t nz = (dv.x | dv.y | dv.z | dv.w | qv.x | qv.y | qv.z | qv.w) & 0x7fff7fffu;
+    const unsigned long long live = __ballot(nz != 0);
+    if ((live >> (16 * (slot & 3))) & 0xffffull) lg |= (s >> 5) < 32 ? 1u << (s >> 5) : 0u;
     const uint32_t* dw = reinterpret_cast<const uint32_t*>(&dv);
     const uint32_t* ow = reinterpret_cast<const uint32_t*>(&ov);
     float dof[8], of[8];
@@ -108,6 +119,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
         if (a.dgate) stg16(a.dgate + off, make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]));
       }
     }
+  }
+  if (dg == 0 && lg) atomicOr(&live_groups, lg);
+  __syncthreads();
+  if (tid == 0) {
+    const int ng = (g.q_block + 31) / 32;
+    const uint32_t all = ng >= 32 ? 0xffffffffu : (1u << ng) - 1u;
+    a.qskip[((long long)b * g.Hq + h) * g.Qb + i] = ng > 32 ? 0u : all & ~live_groups;
   }
   if (!gated) return;
 #pragma unroll
@@ -181,7 +199,7 @@ struct DkdvLds {
   static constexpr int KT = (S::NST * S::STAGE + 1023) / 1024 * 1024;
   static constexpr int VX = KT + S::KW * HD * 2;
   static constexpr int LST = VX + (8 - DKDV_VREG) * S::KW * 2 * 16;
-  static constexpr int BYTES = LST + DKDV_LIST_CAP * 4;
+  static constexpr int BYTES = LST + 2 * DKDV_LIST_CAP * 4;  // Q blocks | their zero-row groups
 };
 constexpr int imax(int x, int y) { return x > y ? x : y; }
 constexpr int DKDV_LDS = imax(DkdvLds<8>::BYTES, imax(DkdvLds<4>::BYTES, DkdvLds<2>::BYTES));
@@ -200,6 +218,7 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
   uint8_t* const Kt = smem + L::KT;
   uint4* const Vx = reinterpret_cast<uint4*>(smem + L::VX);
   int* const lst_i = reinterpret_cast<int*>(smem + L::LST);
+  int* const lst_m = lst_i + DKDV_LIST_CAP;
 
   const Geom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -246,6 +265,15 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
     // A chunk's loads need only two running offsets (of its row 0 in q / dout
     // and in lse2 / dr), so a fill is a few scalar adds and the direct loads.
     int hh = 0, e0 = 0, cnt = 0, page = 0;  // current head's CSR row and list page
+    // a list page: the Q blocks and, per block, its 32-row groups of zero rows
+    auto load_list = [&](int hx, int base) {
+      const long long qb0 = ((long long)b * g.Hq + hk * g.group + hx) * g.Qb;
+      for (int t = tid; t < DKDV_LIST_CAP && base + t < cnt; t += NW * 64) {
+        const int si = a.col[e0 + base + t];
+        lst_i[t] = si;
+        lst_m[t] = (int)a.qskip[qb0 + si];
+      }
+    };
     auto load_head = [&](int hx) {  // first list page of head hx (all waves; drains loads)
       const long long r = ((long long)b * g.Hq + hk * g.group + hx) * g.KVb + j;
       // uniform, and kept scalar: everything the fills derive from them stays scalar
@@ -253,12 +281,14 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       cnt = __builtin_amdgcn_readfirstlane(a.row_ptr[r + 1]) - e0;
       page = 0;
       __syncthreads();
-      for (int t = tid; t < DKDV_LIST_CAP && t < cnt; t += NW * 64) lst_i[t] = a.col[e0 + t];
+      load_list(hx, 0);
       __syncthreads();
     };
     // stager: list entry se, rows of its Q block from the next chunk on, and
-    // the element offsets of the next chunk's row 0 in q / dout and in lse2 / dr
-    int se = 0, left = 0;
+    // the element offsets of the next chunk's row 0 in q / dout and in lse2 / dr;
+    // crow: that row inside the block, zm: the block's zero-row groups
+    int se = 0, left = 0, crow = 0;
+    uint32_t zm = 0;
     long long cq = 0, cl = 0;
     bool more = true;
     auto settle = [&]() {  // from entry se of head hh, find the next entry (skipping empty heads)
@@ -273,10 +303,12 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       if (se - page >= DKDV_LIST_CAP) {  // next page (only for lists longer than the cap)
         __syncthreads();
         page = se;
-        for (int t = tid; t < DKDV_LIST_CAP && page + t < cnt; t += NW * 64) lst_i[t] = a.col[e0 + page + t];
+        load_list(hh, page);
         __syncthreads();
       }
       const int si = __builtin_amdgcn_readfirstlane(lst_i[se - page]);
+      zm = (uint32_t)__builtin_amdgcn_readfirstlane(lst_m[se - page]);
+      crow = 0;
       left = max(0, min(g.q_block, qlen - si * g.q_block));  // >= 1 for a listed Q block
       const int h = hk * g.group + hh;
       const long long r0 = (long long)si * g.q_block;
@@ -286,12 +318,33 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
     load_head(0);
     settle();
 
-    // per slot, 8 bits of `slots`: valid rows of its chunk (1 .. QC), 0 if empty
-    uint32_t slots = 0;
+    // per slot, 8 bits of `slots`: valid rows of its chunk (1 .. QC), 0 if empty;
+    // 4 bits of `zsl`: its row groups of zero rows
+    uint32_t slots = 0, zsl = 0;
     const long long qstep = (long long)QC * qrs;
+    auto advance = [&]() {
+      left -= QC;
+      if (left > 0) {
+        cq += qstep;
+        cl += QC;
+        crow += QC;
+      } else {
+        ++se;
+        settle();
+      }
+    };
+    constexpr uint32_t RGM = (1u << RG) - 1u;
+    // Rows with q = 0 and dO = 0 (the padded slots of partial video tiles,
+    // where callers pass a zero gradient) have dS = 0 and add exactly nothing
+    // to dK and dV: a chunk made only of them is neither loaded nor computed,
+    // and a row group made only of them is not computed.
+    auto zero_groups = [&]() { return (crow >> 5) < 32 ? (zm >> (crow >> 5)) & RGM : 0u; };
     auto fill = [&](int s) {
       slots &= ~(0xFFu << (8 * s));
+      zsl &= ~(0xFu << (4 * s));
+      while (more && zero_groups() == RGM) advance();
       if (!more) return;
+      zsl |= zero_groups() << (4 * s);
       const int last = min(left, QC) - 1;  // rows past it repeat it
       slots |= (uint32_t)(last + 1) << (8 * s);
       uint8_t* st = ring + s * STAGE;
@@ -305,14 +358,7 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
         dma4(a.lse2 + cl, loff, lds_l);
         dma4(a.dr + cl, loff, lds_l + 4 * QC);
       }
-      left -= QC;
-      if (left > 0) {
-        cq += qstep;
-        cl += QC;
-      } else {
-        ++se;
-        settle();
-      }
+      advance();
     };
     auto rem_of = [&](int s) { return (int)((slots >> (8 * s)) & 0xFFu); };
 
@@ -403,7 +449,7 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       for (int s = 0;;) {
         fill(s == 0 ? NST - 1 : s - 1);  // the slot freed by the previous step
         const int rows = rem_of(s);
-        if (busy(rows)) compute(ring + s * STAGE, rows);
+        if (busy(rows) && !((zsl >> (4 * s + rg)) & 1u)) compute(ring + s * STAGE, rows);
         s = next(s);
         wait_chunk(s);
         lds_barrier();
@@ -560,16 +606,26 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
   const int e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[rid]);  // uniform: the walk stays scalar
   const int cnt = __builtin_amdgcn_readfirstlane(a.row_ptr[rid + 1]) - e0;
 
-  // A wave whose query rows are all zero (the padded slots of partial video
-  // tiles) has S = 0 exactly for finite K: it skips the score MFMAs and runs
-  // the rest of the step on S = 0, which gives the same P and dS bit for bit.
+  // Rows with q = 0 and dO = 0 (the padded slots of partial video tiles, where
+  // callers pass a zero gradient) have dS = 0: a wave made only of them skips
+  // the walk's arithmetic (its dq rows are the compression term or zero), and
+  // a work-group made only of them skips the walk.
+  const uint32_t zmask = a.qskip[rid];
+  const int grp = sub * NW + wave;  // this wave's 32-row group of the block
+  const bool zrows = grp < 32 && ((zmask >> grp) & 1u);
+  const uint32_t wg_groups = sub * NW < 32 ? (zmask >> (sub * NW)) & ((1u << NW) - 1u) : 0u;
+  const int walk_cnt = wg_groups == (1u << NW) - 1u ? 0 : cnt;
+  // A wave whose query rows are all zero has S = 0 exactly for finite K: it
+  // skips the score MFMAs and runs the rest of the step on S = 0, which gives
+  // the same P and dS bit for bit.
   uint32_t nzq = 0;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) nzq |= (qr[ks].x | qr[ks].y | qr[ks].z | qr[ks].w) & 0x7fff7fffu;
   const bool zq = __ballot(nzq != 0) == 0ull;
 
-  walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, cnt, a.k, a.v, wave, lane,
+  walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, walk_cnt, a.k, a.v, wave, lane,
                    [&](const uint8_t* Ks, const uint8_t* Vs, int rem) {
+    if (zrows) return;
     // per half of 32 keys: S^T = K Q^T, dP^T = V dO^T, dS = P * (dP - D), then
     // dQ^T += K^T dS^T over its two key steps of 16
 #pragma unroll

@@ -30,6 +30,10 @@ struct BwdArgs {
   const uint16_t* dout;
   const float* lse2;       // lse * log2(e), +inf for rows without a live key
   const float* dr;         // rowsum(dO * O_sel), laid out like lse
+  // per Q block [B,Hq,Qb]: bit g set when every existing row of the block's
+  // rows 32g .. 32g+31 has q = 0 and dO = 0 (such rows add nothing to dK / dV
+  // and have dS = 0); 0 for blocks of more than 1024 rows
+  const uint32_t* qskip;
   const int32_t* row_ptr;  // Q-owned (dQ) or KV-owned (dK/dV) CSR
   const int32_t* col;
   const float* dqc;  // gate: pooled-tile gradients added to valid slots, else null
@@ -43,6 +47,7 @@ struct BwdArgs {
 // Row term and gate-side reductions of the backward.
 struct PreArgs {
   Geom g;
+  const uint16_t* q;
   const uint16_t* dout;
   const uint16_t* osel;  // sparse-branch output
   const uint16_t* gate;
@@ -53,6 +58,7 @@ struct PreArgs {
   float* lse2;
   float* doc;       // gate: [B,Hq,Qb,HD] sum over the tile of gate * dO
   uint16_t* dgate;  // gate: optional
+  uint32_t* qskip;  // [B,Hq,Qb] zero-row groups (see BwdArgs)
 };
 
 // Pooled tiles, coarse scores, top-k and coarse attention.

@@ -202,6 +202,26 @@ def test_zero_query_rows_of_a_block_share_one_output():
             assert np.isfinite(l).all()
 
 
+def test_rows_with_zero_query_and_zero_gradient_are_skipped_exactly():
+    """Partial query tiles whose padded slots hold zero q and zero dO (a
+    training caller passes no gradient for padded outputs): those rows have
+    dS = 0, so the backward skips whole row chunks and single row groups of
+    them. The tiles' valid counts (61, 199) and the KV tiles' live keys (256,
+    100, 64) make every dK/dV span shape meet a chunk of only zero rows, one of
+    mixed row groups and one of live rows; results must still match the oracle,
+    with dq exactly zero on the padded rows."""
+    for dtype, layout in (("bf16", "bshd"), ("fp16", "bhsd")):
+        case = build_case(f"zero_rows_{dtype}_{layout}", dtype=dtype, layout=layout, B=1, Hq=2,
+                          Hkv=1, D=128, q_var=[61, 256, 199], kv_var=[256, 100, 64, 256],
+                          map_kind="ones", seed=23)
+        _say(f"[{case.name}]")
+        res = run_case(case)
+        _compare_case(case, res, oracle.Oracle(case, np.float32))
+        dq = res["dq"] if layout == "bhsd" else res["dq"].transpose(0, 2, 1, 3)
+        for i, qv in enumerate(case.q_var.tolist()):
+            assert np.all(dq[:, :, i * 256 + qv:(i + 1) * 256] == 0), (case.name, i)
+
+
 def test_bhsd_and_bshd_are_bit_identical():
     a = make_case("p1_gated", layout="bhsd")
     b = _as_bshd(a)
