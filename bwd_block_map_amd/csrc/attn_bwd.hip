@@ -615,13 +615,6 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
   const bool zrows = grp < 32 && ((zmask >> grp) & 1u);
   const uint32_t wg_groups = sub * NW < 32 ? (zmask >> (sub * NW)) & ((1u << NW) - 1u) : 0u;
   const int walk_cnt = wg_groups == (1u << NW) - 1u ? 0 : cnt;
-  // A wave whose query rows are all zero has S = 0 exactly for finite K: it
-  // skips the score MFMAs and runs the rest of the step on S = 0, which gives
-  // the same P and dS bit for bit.
-  uint32_t nzq = 0;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) nzq |= (qr[ks].x | qr[ks].y | qr[ks].z | qr[ks].w) & 0x7fff7fffu;
-  const bool zq = __ballot(nzq != 0) == 0ull;
 
   walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, walk_cnt, a.k, a.v, wave, lane,
                    [&](const uint8_t* Ks, const uint8_t* Vs, int rem) {
@@ -633,15 +626,10 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
       f32x16_t sv, pv;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = pv[r] = 0.f;
-      if (zq) {  // all-zero query rows: S = 0
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          sv = E::mfma(ro.at(Ks, 32 * hf, ks), qr[ks], sv);
-          pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
-        }
+      for (int ks = 0; ks < 8; ++ks) {
+        sv = E::mfma(ro.at(Ks, 32 * hf, ks), qr[ks], sv);
+        pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
       }
       // lane holds keys 32hf + 8(r/4) + 4hl + (r%4) of its row; keys past the
       // valid ones get P = 0 through a -inf exponent
