@@ -28,8 +28,10 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]
-# Per-source register form of the MFMA accumulators: the forward and dQ keep
-# them in VGPRs; dK/dV keeps its large accumulator set in AGPRs.
+# Per-source register form of the MFMA accumulators: the forward is built with
+# them forced into VGPRs; the backward keeps the compiler's default, which also
+# puts them in VGPRs at two waves per SIMD (forcing the form there made no
+# measurable difference).
 EXTRA = {
     "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "attn_bwd.hip": [],
