@@ -209,7 +209,9 @@ int vsa_fwd(const vsa_problem* p, const void* q, const void* k, const void* v,
  * KV-owned index without atomics, dK / dV summed over the Q heads of each KV
  * head. With a gate, the compression branch adds its pooled gradients (valid
  * slots only) and dgate (optional) receives dL/dgate. No gradient flows
- * through the top-k choice.
+ * through the top-k choice. Rows whose q and dout are both zero (the padded
+ * slots of video tiles in training) have dS = 0 and are skipped; for finite
+ * inputs the results are those of the full computation.
  *   q, k, v, gate  the forward's inputs
  *   dout        q-shaped upstream gradient; NULL means zeros
  *   out         the forward's output (read only when gate_mode == NONE; with a
