@@ -281,6 +281,8 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
 // Coarse backward, row form: P_c, dS_c for CR2 rows (kept in workspace for the
 // column pass) and dQ_c = scale dS_c K_c. For dQ_c the pooled K rows stream
 // through an LDS tile with all loads of a tile in flight.
+// 8 rows per work-group: with 4, two work-groups share a CU at 1440 KV tiles,
+// but twice as many row blocks then stream every pooled K/V row (6 % slower)
 constexpr int CR2 = 8;
 constexpr int CT2 = 32;                  // pooled K rows per staging tile
 constexpr int TILE2_FLOATS = CT2 * HD;
@@ -352,8 +354,11 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a
     }
   }
   // dQ_c[r][d] = scale sum_j dS_c[r][j] K_c[j][d], CT2 pooled K rows at a time (tile[j][d])
+  constexpr int RH = CR2 / 2;  // rows per half of the work-group
   const int d = tid & (HD - 1), half = tid >> 7;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[RH];
+#pragma unroll
+  for (int u = 0; u < RH; ++u) acc[u] = 0.f;
   constexpr int KLOADS = CT2 * HD / 4 / 256;
   for (int j0 = 0; j0 < KVb; j0 += CT2) {
     __syncthreads();  // dS is final / the previous tile is consumed
@@ -371,12 +376,12 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a
     for (int jt = 0; jt < nj; ++jt) {
       const float kv = tile[jt * HD + d];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = __builtin_fmaf(dS[(half * 4 + u) * KVb + j0 + jt], kv, acc[u]);
+      for (int u = 0; u < RH; ++u) acc[u] = __builtin_fmaf(dS[(half * RH + u) * KVb + j0 + jt], kv, acc[u]);
     }
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int rr = half * 4 + u;
+  for (int u = 0; u < RH; ++u) {
+    const int rr = half * RH + u;
     if (rr < nr) a.dqc[g.pq(b, h, i0 + rr) + d] = g.scale * acc[u];
   }
 }
@@ -465,11 +470,16 @@ size_t coarse_bwd_lds(int KVb) {
 }
 
 int coarse_rows_per_block(int KVb) {
-  // scores [CR][KVb] + qc [CR][HD] + 4 histograms + the staging tile must fit in 160 KiB
-  const long long budget = 160 * 1024 - 4 * 256 * 4 - TILE_FLOATS * 4;
+  // scores [CR][KVb] + qc [CR][HD] + 4 histograms + the staging tile. Prefer
+  // the largest CR with which two work-groups share a CU's 160 KiB (a single
+  // four-wave work-group leaves each SIMD one wave to hide LDS latency with),
+  // else the largest that fits at all.
+  auto need = [&](int cr) { return ((long long)cr * (KVb + HD) + 4 * 256 + TILE_FLOATS) * 4; };
+  for (int cr = 16; cr >= 1; cr >>= 1)
+    if (need(cr) <= 80 * 1024) return cr;
   int cr = 16;
-  while (cr > 1 && (long long)cr * (KVb + HD) * 4 > budget) cr >>= 1;
-  return cr;
+  while (cr > 1 && need(cr) > 160 * 1024) cr >>= 1;
+  return need(cr) <= 160 * 1024 ? cr : 0;  // 0: KVb too large for these kernels
 }
 
 hipError_t launch_pool(const Geom& g, int dtype, const void* q, const void* k, const void* v,
