@@ -47,11 +47,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
   const int tid = threadIdx.x, slot = tid >> 4, dg = tid & 15;
   const long long qrs = g.q_rs(), qb = g.q_base(b, h);
   const bool gated = a.gate_mode != VSA_GATE_NONE;
-  // 32-row groups of the block with a row whose q or dO is not zero
-  __shared__ uint32_t live_groups;
-  if (tid == 0) live_groups = 0;
+  // live extent: 1 + the last row whose q or dO has a non-zero element
+  __shared__ int live_end;
+  if (tid == 0) live_end = 0;
   __syncthreads();
-  uint32_t lg = 0;
+  int lend = 0;
   float gacc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) gacc[u] = 0.f;
@@ -66,11 +66,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
     const uint4 dv = ldg16(a.dout + off);
     const uint4 ov = ldg16(a.osel + off);
     const uint4 qv = ldg16(a.q + off);
-    // a row is live when one of its 16 lanes sees a non-zero q or dO element
-    // (either sign of zero counts as zero); the wave holds rows 4w .. 4w+3
+    // the row is live when one of its 16 lanes sees a non-zero element (either
+    // sign of zero counts as zero); the wave holds rows 4w .. 4w+3
     const uint32_t nz = (dv.x | dv.y | dv.z | dv.w | qv.x | qv.y | qv.z | qv.w) & 0x7fff7fffu;
-    const unsigned long long live = __ballot(nz != 0);
-    if ((live >> (16 * (slot & 3))) & 0xffffull) lg |= (s >> 5) < 32 ? 1u << (s >> 5) : 0u;
+    if ((__ballot(nz != 0) >> (16 * (slot & 3))) & 0xffffull) lend = s + 1;
     const uint32_t* dw = reinterpret_cast<const uint32_t*>(&dv);
     const uint32_t* ow = reinterpret_cast<const uint32_t*>(&ov);
     float dof[8], of[8];
@@ -120,13 +119,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
       }
     }
   }
-  if (dg == 0 && lg) atomicOr(&live_groups, lg);
+  if (dg == 0 && lend) atomicMax(&live_end, lend);
   __syncthreads();
-  if (tid == 0) {
-    const int ng = (g.q_block + 31) / 32;
-    const uint32_t all = ng >= 32 ? 0xffffffffu : (1u << ng) - 1u;
-    a.qskip[((long long)b * g.Hq + h) * g.Qb + i] = ng > 32 ? 0u : all & ~live_groups;
-  }
+  if (tid == 0) a.qlive[((long long)b * g.Hq + h) * g.Qb + i] = live_end;
   if (!gated) return;
 #pragma unroll
   for (int u = 0; u < 8; ++u) red[slot][8 * dg + u] = gacc[u];
@@ -199,7 +194,7 @@ struct DkdvLds {
   static constexpr int KT = (S::NST * S::STAGE + 1023) / 1024 * 1024;
   static constexpr int VX = KT + S::KW * HD * 2;
   static constexpr int LST = VX + (8 - DKDV_VREG) * S::KW * 2 * 16;
-  static constexpr int BYTES = LST + 2 * DKDV_LIST_CAP * 4;  // Q blocks | their zero-row groups
+  static constexpr int BYTES = LST + 2 * DKDV_LIST_CAP * 4;  // Q blocks | their live extents
 };
 constexpr int imax(int x, int y) { return x > y ? x : y; }
 constexpr int DKDV_LDS = imax(DkdvLds<8>::BYTES, imax(DkdvLds<4>::BYTES, DkdvLds<2>::BYTES));
@@ -218,7 +213,7 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
   uint8_t* const Kt = smem + L::KT;
   uint4* const Vx = reinterpret_cast<uint4*>(smem + L::VX);
   int* const lst_i = reinterpret_cast<int*>(smem + L::LST);
-  int* const lst_m = lst_i + DKDV_LIST_CAP;
+  int* const lst_e = lst_i + DKDV_LIST_CAP;
 
   const Geom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -259,19 +254,18 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
     const RowOffs ro(lane);
     const TrOffs to(lane);
     const int rb = 32 * rg;  // this wave's rows inside a chunk
-    const int qlen = g.q_len(b);
 
     // ---- the list walker: heads of the group, their KV-owned entries, row chunks ----
     // A chunk's loads need only two running offsets (of its row 0 in q / dout
     // and in lse2 / dr), so a fill is a few scalar adds and the direct loads.
     int hh = 0, e0 = 0, cnt = 0, page = 0;  // current head's CSR row and list page
-    // a list page: the Q blocks and, per block, its 32-row groups of zero rows
+    // a list page: the Q blocks and their live extents
     auto load_list = [&](int hx, int base) {
       const long long qb0 = ((long long)b * g.Hq + hk * g.group + hx) * g.Qb;
       for (int t = tid; t < DKDV_LIST_CAP && base + t < cnt; t += NW * 64) {
         const int si = a.col[e0 + base + t];
         lst_i[t] = si;
-        lst_m[t] = (int)a.qskip[qb0 + si];
+        lst_e[t] = a.qlive[qb0 + si];
       }
     };
     auto load_head = [&](int hx) {  // first list page of head hx (all waves; drains loads)
@@ -285,31 +279,36 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       __syncthreads();
     };
     // stager: list entry se, rows of its Q block from the next chunk on, and
-    // the element offsets of the next chunk's row 0 in q / dout and in lse2 / dr;
-    // crow: that row inside the block, zm: the block's zero-row groups
-    int se = 0, left = 0, crow = 0;
-    uint32_t zm = 0;
+    // the element offsets of the next chunk's row 0 in q / dout and in lse2 / dr
+    int se = 0, left = 0;
     long long cq = 0, cl = 0;
     bool more = true;
-    auto settle = [&]() {  // from entry se of head hh, find the next entry (skipping empty heads)
-      while (se >= cnt) {
-        if (++hh >= g.group) {
-          more = false;
-          return;
+    // Rows past a block's live extent have q = 0 and dO = 0 (the padded slots
+    // of partial video tiles, where callers pass a zero gradient): their dS is
+    // 0 and they add exactly nothing to dK and dV, so the walk stops there and
+    // passes over blocks without a live row.
+    auto settle = [&]() {  // from entry se of head hh, find the next entry with live rows
+      for (;;) {
+        while (se >= cnt) {
+          if (++hh >= g.group) {
+            more = false;
+            return;
+          }
+          load_head(hh);
+          se = 0;
         }
-        load_head(hh);
-        se = 0;
-      }
-      if (se - page >= DKDV_LIST_CAP) {  // next page (only for lists longer than the cap)
-        __syncthreads();
-        page = se;
-        load_list(hh, page);
-        __syncthreads();
+        if (se - page >= DKDV_LIST_CAP) {  // next page (only for lists longer than the cap)
+          __syncthreads();
+          page = se;
+          load_list(hh, page);
+          __syncthreads();
+        }
+        left = min(__builtin_amdgcn_readfirstlane(lst_e[se - page]),
+                   g.q_block);  // live rows, never more than exist
+        if (left > 0) break;
+        ++se;
       }
       const int si = __builtin_amdgcn_readfirstlane(lst_i[se - page]);
-      zm = (uint32_t)__builtin_amdgcn_readfirstlane(lst_m[se - page]);
-      crow = 0;
-      left = max(0, min(g.q_block, qlen - si * g.q_block));  // >= 1 for a listed Q block
       const int h = hk * g.group + hh;
       const long long r0 = (long long)si * g.q_block;
       cq = uniform_i64(g.q_base(b, h) + r0 * qrs);
@@ -318,33 +317,12 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
     load_head(0);
     settle();
 
-    // per slot, 8 bits of `slots`: valid rows of its chunk (1 .. QC), 0 if empty;
-    // 4 bits of `zsl`: its row groups of zero rows
-    uint32_t slots = 0, zsl = 0;
+    // per slot, 8 bits of `slots`: valid rows of its chunk (1 .. QC), 0 if empty
+    uint32_t slots = 0;
     const long long qstep = (long long)QC * qrs;
-    auto advance = [&]() {
-      left -= QC;
-      if (left > 0) {
-        cq += qstep;
-        cl += QC;
-        crow += QC;
-      } else {
-        ++se;
-        settle();
-      }
-    };
-    constexpr uint32_t RGM = (1u << RG) - 1u;
-    // Rows with q = 0 and dO = 0 (the padded slots of partial video tiles,
-    // where callers pass a zero gradient) have dS = 0 and add exactly nothing
-    // to dK and dV: a chunk made only of them is neither loaded nor computed,
-    // and a row group made only of them is not computed.
-    auto zero_groups = [&]() { return (crow >> 5) < 32 ? (zm >> (crow >> 5)) & RGM : 0u; };
     auto fill = [&](int s) {
       slots &= ~(0xFFu << (8 * s));
-      zsl &= ~(0xFu << (4 * s));
-      while (more && zero_groups() == RGM) advance();
       if (!more) return;
-      zsl |= zero_groups() << (4 * s);
       const int last = min(left, QC) - 1;  // rows past it repeat it
       slots |= (uint32_t)(last + 1) << (8 * s);
       uint8_t* st = ring + s * STAGE;
@@ -358,7 +336,14 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
         dma4(a.lse2 + cl, loff, lds_l);
         dma4(a.dr + cl, loff, lds_l + 4 * QC);
       }
-      advance();
+      left -= QC;
+      if (left > 0) {
+        cq += qstep;
+        cl += QC;
+      } else {
+        ++se;
+        settle();
+      }
     };
     auto rem_of = [&](int s) { return (int)((slots >> (8 * s)) & 0xFFu); };
 
@@ -449,7 +434,7 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       for (int s = 0;;) {
         fill(s == 0 ? NST - 1 : s - 1);  // the slot freed by the previous step
         const int rows = rem_of(s);
-        if (busy(rows) && !((zsl >> (4 * s + rg)) & 1u)) compute(ring + s * STAGE, rows);
+        if (busy(rows)) compute(ring + s * STAGE, rows);
         s = next(s);
         wait_chunk(s);
         lds_barrier();
@@ -606,19 +591,25 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
   const int e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[rid]);  // uniform: the walk stays scalar
   const int cnt = __builtin_amdgcn_readfirstlane(a.row_ptr[rid + 1]) - e0;
 
-  // Rows with q = 0 and dO = 0 (the padded slots of partial video tiles, where
-  // callers pass a zero gradient) have dS = 0: a wave made only of them skips
-  // the walk's arithmetic (its dq rows are the compression term or zero), and
-  // a work-group made only of them skips the walk.
-  const uint32_t zmask = a.qskip[rid];
-  const int grp = sub * NW + wave;  // this wave's 32-row group of the block
-  const bool zrows = grp < 32 && ((zmask >> grp) & 1u);
-  const uint32_t wg_groups = sub * NW < 32 ? (zmask >> (sub * NW)) & ((1u << NW) - 1u) : 0u;
-  const int walk_cnt = wg_groups == (1u << NW) - 1u ? 0 : cnt;
+  // A wave whose query rows are all zero (the padded slots of partial video
+  // tiles) has S = 0 exactly for finite K: it skips the score MFMAs and runs
+  // the rest of the step on S = 0, which gives the same P and dS bit for bit.
+  uint32_t nzq = 0;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) nzq |= (qr[ks].x | qr[ks].y | qr[ks].z | qr[ks].w) & 0x7fff7fffu;
+  const bool zq = __ballot(nzq != 0) == 0ull;
+
+  // Rows past the block's live extent have q = 0 and dO = 0 (the padded slots
+  // of partial video tiles, where callers pass a zero gradient), so dS = 0: a
+  // wave made only of them skips the walk's arithmetic (its dq rows are the
+  // compression term or zero), and a work-group made only of them skips the walk.
+  const int qlive = a.qlive[rid];
+  const bool dead = sub * 32 * NW + wave * 32 >= qlive;
+  const int walk_cnt = sub * 32 * NW >= qlive ? 0 : cnt;
 
   walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, walk_cnt, a.k, a.v, wave, lane,
                    [&](const uint8_t* Ks, const uint8_t* Vs, int rem) {
-    if (zrows) return;
+    if (dead) return;
     // per half of 32 keys: S^T = K Q^T, dP^T = V dO^T, dS = P * (dP - D), then
     // dQ^T += K^T dS^T over its two key steps of 16
 #pragma unroll
@@ -626,10 +617,15 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
       f32x16_t sv, pv;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = pv[r] = 0.f;
+      if (zq) {  // all-zero query rows: S = 0
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        sv = E::mfma(ro.at(Ks, 32 * hf, ks), qr[ks], sv);
-        pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
+        for (int ks = 0; ks < 8; ++ks) pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          sv = E::mfma(ro.at(Ks, 32 * hf, ks), qr[ks], sv);
+          pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
+        }
       }
       // lane holds keys 32hf + 8(r/4) + 4hl + (r%4) of its row; keys past the
       // valid ones get P = 0 through a -inf exponent

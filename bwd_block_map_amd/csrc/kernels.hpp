@@ -30,10 +30,9 @@ struct BwdArgs {
   const uint16_t* dout;
   const float* lse2;       // lse * log2(e), +inf for rows without a live key
   const float* dr;         // rowsum(dO * O_sel), laid out like lse
-  // per Q block [B,Hq,Qb]: bit g set when every existing row of the block's
-  // rows 32g .. 32g+31 has q = 0 and dO = 0 (such rows add nothing to dK / dV
-  // and have dS = 0); 0 for blocks of more than 1024 rows
-  const uint32_t* qskip;
+  // per Q block [B,Hq,Qb]: 1 + its last row whose q or dO is not zero (the
+  // rows after it add nothing to dK / dV and have dS = 0)
+  const int32_t* qlive;
   const int32_t* row_ptr;  // Q-owned (dQ) or KV-owned (dK/dV) CSR
   const int32_t* col;
   const float* dqc;  // gate: pooled-tile gradients added to valid slots, else null
@@ -58,7 +57,7 @@ struct PreArgs {
   float* lse2;
   float* doc;       // gate: [B,Hq,Qb,HD] sum over the tile of gate * dO
   uint16_t* dgate;  // gate: optional
-  uint32_t* qskip;  // [B,Hq,Qb] zero-row groups (see BwdArgs)
+  int32_t* qlive;  // [B,Hq,Qb] live extents (see BwdArgs)
 };
 
 // Pooled tiles, coarse scores, top-k and coarse attention.

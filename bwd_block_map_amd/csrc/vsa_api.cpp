@@ -180,7 +180,7 @@ FwdWs carve_fwd(const vsa_problem* p, void* base, size_t* bytes) {
 struct BwdWs {
   float* dr;
   float* lse2;
-  uint32_t* qskip;
+  int32_t* qlive;
   float* doc;
   float* dqc;
   float* dkc;
@@ -194,7 +194,7 @@ BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
   BwdWs w{};
   w.dr = c.take<float>(std::max(rows_total(p), 1LL));
   w.lse2 = c.take<float>(std::max(rows_total(p), 1LL));
-  w.qskip = c.take<uint32_t>(std::max((long long)p->B * p->Hq * p->Qb, 1LL));
+  w.qlive = c.take<int32_t>(std::max((long long)p->B * p->Hq * p->Qb, 1LL));
   if (p->gate_mode != VSA_GATE_NONE) {
     w.doc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
     w.dqc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
@@ -531,7 +531,7 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   pa.lse2 = w.lse2;
   pa.doc = w.doc;
   pa.dgate = (uint16_t*)dgate;
-  pa.qskip = w.qskip;
+  pa.qlive = w.qlive;
   {
     Prof pr(VSA_KERNEL_BWD_PRE, st);
     e = vsa::launch_bwd_pre(pa, p->dtype, st);
@@ -566,7 +566,7 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   ba.dout = (const uint16_t*)dout;
   ba.lse2 = w.lse2;
   ba.dr = w.dr;
-  ba.qskip = w.qskip;
+  ba.qlive = w.qlive;
   ba.dqc = gated ? w.dqc : nullptr;
   ba.dkc = gated ? w.dkc : nullptr;
   ba.dvc = gated ? w.dvc : nullptr;
