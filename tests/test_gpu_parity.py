@@ -205,14 +205,14 @@ def test_zero_query_rows_of_a_block_share_one_output():
 def test_rows_with_zero_query_and_zero_gradient_are_skipped_exactly():
     """Partial query tiles whose padded slots hold zero q and zero dO (a
     training caller passes no gradient for padded outputs): those rows have
-    dS = 0, so the backward skips whole row chunks and single row groups of
-    them. The tiles' valid counts (61, 199) and the KV tiles' live keys (256,
-    100, 64) make every dK/dV span shape meet a chunk of only zero rows, one of
-    mixed row groups and one of live rows; results must still match the oracle,
-    with dq exactly zero on the padded rows."""
+    dS = 0, so the backward stops each block's walk at its last live row and
+    skips dQ waves past it. The tiles' valid counts (61, 199) end in the middle
+    of a 32-, 64- and 128-row chunk of the three dK/dV span shapes (256, 100
+    and 64 live keys), and a tile without valid rows is passed over; results
+    must still match the oracle, with dq exactly zero on the padded rows."""
     for dtype, layout in (("bf16", "bshd"), ("fp16", "bhsd")):
         case = build_case(f"zero_rows_{dtype}_{layout}", dtype=dtype, layout=layout, B=1, Hq=2,
-                          Hkv=1, D=128, q_var=[61, 256, 199], kv_var=[256, 100, 64, 256],
+                          Hkv=1, D=128, q_var=[61, 256, 199, 0], kv_var=[256, 100, 64, 256],
                           map_kind="ones", seed=23)
         _say(f"[{case.name}]")
         res = run_case(case)
