@@ -357,6 +357,7 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       f32x16_t sv, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = dp[r] = 0.f;
+      __builtin_amdgcn_iglp_opt(0);  // MFMA / LDS-read interleaving, as in the forward (dK/dV 1 %)
       uint4 nq = ro.at(Qs, rb, 0), nk = ro.at(Kt, 32 * kslot, 0), nd = ro.at(Ds, rb, 0);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
@@ -610,6 +611,7 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
   walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, walk_cnt, a.k, a.v, wave, lane,
                    [&](const uint8_t* Ks, const uint8_t* Vs, int rem) {
     if (dead) return;
+    __builtin_amdgcn_iglp_opt(0);  // MFMA / LDS-read interleaving, as in the forward
     // per half of 32 keys: S^T = K Q^T, dP^T = V dO^T, dS = P * (dP - D), then
     // dQ^T += K^T dS^T over its two key steps of 16
 #pragma unroll

@@ -104,6 +104,9 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
   walk_kv<NW, NST>(g, b, h / g.group, a.col, e0, cnt, a.k, a.v, wave, lane,
                    [&](const uint8_t* Ks, const uint8_t* Vs, int rem) {
     if (zskip) return;
+    // LLVM's MFMA / LDS-read interleaving strategy 0 for the chunk body
+    // (measured: forward 3 % faster than the default schedule)
+    __builtin_amdgcn_iglp_opt(0);
     // ---- S^T = K Q^T (2 x 32 keys by 32 rows) ----
     f32x16_t s0, s1;
 #pragma unroll
