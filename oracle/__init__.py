@@ -20,6 +20,9 @@ import numpy as np
 _DIR = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_DIR, "oracle.cpp")
 _LIB_PATH = os.path.join(_DIR, "liboracle.so")
+# ORACLE_LIB names another build of oracle.cpp to load instead (the mutation
+# test points it at copies with a planted mistake); it is never rebuilt here.
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIB")
 _LIB = None
 
 _LAYOUT = {"bhsd": 0, "bshd": 1, "tnd": 2}
@@ -37,21 +40,23 @@ class OracleProblem(C.Structure):
     ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
     """Compile liboracle.so (plain g++, OpenMP, no target-specific flags so the
-    binary runs on any x86-64 host)."""
-    cmd = ["g++", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c++17", _SRC, "-o", _LIB_PATH + ".tmp"]
+    binary runs on any x86-64 host). src / out let a test build a copy."""
+    cmd = ["g++", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c++17", src, "-o", out + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + r.stderr)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    os.replace(out + ".tmp", out)
     if verbose:
         print(" ".join(cmd))
-    return _LIB_PATH
+    return out
 
 
 def lib():
     global _LIB
+    if _LIB is None and _LIB_OVERRIDE:
+        _LIB = C.CDLL(_LIB_OVERRIDE)
     if _LIB is None:
         if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
             build()

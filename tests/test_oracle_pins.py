@@ -15,6 +15,7 @@ a wrong sign or index, a transposed operand, a missing mask) fails it.
 
 from __future__ import annotations
 
+import dataclasses
 import json
 import math
 import os
@@ -22,9 +23,10 @@ import os
 import numpy as np
 import pytest
 import torch
+import torch.nn.functional as F
 
 import oracle
-from tests.helpers import expand_token_mask, sdpa_reference
+from tests.helpers import expand_token_mask, sdpa_reference, torch_vsa_reference
 from workloads.synth import build_case, make_case
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -277,15 +279,111 @@ def test_compression_single_tile_and_softmax():
         np.testing.assert_allclose(lc[0, h], logsumexp(C[0, h][:, valid], axis=-1), atol=1e-14)
 
 
-def test_gate_composition_adds_gate_times_coarse_output():
-    case = _vsa_small(gate_mode="per_token")
-    orc = oracle.Oracle(case)
+# ---------------------------------------------------------------------------
+# The gated compression branch (composition, pooling gradient, coarse domain)
+# ---------------------------------------------------------------------------
+
+def _gated_cases():
+    # GQA, top-k, per-token gate, a partial Q tile, an empty and a one-slot KV tile
+    yield build_case("gated_tok_gqa", dtype="bf16", layout="bshd", B=1, Hq=4, Hkv=2, D=16,
+                     q_block=8, kv_block=8, q_var=[8, 3, 8, 6], kv_var=[8, 1, 0, 8, 5, 8],
+                     topk=3, map_kind="none", gate_mode="per_token", seed=31)
+    # q-shaped signed gate (the FastVideo gated test's form), BHSD, two batch entries
+    yield build_case("gated_elem_bhsd", dtype="bf16", layout="bhsd", B=2, Hq=2, Hkv=2, D=16,
+                     q_block=8, kv_block=8, q_var=[8, 8, 2], kv_var=[8, 5, 8, 3],
+                     topk=2, map_kind="none", gate_mode="per_element", gate_kind="scaled",
+                     pad_dout=False, seed=32)
+    # a caller-given map with unpadded inputs (no top-k), per-token gate, MQA
+    yield build_case("gated_map_mqa", dtype="fp16", layout="bshd", B=1, Hq=3, Hkv=1, D=16,
+                     q_block=8, kv_block=8, q_var=[5, 8, 8], kv_var=[8, 7, 8], map_kind="per_row",
+                     map_per_row=2, gate_mode="per_token", pad_inputs=False, seed=33)
+
+
+@pytest.mark.parametrize("case", list(_gated_cases()), ids=lambda c: c.name)
+def test_gated_path_matches_torch_autograd_reference(case):
+    """out, dq, dk, dv and dgate of the whole gated path against an independent
+    float64 torch implementation (SDPA for the sparse branch, a tile-averaging
+    matrix for the pooling, softmax over non-empty tiles, additive gate),
+    differentiated by autograd."""
+    orc = oracle.Oracle(case, np.float64)
+    bmap = orc.block_map()
+    out, _, _ = orc.fwd()
+    dq, dk, dv, dg = orc.bwd()
+    r_out, r_dq, r_dk, r_dv, r_dg = torch_vsa_reference(case, bmap)
+    for name, got, ref in (("out", out, r_out), ("dq", dq, r_dq), ("dk", dk, r_dk),
+                           ("dv", dv, r_dv), ("dgate", dg, r_dg)):
+        assert _rel(got, ref) < 1e-11, name
+
+
+def test_zero_gate_reduces_to_the_ungated_path():
+    """gate = 0: out is O_sel exactly and q/k/v get exactly the gradients of
+    the path without a gate (the compression branch adds +0 everywhere)."""
+    case = next(c for c in _gated_cases() if c.name == "gated_tok_gqa")
+    case.gate = torch.zeros_like(case.gate)
+    plain = dataclasses.replace(case, gate_mode="none", gate=None)
+    orc, ref = oracle.Oracle(case), oracle.Oracle(plain)
+    assert np.array_equal(orc.block_map(), ref.block_map())
+    out, osel, lse = orc.fwd()
+    r_out, _, r_lse = ref.fwd()
+    assert np.array_equal(out, osel) and np.array_equal(out, r_out)
+    assert np.array_equal(lse, r_lse)
+    for got, want in zip(orc.bwd()[:3], ref.bwd()[:3]):
+        assert np.array_equal(got, want)
+
+
+def test_one_live_kv_tile_compression_closed_form():
+    """A single KV tile with valid tokens: P_c = 1, so O_c = Vc (the mean of its
+    valid v rows), dgate_s = <dO_s, Vc>, dS_c = 0 (no pooled term in dq, dk)
+    and every valid slot t of that tile gets dv += sum_{heads, all slots s}
+    gate_s dO_s / valid, padded slots nothing."""
+    n = 5
+    case = build_case("one_live", dtype="bf16", layout="bshd", B=1, Hq=2, Hkv=1, D=16,
+                      q_block=8, kv_block=8, q_var=[8, 6], kv_var=[0, n, 0], map_kind="ones",
+                      gate_mode="per_token", pad_inputs=False, seed=41)
+    plain = dataclasses.replace(case, gate_mode="none", gate=None)
+    orc, ref = oracle.Oracle(case), oracle.Oracle(plain)
     out, osel, _ = orc.fwd()
-    oc, _ = orc.coarse()
-    g = orc.gate  # [B,S,H]
-    tile = np.arange(case.Sq) // case.q_block
-    want = osel + g[..., None] * oc[0].transpose(1, 0, 2)[tile][None]
-    np.testing.assert_allclose(out, want, atol=1e-14)
+    dq, dk, dv, dg = orc.bwd()
+    p_dq, p_dk, p_dv, _ = ref.bwd()
+    v = case.v.double().numpy()[0]        # [S, Hkv, D]
+    do = case.dout.double().numpy()[0]    # [S, H, D]
+    g = case.gate.double().numpy()[0]     # [S, H]
+    vc = v[8:8 + n, 0].mean(0)            # tile 1, its n valid slots
+    np.testing.assert_allclose(out[0] - osel[0], g[..., None] * vc, atol=1e-13)
+    np.testing.assert_allclose(dg[0], do @ vc, atol=1e-13)
+    np.testing.assert_allclose(dq, p_dq, atol=1e-13)
+    np.testing.assert_allclose(dk, p_dk, atol=1e-13)
+    extra = np.zeros_like(dv)
+    extra[0, 8:8 + n, 0] = (g[..., None] * do).sum((0, 1)) / n
+    np.testing.assert_allclose(dv - p_dv, extra, atol=1e-12)
+
+
+@pytest.mark.parametrize("partial", [False, True])
+def test_coarse_attention_is_sdpa_over_pooled_tokens(partial):
+    """O_c and lse_c equal dense softmax attention (torch SDPA, float64) over
+    the mean-pooled tiles as tokens, with the empty KV tiles masked out; the
+    pooled tiles are numpy means of each tile's valid rows."""
+    q_var = [8, 3, 8, 6] if partial else [8] * 4
+    kv_var = [8, 1, 0, 8, 5] if partial else [8] * 5
+    case = build_case("pooled_sdpa", dtype="bf16", layout="bhsd", B=1, Hq=4, Hkv=2, D=16,
+                      q_block=8, kv_block=8, q_var=q_var, kv_var=kv_var, map_kind="ones",
+                      gate_mode="per_token", pad_inputs=False, seed=42)
+    oc, lc = oracle.Oracle(case).coarse()
+    q, k, v = (t.double().numpy()[0] for t in (case.q, case.k, case.v))  # [H, S, D]
+
+    def means(x, var):
+        return np.stack([x[:, i * 8:i * 8 + n].mean(1) if n else np.zeros(x[:, 0].shape)
+                         for i, n in enumerate(var)], 1)
+    qc, kc, vc = means(q, q_var), means(k, kv_var), means(v, kv_var)
+    live = torch.as_tensor(np.asarray(kv_var) > 0)
+    t = lambda x: torch.as_tensor(x)[None]  # noqa: E731
+    mask = live.expand(len(q_var), -1)
+    want = F.scaled_dot_product_attention(t(qc), t(kc), t(vc), attn_mask=mask, scale=case.scale,
+                                          enable_gqa=True)[0].numpy()
+    np.testing.assert_allclose(oc[0], want, atol=1e-13)
+    s = case.scale * torch.as_tensor(qc) @ torch.as_tensor(kc).repeat_interleave(2, 0).transpose(1, 2)
+    want_l = torch.logsumexp(s.masked_fill(~live, float("-inf")), -1).numpy()
+    np.testing.assert_allclose(lc[0], want_l, atol=1e-13)
 
 
 # ---------------------------------------------------------------------------
