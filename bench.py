@@ -87,14 +87,40 @@ def valid_pairs(case, bmap: torch.Tensor):
     return valid, padded
 
 
-def cpu_baseline(case, gpu_map_rows_seed=0, target_s=15.0):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    every row of a random set of Q tiles of head 0 (its own pooled-score top-k
-    selection), forward only; rate in the same effective-TFLOP/s unit."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_threads():
+    """Threads for the oracle: every core of the affinity set, but no more than
+    the job's CPU share when the environment states one (OMP_NUM_THREADS)."""
+    aff = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS")
+    return (min(aff, int(share)) if share and share.isdigit() and int(share) > 0 else aff), aff
+
+
+def cpu_baseline(case, gpu_valid_pairs, target_s=12.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload,
+    fwd and bwd timed separately and each extrapolated linearly to the whole
+    workload by its valid (q, k) pair count (labelled as such).
+
+    Sample: head 0 of the workload with its own pooled-score top-k selection.
+    fwd: every row of a random set of Q tiles (oracle fwd_rows). bwd: the full
+    oracle backward (row pass with dq, key pass with dk/dv, compression
+    backward) of the same head with the selection restricted to a random set of
+    Q tiles. Rates are in the bench's unit: 4*D (fwd) and 10*D (bwd) flop per
+    valid pair of the sample."""
     import oracle
     from workloads.synth import build_case
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads, aff = _host_threads()
     sub = build_case(case.name + "_head0", dtype=case.dtype, layout=case.layout, B=1, Hq=1,
                      Hkv=1, D=case.D, q_block=case.q_block, kv_block=case.kv_block,
                      q_var=case.q_var, kv_var=case.kv_var, topk=case.topk, map_kind="none",
@@ -105,40 +131,65 @@ def cpu_baseline(case, gpu_map_rows_seed=0, target_s=15.0):
     tens["gate"] = case.gate[sl].contiguous().cpu() if case.gate is not None else None
     orc = oracle.Oracle(sub, np.float32, threads=threads, tensors=tens)
     t0 = time.perf_counter()
-    bmap = orc.block_map()  # pooling + top-k for the head
-    if sub.gate_mode != "none":
-        orc.coarse()
+    bmap = orc.block_map()  # pooling + top-k of the head
     t_sel = time.perf_counter() - t0
-    qv = np.minimum(np.asarray(sub.q_var), sub.q_block) if sub.q_var is not None else None
-    kv = np.asarray(sub.kv_var) if sub.kv_var is not None else None
+    kv = np.asarray(sub.kv_var, np.float64)
+    qv = np.minimum(np.asarray(sub.q_var, np.float64), sub.q_block)
     rng = np.random.default_rng(1234)
     tiles = rng.permutation(sub.Qb)
-    # calibrate on one tile, then size the sample to the time target
+
+    def pairs(ts):  # valid (q, k) pairs of the listed Q tiles
+        return float(sum(qv[t] * kv[bmap[0, 0, t].astype(bool)].sum() for t in ts))
+
     def rows_of(ts):
         return np.array([[0, 0, t * sub.q_block + r] for t in ts for r in range(sub.q_block)],
                         np.int32)
+
+    def bwd_of(ts):
+        m = np.zeros_like(bmap)
+        m[0, 0, ts] = bmap[0, 0, ts]
+        o = oracle.Oracle(sub, np.float32, threads=threads, tensors=tens)
+        o.set_map(m)
+        t = time.perf_counter()
+        o.bwd()
+        return time.perf_counter() - t
+
+    # forward: calibrate on one tile, then size the sample to the time target
     t0 = time.perf_counter()
     orc.fwd_rows(rows_of(tiles[:1]))
     one = time.perf_counter() - t0
-    n_tiles = int(max(1, min(len(tiles) - 1, target_s / max(one, 1e-3))))
-    sample = tiles[1:1 + n_tiles]
+    nf = int(max(1, min(len(tiles) - 1, 0.4 * target_s / max(one, 1e-3))))
+    fs = tiles[1:1 + nf]
     t0 = time.perf_counter()
-    orc.fwd_rows(rows_of(sample))
-    dt = time.perf_counter() - t0
-    flops = 0.0
-    for t in sample:
-        sel = bmap[0, 0, t].astype(bool)
-        flops += 4.0 * sub.D * sub.q_block * float(kv[sel].sum())  # every row of the tile
+    orc.fwd_rows(rows_of(fs))
+    t_f = time.perf_counter() - t0
+    # backward: the same, on other tiles (calibrated on two, since a backward
+    # call also has fixed costs: the head's pooling, coarse branch, key scan)
+    one = bwd_of(tiles[:2]) / 2
+    nb = int(max(1, min(len(tiles) - 1, 0.6 * target_s / max(one, 1e-3))))
+    bs = tiles[-nb:]
+    t_b = bwd_of(bs)
+    pf, pb = pairs(fs), pairs(bs)
+    fwd_rate = 4.0 * sub.D * pf / t_f / 1e12
+    bwd_rate = 10.0 * sub.D * pb / t_b / 1e12
+    t_f_all = t_f * gpu_valid_pairs / pf
+    t_b_all = t_b * gpu_valid_pairs / pb
     return {
-        "value": flops / dt / 1e12,
+        "value": (4.0 + 10.0) * sub.D * gpu_valid_pairs / (t_f_all + t_b_all) / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fwd of all {sub.q_block} rows of {len(sample)} random Q tiles of head 0 "
-                   f"(of {sub.Qb} tiles x {case.Hq} heads), fp32 oracle, {dt:.1f} s; "
-                   f"rate over the sampled rows' valid keys"),
-        "seconds": round(dt, 2),
+        "sample": (f"fp32 oracle on head 0 of {case.Hq} with its own top-k selection: fwd of "
+                   f"all {sub.q_block} rows of {len(fs)} random Q tiles ({t_f:.1f} s), full "
+                   f"backward with the selection cut to {len(bs)} other Q tiles ({t_b:.1f} s); "
+                   f"rates over the sampled valid pairs; whole-workload seconds extrapolated "
+                   f"linearly by valid pairs"),
+        "fwd_tflops": round(fwd_rate, 4), "bwd_tflops": round(bwd_rate, 4),
+        "fwd_seconds_sample": round(t_f, 2), "bwd_seconds_sample": round(t_b, 2),
+        "fwd_seconds_extrapolated": round(t_f_all, 1),
+        "bwd_seconds_extrapolated": round(t_b_all, 1),
         "selection_seconds": round(t_sel, 2),
+        "cpu_model": _cpu_model(), "affinity_cores": aff,
     }
 
 
@@ -351,7 +402,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="c5_vsa256_720p_gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--dout-unpadded", action="store_true",
+                    help="draw dO without zeroing the padded slots of partial tiles")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES on the device once (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -392,7 +445,7 @@ def main():
 
     torch.cuda.set_device(0)
     log(f"[bench] generating {args.workload} on cuda:0")
-    case = make_case(args.workload, device="cuda")
+    case = make_case(args.workload, device="cuda", **({"pad_dout": False} if args.dout_unpadded else {}))
     d = device_inputs(case)
     p = vsa.make_problem(
         dtype=case.torch_dtype, layout=case.layout, B=case.B, Hq=case.Hq, Hkv=case.Hkv,
@@ -445,8 +498,12 @@ def main():
 
     per_kernel = {k: {"ms_per_launch": (ms / n if n else 0.0), "launches_per_step": n / args.steps}
                   for k, (ms, n) in prof.items()}
+    # algorithmic work of each stage (the metric's 4*D + 10*D per valid pair:
+    # dK/dV does S, dP, dV, dK; dQ adds only its own GEMM, its recomputed S and
+    # dP being overhead) and the work each stage executes
     kflops = {"sparse_fwd": 4.0 * case.D * valid, "sparse_dkdv": 8.0 * case.D * valid,
-              "sparse_dq": 6.0 * case.D * valid}
+              "sparse_dq": 2.0 * case.D * valid}
+    kflops_exec = dict(kflops, sparse_dq=6.0 * case.D * valid)
     dom = max(kflops, key=lambda k: prof[k][0])
     dom_ms = prof[dom][0] / max(prof[dom][1], 1)
     achieved = kflops[dom] / (dom_ms * 1e-3) / 1e12
@@ -469,7 +526,8 @@ def main():
         "config": {"workload": case.name, "layout": case.layout, "B": case.B, "H": case.Hq,
                    "D": case.D, "tiles": case.Qb, "tile": case.q_block, "topk": case.topk,
                    "gate": case.gate_mode, "tokens_valid": int(np.sum(case.q_var))
-                   if case.q_var is not None else case.Sq},
+                   if case.q_var is not None else case.Sq,
+                   "dout": "unpadded" if args.dout_unpadded else "zero in padded slots"},
         "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
         "fwd_ms_min": round(float(min(fwd_all)), 3), "bwd_ms_min": round(float(min(bwd_all)), 3),
         "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2),
@@ -479,6 +537,9 @@ def main():
         "fwd_tflops_padded": round(4.0 * case.D * padded / (fwd_ms * 1e-3) / 1e12, 2),
         "per_kernel_ms": {k: round(v["ms_per_launch"] * v["launches_per_step"], 3)
                           for k, v in per_kernel.items()},
+        "stage_tflops": {k: {"algorithmic": round(kflops[k] / (prof[k][0] / max(prof[k][1], 1) * 1e-3) / 1e12, 1),
+                             "executed": round(kflops_exec[k] / (prof[k][0] / max(prof[k][1], 1) * 1e-3) / 1e12, 1)}
+                         for k in kflops if prof.get(k, (0, 0))[1]},
         "roofline": roofline,
     }
     if args.copy_probe > 0:  # a plain copy of known size, for counter calibration
@@ -489,7 +550,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline(case, target_s=args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(case, valid, target_s=args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -355,3 +355,26 @@ def test_c2_full_size_sampled_heads():
         check("dq", dq[b, h], res["dq"][b, h], GRAD_TOL)
         check("dk", dk[b, h], res["dk"][b, h], GRAD_TOL)
         check("dv", dv[b, h], res["dv"][b, h], GRAD_TOL)
+
+
+def test_empty_kv_tiles_and_topk_above_the_live_tiles():
+    """KV tiles without a valid token (kv_var = 0) are never selected, never
+    attended and get zero gradients; topk above the number of non-empty tiles
+    selects every non-empty tile. GQA with the per-token gate, so the coarse
+    softmax also runs over the non-empty tiles only."""
+    for layout in ("bshd", "bhsd"):
+        case = build_case(f"empty_kv_topk_{layout}", dtype="bf16", layout=layout, B=1, Hq=4,
+                          Hkv=2, D=128, q_var=[256, 130, 256], kv_var=[256, 0, 100, 0, 64],
+                          topk=4, map_kind="none", gate_mode="per_token", seed=37)
+        _say(f"[{case.name}]")
+        res = run_case(case)
+        m = res["map"]
+        assert np.all(m[..., [1, 3]] == 0) and np.all(m[..., [0, 2, 4]] == 1)
+        orc = oracle.Oracle(case, np.float32)
+        assert np.array_equal(orc.block_map(), m)
+        _compare_case(case, res, orc)
+        dk = res["dk"] if layout == "bhsd" else res["dk"].transpose(0, 2, 1, 3)
+        dv = res["dv"] if layout == "bhsd" else res["dv"].transpose(0, 2, 1, 3)
+        for j in (1, 3):
+            assert np.all(dk[:, :, j * 256:(j + 1) * 256] == 0) and \
+                np.all(dv[:, :, j * 256:(j + 1) * 256] == 0), (layout, j)

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from tests.helpers import GRAD_TOL, OUT_TOL, check
-from workloads.synth import make_case
+from workloads.synth import build_case, make_case
 
 pytestmark = pytest.mark.gpu
 
@@ -98,3 +98,45 @@ def test_block_map_entry_against_the_oracle():
     check("dq", dq_r, q.grad.float().cpu().numpy(), GRAD_TOL)
     check("dk", dk_r, k.grad.float().cpu().numpy(), GRAD_TOL)
     check("dv", dv_r, v.grad.float().cpu().numpy(), GRAD_TOL)
+
+
+def test_vsa128_video_entries_against_the_oracle():
+    """VSA-128: (2, 8, 8) video tiles of 128 tokens through video_sparse_attn and
+    its BSHD twin, with partial q_var / kv_var, pooled-score top-k and a signed
+    q-shaped gate, autograd through q, k, v and the gate, against the oracle."""
+    from tests.test_gpu_parity import _topk_agreement
+    case = build_case("vsa128", dtype="bf16", layout="bhsd", B=1, Hq=2, D=128, q_block=128,
+                      kv_block=128, q_var=[128, 77, 128, 40], kv_var=[128, 128, 33, 128, 90],
+                      topk=3, map_kind="none", gate_mode="per_element", gate_kind="scaled",
+                      pad_dout=False, seed=43, device="cuda")
+    orc = oracle.Oracle(case, np.float64, threads=8)
+    o_ref, _, _ = orc.fwd()
+    dq_r, dk_r, dv_r, dg_r = orc.bwd()
+    for layout in ("bhsd", "bshd"):
+        c = case
+        if layout == "bshd":
+            import copy
+            c = copy.copy(case)
+            for n in ("q", "k", "v", "dout", "gate"):
+                setattr(c, n, _transposed(getattr(case, n)))
+        q, k, v, g = (_leaf(getattr(c, n)) for n in ("q", "k", "v", "gate"))
+        fn = vsa.video_sparse_attn if layout == "bhsd" else vsa.video_sparse_attn_bshd
+        out = fn(q, k, v, c.kv_var, c.q_var, c.topk, block_size=(2, 8, 8),
+                 compress_attn_weight=g, scale=c.scale)
+        (out * c.dout.cuda()).sum().backward()
+        back = (lambda t: t.transpose(1, 2)) if layout == "bshd" else (lambda t: t)
+        # the selection the library made must be the oracle's (no near-ties here)
+        p = vsa.make_problem(dtype=q.dtype, layout=layout, B=1, Hq=2, Hkv=2, Sq=c.Sq,
+                             Skv=c.Skv, D=128, q_block=128, kv_block=128,
+                             q_valid=torch.as_tensor(c.q_var, dtype=torch.int32, device="cuda"),
+                             kv_valid=torch.as_tensor(c.kv_var, dtype=torch.int32, device="cuda"),
+                             scale=c.scale, topk=c.topk, gate_mode="per_element")
+        buf = vsa.Buffers(p, q.detach(), training=False)
+        vsa.vsa_fwd(p, q.detach(), k.detach(), v.detach(), buf.map, g.detach(), buf.out, buf.lse,
+                    None, buf.ws_fwd)
+        torch.cuda.synchronize()
+        assert _topk_agreement(orc, buf.map.cpu().numpy()).all()
+        print(f"[vsa128 {layout}]")
+        check("out", o_ref, back(out.detach()).float().cpu().numpy(), OUT_TOL)
+        for name, ref, t in (("dq", dq_r, q), ("dk", dk_r, k), ("dv", dv_r, v), ("dgate", dg_r, g)):
+            check(name, ref, back(t.grad).float().cpu().numpy(), GRAD_TOL)
