@@ -6,7 +6,8 @@ memory and the current stream. Importing works without a GPU; calling a
 compute entry point without the built library raises (there is no fallback).
 
 Entry points (same names as the C ABI): vsa_validate, vsa_sizes,
-block_map_to_index, vsa_fwd, vsa_bwd, vsa_last_error, vsa_abi_version.
+block_map_to_index, vsa_fwd, vsa_fwd_noalloc, vsa_bwd, vsa_last_error,
+vsa_abi_version.
 """
 
 from __future__ import annotations
@@ -29,7 +30,9 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 ABI_VERSION = 1
 
 EXPORTS = ("vsa_last_error", "vsa_abi_version", "vsa_validate", "vsa_sizes",
-           "block_map_to_index", "vsa_fwd", "vsa_bwd", "vsa_profile_begin", "vsa_profile_end")
+           "block_map_to_index", "vsa_fwd", "vsa_fwd_noalloc", "vsa_bwd", "vsa_profile_begin",
+           "vsa_profile_end")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # VSA_NOALLOC_SCRATCH_BYTES
 KERNELS = ("index", "pool", "coarse_fwd", "sparse_fwd", "bwd_pre", "coarse_bwd", "sparse_dkdv",
            "sparse_dq")
 
@@ -72,7 +75,8 @@ def lib():
         L = C.CDLL(LIB_PATH)
         L.vsa_last_error.restype = C.c_char_p
         for name in ("vsa_abi_version", "vsa_validate", "vsa_sizes", "block_map_to_index",
-                     "vsa_fwd", "vsa_bwd", "vsa_profile_begin", "vsa_profile_end"):
+                     "vsa_fwd", "vsa_fwd_noalloc", "vsa_bwd", "vsa_profile_begin",
+                     "vsa_profile_end"):
             getattr(L, name).restype = C.c_int
         _LIB = L
     return _LIB
@@ -244,6 +248,18 @@ def vsa_fwd(p: Problem, q, k, v, block_map, gate, out, lse, saved, ws, stream=No
         p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(block_map), _ptr(gate), _ptr(out), _ptr(lse),
         _ptr(saved), C.c_size_t(0 if saved is None else saved.numel() * saved.element_size()),
         _ptr(ws), C.c_size_t(0 if ws is None else ws.numel() * ws.element_size()),
+        _stream(stream)))
+
+
+def vsa_fwd_noalloc(p: Problem, q, k, v, block_map, gate, out, lse, saved, stream=None) -> None:
+    """vsa_fwd with the library's own device scratch as the forward workspace
+    (no allocation in the call; problems whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES are refused with ERR_WORKSPACE)."""
+    if q is not None:
+        _check_tensors(p, q, k, v, gate, qlike=(("out", out),), lse=lse, block_map=block_map)
+    _check(lib().vsa_fwd_noalloc(
+        p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(block_map), _ptr(gate), _ptr(out), _ptr(lse),
+        _ptr(saved), C.c_size_t(0 if saved is None else saved.numel() * saved.element_size()),
         _stream(stream)))
 
 

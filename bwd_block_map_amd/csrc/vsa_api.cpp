@@ -61,7 +61,7 @@ struct Prof {
   ProfRec* r = nullptr;
   hipStream_t st;
   Prof(int kid, hipStream_t s) : st(s) {
-    if (!g_prof_on) return;
+    if (!g_prof_on || kid < 0) return;  // kid < 0: a launch that records nothing
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (g_prof_recs.size() >= kProfMax) return;
     while (g_prof_pool.size() < 2 * (g_prof_recs.size() + 1)) {
@@ -326,6 +326,146 @@ int check_device(const vsa_problem* p, std::initializer_list<Arg> args) {
   return VSA_OK;
 }
 
+// The forward launch sequence. ws_scratch: ws is the library's own scratch
+// (the no-alloc entry point): it is not checked as a caller pointer, and no
+// profiler events are recorded.
+int fwd_impl(const vsa_problem* p, const void* q, const void* k, const void* v, uint8_t* block_map,
+             const void* gate, void* out, float* lse, void* saved, size_t saved_bytes, void* ws,
+             size_t ws_bytes, void* stream, bool ws_scratch) {
+  int rc = validate(p);
+  if (rc != VSA_OK) return rc;
+  if (!q || !k || !v || !out || !lse)
+    return fail(VSA_ERR_INVALID_ARG, "q, k, v, out and lse must be device buffers");
+  if (p->topk == 0 && !block_map)
+    return fail(VSA_ERR_INVALID_ARG, "block_map must be given when topk == 0");
+  if (p->topk > 0 && block_map && p->map_batch_stride != (long long)p->Hq * p->Qb * p->KVb &&
+      !(p->map_batch_stride == 0 && p->B == 1))
+    return fail(VSA_ERR_INVALID_ARG, "an output block_map must be a dense [B,Hq,Qb,KVb] buffer");
+  if (p->gate_mode != VSA_GATE_NONE && !gate)
+    return fail(VSA_ERR_INVALID_ARG, "gate must be given when gate_mode != NONE");
+  size_t need_ws = 0, need_saved = 0;
+  carve_fwd(p, nullptr, &need_ws);
+  carve_saved(p, nullptr, &need_saved);
+  if (ws_bytes < need_ws || (!ws && need_ws))
+    return fail(VSA_ERR_WORKSPACE, "forward workspace: %zu bytes needed, %zu given", need_ws, ws_bytes);
+  if (saved && saved_bytes < need_saved)
+    return fail(VSA_ERR_WORKSPACE, "saved state: %zu bytes needed, %zu given", need_saved,
+                saved_bytes);
+  if (int c = check_device(p, {{q, "q"}, {k, "k"}, {v, "v"}, {block_map, "block_map"}, {gate, "gate"},
+                               {out, "out"}, {lse, "lse"}, {saved, "saved"},
+                               {ws_scratch ? nullptr : ws, "ws"}}))
+    return c;
+  hipStream_t st = (hipStream_t)stream;
+  const FwdWs w = carve_fwd(p, ws, nullptr);
+  const Saved s = saved ? carve_saved(p, saved, nullptr) : Saved{};
+  vsa::Geom g = make_geom(p);
+  hipError_t e = hipSuccess;
+  const long long cap = nnz_cap(p);
+
+  // pooled tiles, top-k selection and the coarse attention
+  const bool gated = p->gate_mode != VSA_GATE_NONE;
+  float* qc = (gated && saved) ? s.qc : w.qc;
+  float* kc = (gated && saved) ? s.kc : w.kc;
+  float* vc = (gated && saved) ? s.vc : w.vc;
+  float* oc = (gated && saved) ? s.oc : w.oc;
+  float* lse_c = (gated && saved) ? s.lse_c : w.lse_c;
+  const uint8_t* sel_map = block_map;
+  if (is_video(p)) {
+    {
+      Prof pr(ws_scratch ? -1 : VSA_KERNEL_POOL, st);
+      e = vsa::launch_pool(g, p->dtype, q, k, v, qc, kc, vc, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "pool");
+    vsa::CoarseArgs ca{};
+    ca.g = g;
+    ca.qc = qc;
+    ca.kc = kc;
+    ca.vc = vc;
+    ca.topk = p->topk;
+    ca.map = p->topk > 0 ? (block_map ? block_map : w.map) : nullptr;
+    ca.oc = oc;
+    ca.lse_c = lse_c;
+    {
+      Prof pr(ws_scratch ? -1 : VSA_KERNEL_COARSE_FWD, st);
+      e = vsa::launch_coarse_fwd(ca, p->topk > 0, gated, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "coarse forward");
+    if (p->topk > 0) {
+      sel_map = ca.map;
+      g.map_bstride = (long long)p->Hq * p->Qb * p->KVb;
+    }
+  }
+  // index: Q-owned always, KV-owned only when a backward follows
+  int32_t* q_rp = saved ? s.q_rp : w.q_rp;
+  int32_t* q_col = saved ? s.q_col : w.q_col;
+  {
+    Prof pr(ws_scratch ? -1 : VSA_KERNEL_INDEX, st);
+    e = vsa::launch_index(g, sel_map, 0, q_rp, q_col, cap, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "index (Q-owned)");
+  if (saved) {
+    Prof pr(ws_scratch ? -1 : VSA_KERNEL_INDEX, st);
+    e = vsa::launch_index(g, sel_map, 1, s.kv_rp, s.kv_col, cap, st);
+    if (e != hipSuccess) return hip_fail(e, "index (KV-owned)");
+  }
+  vsa::FwdArgs fa{};
+  fa.g = g;
+  fa.q = (const uint16_t*)q;
+  fa.k = (const uint16_t*)k;
+  fa.v = (const uint16_t*)v;
+  fa.gate = (const uint16_t*)gate;
+  fa.oc = oc;
+  fa.gate_mode = p->gate_mode;
+  fa.out = (uint16_t*)out;
+  fa.osel = (gated && saved) ? s.osel : nullptr;
+  fa.lse = lse;
+  fa.row_ptr = q_rp;
+  fa.col = q_col;
+  {
+    Prof pr(ws_scratch ? -1 : VSA_KERNEL_SPARSE_FWD, st);
+    e = vsa::launch_sparse_fwd(fa, p->dtype, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "sparse forward");
+  return ok();
+}
+
+// ---- scratch of the entry point that allocates nothing ----------------------
+// A static device array (each GPU holds its own copy while the library is
+// loaded). Its name is a host-side stand-in in host code: kernels get the
+// device address looked up once per device with hipGetSymbolAddress.
+constexpr size_t kScratchBytes = VSA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device that owns `st` (which must be the current
+// device: the launches go to `st`, the lookup to the current device).
+int scratch_of_stream(hipStream_t st, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "vsa_fwd_noalloc: hipGetDevice");
+  if (st) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(st, &sd);
+    if (e != hipSuccess) return hip_fail(e, "vsa_fwd_noalloc: hipStreamGetDevice");
+    if (sd != dev)
+      return fail(VSA_ERR_INVALID_ARG, "vsa_fwd_noalloc: the stream belongs to device %d, the "
+                  "current device is %d", (int)sd, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_fwd_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "vsa_fwd_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = a;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return VSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -381,100 +521,29 @@ int block_map_to_index(const vsa_problem* p, const uint8_t* block_map, int kv_ow
 int vsa_fwd(const vsa_problem* p, const void* q, const void* k, const void* v, uint8_t* block_map,
             const void* gate, void* out, float* lse, void* saved, size_t saved_bytes, void* ws,
             size_t ws_bytes, void* stream) {
+  return fwd_impl(p, q, k, v, block_map, gate, out, lse, saved, saved_bytes, ws, ws_bytes, stream,
+                  false);
+}
+
+int vsa_fwd_noalloc(const vsa_problem* p, const void* q, const void* k, const void* v,
+                    uint8_t* block_map, const void* gate, void* out, float* lse, void* saved,
+                    size_t saved_bytes, void* stream) {
   int rc = validate(p);
   if (rc != VSA_OK) return rc;
+  size_t need = 0;
+  carve_fwd(p, nullptr, &need);
+  if (need > kScratchBytes)
+    return fail(VSA_ERR_WORKSPACE,
+                "vsa_fwd_noalloc: the forward workspace needs %zu bytes, more than its %zu-byte "
+                "scratch (use vsa_fwd with a caller workspace)",
+                need, kScratchBytes);
   if (!q || !k || !v || !out || !lse)
     return fail(VSA_ERR_INVALID_ARG, "q, k, v, out and lse must be device buffers");
-  if (p->topk == 0 && !block_map)
-    return fail(VSA_ERR_INVALID_ARG, "block_map must be given when topk == 0");
-  if (p->topk > 0 && block_map && p->map_batch_stride != (long long)p->Hq * p->Qb * p->KVb &&
-      !(p->map_batch_stride == 0 && p->B == 1))
-    return fail(VSA_ERR_INVALID_ARG, "an output block_map must be a dense [B,Hq,Qb,KVb] buffer");
-  if (p->gate_mode != VSA_GATE_NONE && !gate)
-    return fail(VSA_ERR_INVALID_ARG, "gate must be given when gate_mode != NONE");
-  size_t need_ws = 0, need_saved = 0;
-  carve_fwd(p, nullptr, &need_ws);
-  carve_saved(p, nullptr, &need_saved);
-  if (ws_bytes < need_ws || (!ws && need_ws))
-    return fail(VSA_ERR_WORKSPACE, "forward workspace: %zu bytes needed, %zu given", need_ws, ws_bytes);
-  if (saved && saved_bytes < need_saved)
-    return fail(VSA_ERR_WORKSPACE, "saved state: %zu bytes needed, %zu given", need_saved,
-                saved_bytes);
-  if (int c = check_device(p, {{q, "q"}, {k, "k"}, {v, "v"}, {block_map, "block_map"}, {gate, "gate"},
-                               {out, "out"}, {lse, "lse"}, {saved, "saved"}, {ws, "ws"}}))
-    return c;
-  hipStream_t st = (hipStream_t)stream;
-  const FwdWs w = carve_fwd(p, ws, nullptr);
-  const Saved s = saved ? carve_saved(p, saved, nullptr) : Saved{};
-  vsa::Geom g = make_geom(p);
-  hipError_t e = hipSuccess;
-  const long long cap = nnz_cap(p);
-
-  // pooled tiles, top-k selection and the coarse attention
-  const bool gated = p->gate_mode != VSA_GATE_NONE;
-  float* qc = (gated && saved) ? s.qc : w.qc;
-  float* kc = (gated && saved) ? s.kc : w.kc;
-  float* vc = (gated && saved) ? s.vc : w.vc;
-  float* oc = (gated && saved) ? s.oc : w.oc;
-  float* lse_c = (gated && saved) ? s.lse_c : w.lse_c;
-  const uint8_t* sel_map = block_map;
-  if (is_video(p)) {
-    {
-      Prof pr(VSA_KERNEL_POOL, st);
-      e = vsa::launch_pool(g, p->dtype, q, k, v, qc, kc, vc, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "pool");
-    vsa::CoarseArgs ca{};
-    ca.g = g;
-    ca.qc = qc;
-    ca.kc = kc;
-    ca.vc = vc;
-    ca.topk = p->topk;
-    ca.map = p->topk > 0 ? (block_map ? block_map : w.map) : nullptr;
-    ca.oc = oc;
-    ca.lse_c = lse_c;
-    {
-      Prof pr(VSA_KERNEL_COARSE_FWD, st);
-      e = vsa::launch_coarse_fwd(ca, p->topk > 0, gated, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "coarse forward");
-    if (p->topk > 0) {
-      sel_map = ca.map;
-      g.map_bstride = (long long)p->Hq * p->Qb * p->KVb;
-    }
-  }
-  // index: Q-owned always, KV-owned only when a backward follows
-  int32_t* q_rp = saved ? s.q_rp : w.q_rp;
-  int32_t* q_col = saved ? s.q_col : w.q_col;
-  {
-    Prof pr(VSA_KERNEL_INDEX, st);
-    e = vsa::launch_index(g, sel_map, 0, q_rp, q_col, cap, st);
-  }
-  if (e != hipSuccess) return hip_fail(e, "index (Q-owned)");
-  if (saved) {
-    Prof pr(VSA_KERNEL_INDEX, st);
-    e = vsa::launch_index(g, sel_map, 1, s.kv_rp, s.kv_col, cap, st);
-    if (e != hipSuccess) return hip_fail(e, "index (KV-owned)");
-  }
-  vsa::FwdArgs fa{};
-  fa.g = g;
-  fa.q = (const uint16_t*)q;
-  fa.k = (const uint16_t*)k;
-  fa.v = (const uint16_t*)v;
-  fa.gate = (const uint16_t*)gate;
-  fa.oc = oc;
-  fa.gate_mode = p->gate_mode;
-  fa.out = (uint16_t*)out;
-  fa.osel = (gated && saved) ? s.osel : nullptr;
-  fa.lse = lse;
-  fa.row_ptr = q_rp;
-  fa.col = q_col;
-  {
-    Prof pr(VSA_KERNEL_SPARSE_FWD, st);
-    e = vsa::launch_sparse_fwd(fa, p->dtype, st);
-  }
-  if (e != hipSuccess) return hip_fail(e, "sparse forward");
-  return ok();
+  void* ws = nullptr;
+  rc = scratch_of_stream((hipStream_t)stream, &ws);
+  if (rc != VSA_OK) return rc;
+  return fwd_impl(p, q, k, v, block_map, gate, out, lse, saved, saved_bytes, ws, kScratchBytes,
+                  stream, true);
 }
 
 int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, const void* gate,

@@ -22,7 +22,8 @@
  *  - Every tensor argument is a DEVICE pointer to a contiguous buffer in the
  *    layout stated below; the caller allocates and owns every buffer (inputs,
  *    outputs, the saved state and the workspace). The library allocates no
- *    device memory and keeps no state between calls.
+ *    device memory and keeps no state between calls; the one exception is the
+ *    fixed scratch array that vsa_fwd_noalloc uses in place of a workspace.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream).
  *  - Return value: VSA_OK or one of the VSA_ERR_* codes. Argument errors are
  *    detected on the host before anything is launched; vsa_last_error() then
@@ -201,6 +202,29 @@ int block_map_to_index(const vsa_problem* p, const uint8_t* block_map, int kv_ow
 int vsa_fwd(const vsa_problem* p, const void* q, const void* k, const void* v,
             uint8_t* block_map, const void* gate, void* out, float* lse, void* saved,
             size_t saved_bytes, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The computation, arguments and results are those of vsa_fwd (out and lse
+ * bit for bit), without ws / ws_bytes: the forward workspace is a scratch
+ * array of VSA_NOALLOC_SCRATCH_BYTES that the library keeps in each GPU's
+ * memory (a static device array, held until the process ends; its device
+ * address is looked up on the first call on each device). This call makes no
+ * hipMalloc, hipFree or other allocating call and records no profiler events.
+ *  - A problem whose forward workspace (ws_fwd of vsa_sizes) exceeds
+ *    VSA_NOALLOC_SCRATCH_BYTES gives VSA_ERR_WORKSPACE before any launch.
+ *  - stream must belong to the current device (else VSA_ERR_INVALID_ARG).
+ *  - Every call on one GPU uses that GPU's single scratch: calls that overlap
+ *    on one GPU (other streams, other threads) race and must be serialised by
+ *    the caller. Nothing in the scratch needs to start at zero: each call
+ *    writes every part of it that it reads.
+ *  - saved (training) is still a caller buffer, as for vsa_fwd.
+ */
+#define VSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int vsa_fwd_noalloc(const vsa_problem* p, const void* q, const void* k, const void* v,
+                    uint8_t* block_map, const void* gate, void* out, float* lse, void* saved,
+                    size_t saved_bytes, void* stream);
 
 /*
  * Backward of L = sum(out * dout) ([FV-cute] `_CuteAttentionQ128.backward`;

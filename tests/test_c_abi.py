@@ -115,3 +115,19 @@ def test_compute_calls_reject_bad_arguments_before_launching():
     with pytest.raises(vsa.VsaError) as e:
         vsa.vsa_bwd(p, None, None, None, None, None, None, None, None, None, None, None, None, None)
     assert e.value.code == vsa.ERR_INVALID_ARG
+
+
+def test_noalloc_forward_refuses_a_workspace_beyond_its_scratch():
+    """vsa_fwd_noalloc checks the problem's forward workspace against its fixed
+    scratch on the host, before it looks at any pointer or device: the 720p
+    video problem (top-k map, pooled tiles, coarse output: > 64 MiB) is refused
+    with VSA_ERR_WORKSPACE. The pointers are placeholders that are never read."""
+    import ctypes as C
+    p = _prob(layout="bshd", Hq=40, Hkv=40, Sq=368640, Skv=368640, topk=144,
+              gate_mode="per_token")
+    assert vsa.vsa_sizes(p)["ws_fwd"] > vsa.NOALLOC_SCRATCH_BYTES
+    fake = C.c_void_p(256)
+    rc = vsa.lib().vsa_fwd_noalloc(p.ref, fake, fake, fake, fake, fake, fake, fake, None,
+                                   C.c_size_t(0), None)
+    assert rc == vsa.ERR_WORKSPACE
+    assert "scratch" in vsa.vsa_last_error()
