@@ -403,6 +403,8 @@ def main():
     ap.add_argument("--workload", default="c5_vsa256_720p_gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--atomic-dq", action="store_true",
+                    help="time the backward that adds dQ inside the dK/dV pass with atomics")
     ap.add_argument("--dout-unpadded", action="store_true",
                     help="draw dO without zeroing the padded slots of partial tiles")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -453,7 +455,7 @@ def main():
         q_valid=d["q_valid"], kv_valid=d["kv_valid"], cu_seqlens_q=d["cu_q"],
         cu_seqlens_kv=d["cu_kv"], max_seqlen_q=max(case.q_lens) if case.q_lens else 0,
         max_seqlen_kv=max(case.kv_lens) if case.kv_lens else 0, scale=case.scale,
-        topk=case.topk, gate_mode=case.gate_mode)
+        topk=case.topk, gate_mode=case.gate_mode, atomic_dq=args.atomic_dq)
     buf = vsa.Buffers(p, d["q"], training=True)
     bmap = d["map"] if case.topk == 0 else buf.map
     dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
@@ -501,7 +503,9 @@ def main():
     # algorithmic work of each stage (the metric's 4*D + 10*D per valid pair:
     # dK/dV does S, dP, dV, dK; dQ adds only its own GEMM, its recomputed S and
     # dP being overhead) and the work each stage executes
-    kflops = {"sparse_fwd": 4.0 * case.D * valid, "sparse_dkdv": 8.0 * case.D * valid,
+    # (with --atomic-dq the dK/dV pass also does the dQ GEMM: 10*D per pair)
+    kflops = {"sparse_fwd": 4.0 * case.D * valid,
+              "sparse_dkdv": (10.0 if args.atomic_dq else 8.0) * case.D * valid,
               "sparse_dq": 2.0 * case.D * valid}
     kflops_exec = dict(kflops, sparse_dq=6.0 * case.D * valid)
     dom = max(kflops, key=lambda k: prof[k][0])
@@ -527,7 +531,8 @@ def main():
                    "D": case.D, "tiles": case.Qb, "tile": case.q_block, "topk": case.topk,
                    "gate": case.gate_mode, "tokens_valid": int(np.sum(case.q_var))
                    if case.q_var is not None else case.Sq,
-                   "dout": "unpadded" if args.dout_unpadded else "zero in padded slots"},
+                   "dout": "unpadded" if args.dout_unpadded else "zero in padded slots",
+                   "dq": "atomic in the dK/dV pass" if args.atomic_dq else "separate Q-owned pass"},
         "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
         "fwd_ms_min": round(float(min(fwd_all)), 3), "bwd_ms_min": round(float(min(bwd_all)), 3),
         "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2),

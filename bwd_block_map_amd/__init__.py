@@ -27,14 +27,15 @@ BF16, FP16 = 0, 1
 BHSD, BSHD, TND = 0, 1, 2
 GATE_NONE, GATE_PER_TOKEN, GATE_PER_ELEMENT = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ABI_VERSION = 1
+ABI_VERSION = 2
+FLAG_ATOMIC_DQ = 1
 
 EXPORTS = ("vsa_last_error", "vsa_abi_version", "vsa_validate", "vsa_sizes",
            "block_map_to_index", "vsa_fwd", "vsa_fwd_noalloc", "vsa_bwd", "vsa_profile_begin",
            "vsa_profile_end")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # VSA_NOALLOC_SCRATCH_BYTES
 KERNELS = ("index", "pool", "coarse_fwd", "sparse_fwd", "bwd_pre", "coarse_bwd", "sparse_dkdv",
-           "sparse_dq")
+           "sparse_dq", "dq_atomic_aux")
 
 _DTYPES = {torch.bfloat16: BF16, torch.float16: FP16}
 _LAYOUTS = {"bhsd": BHSD, "bshd": BSHD, "tnd": TND}
@@ -58,7 +59,7 @@ class VsaProblem(C.Structure):
         ("cu_seqlens_q", C.c_void_p), ("cu_seqlens_kv", C.c_void_p),
         ("max_seqlen_q", C.c_int32), ("max_seqlen_kv", C.c_int32),
         ("scale", C.c_float), ("topk", C.c_int32), ("gate_mode", C.c_int32),
-        ("map_batch_stride", C.c_int64),
+        ("map_batch_stride", C.c_int64), ("flags", C.c_int32),
     ]
 
 
@@ -131,8 +132,11 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
                  cu_seqlens_q: Optional[torch.Tensor] = None,
                  cu_seqlens_kv: Optional[torch.Tensor] = None, max_seqlen_q: int = 0,
                  max_seqlen_kv: int = 0, scale: Optional[float] = None, topk: int = 0,
-                 gate_mode: str = "none", map_batch_stride: Optional[int] = None) -> Problem:
-    """Fill a vsa_problem. q_valid / kv_valid / cu_seqlens are int32 device tensors."""
+                 gate_mode: str = "none", map_batch_stride: Optional[int] = None,
+                 atomic_dq: bool = False) -> Problem:
+    """Fill a vsa_problem. q_valid / kv_valid / cu_seqlens are int32 device tensors.
+    atomic_dq selects the backward that adds dQ inside the KV-owned pass
+    (VSA_FLAG_ATOMIC_DQ)."""
     lay = _LAYOUTS[layout]
     if lay == TND:
         Qb = -(-max_seqlen_q // q_block)
@@ -168,7 +172,8 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
         cu_seqlens_kv=None if cu_seqlens_kv is None else cu_seqlens_kv.data_ptr(),
         max_seqlen_q=max_seqlen_q, max_seqlen_kv=max_seqlen_kv,
         scale=1.0 / math.sqrt(D) if scale is None else float(scale), topk=topk,
-        gate_mode=_GATES[gate_mode], map_batch_stride=map_batch_stride)
+        gate_mode=_GATES[gate_mode], map_batch_stride=map_batch_stride,
+        flags=FLAG_ATOMIC_DQ if atomic_dq else 0)
     return Problem(s, keep)
 
 

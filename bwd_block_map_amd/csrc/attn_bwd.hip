@@ -156,7 +156,9 @@ constexpr int DKDV_NW = 8;
 constexpr int DKDV_SPAN = 256;
 constexpr int DKDV_LIST_CAP = 1024;
 
-template <int KS>
+// AQ: the variant that also adds each chunk's dQ = dS K into a float
+// accumulator with atomics (fewer ring slots: its dS tile takes LDS).
+template <int KS, bool AQ = false>
 struct DkdvShape {
   static constexpr int NW = DKDV_NW;
   static constexpr int RG = NW / KS;                 // row groups
@@ -164,7 +166,8 @@ struct DkdvShape {
   static constexpr int QC = 32 * RG;                 // query rows per chunk
   static constexpr int QT = QC * HD * 2;             // bytes of a QC-row tile
   static constexpr int STAGE = 2 * QT + 2 * QC * 4;  // Q | dO | lse2 | dr
-  static constexpr int NST = KS == 8 ? 4 : KS == 4 ? 3 : 2;  // ring slots (LDS budget)
+  // ring slots (LDS budget)
+  static constexpr int NST = AQ ? (KS == 8 ? 3 : 2) : (KS == 8 ? 4 : KS == 4 ? 3 : 2);
   // direct loads per chunk and wave: Q and dO rows; the first wave of each row
   // group also loads the group's lse2 and dr
   static constexpr int LPC_ROWS = 2 * (QC / 4 / NW);
@@ -188,25 +191,52 @@ __device__ __forceinline__ int dkdv_shape(int live) { return live > 128 ? 8 : li
 // tile, the V^T columns d >= 16 DKDV_VREG ([ks - VREG][key][lane half]; the
 // registers do not hold all eight) and the list page
 constexpr int DKDV_VREG = 6;
-template <int KS>
+// dS tile of the atomic-dQ variant: per row group, [key][32 rows] bf16 rows of
+// 64 B padded to 72 B (an odd number of 8-byte bank pairs, so the 64 lanes'
+// 8-byte writes of one step and the transposed reads spread over the banks)
+constexpr int DS_ROW = 72;
+constexpr int DS_BYTES = 256 * DS_ROW;  // RG * KW = 256 (key, row group) rows
+template <int KS, bool AQ = false>
 struct DkdvLds {
-  using S = DkdvShape<KS>;
+  using S = DkdvShape<KS, AQ>;
   static constexpr int KT = (S::NST * S::STAGE + 1023) / 1024 * 1024;
   static constexpr int VX = KT + S::KW * HD * 2;
   static constexpr int LST = VX + (8 - DKDV_VREG) * S::KW * 2 * 16;
-  static constexpr int BYTES = LST + 2 * DKDV_LIST_CAP * 4;  // Q blocks | their live extents
+  static constexpr int DSB = LST + 2 * DKDV_LIST_CAP * 4;  // Q blocks | their live extents
+  static constexpr int CROW = DSB + (AQ ? DS_BYTES : 0);    // row-0 offset of each slot's chunk
+  static constexpr int BYTES = CROW + (AQ ? 8 * S::NST : 0);
 };
 constexpr int imax(int x, int y) { return x > y ? x : y; }
 constexpr int DKDV_LDS = imax(DkdvLds<8>::BYTES, imax(DkdvLds<4>::BYTES, DkdvLds<2>::BYTES));
-static_assert(DKDV_LDS <= 160 * 1024, "dK/dV LDS budget");
+// the atomic-dQ variant runs spans of up to 128 live keys in the 128-key shape
+constexpr int DKDV_LDS_AQ = imax(DkdvLds<8, true>::BYTES, DkdvLds<4, true>::BYTES);
+static_assert(DKDV_LDS <= 160 * 1024 && DKDV_LDS_AQ <= 160 * 1024, "dK/dV LDS budget");
 
-// dK / dV of keys k0 .. kend-1 of KV block j (live keys: the first `live`)
-template <class ET, int KS>
+// Transposed A operand of dQ = dS K read from the dS tile ([key][row], 72-byte
+// rows): M index = row (lane % 32), contraction over keys kb .. kb+15 in the
+// k-slot order of TrOffs (so it pairs with TrOffs reads of the K tile).
+struct DsTr {
+  uint32_t o[2];
+  __device__ __forceinline__ explicit DsTr(int lane) {
+    const TrLane t(lane);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) o[hi] = (t.row_off + 8 * hi) * DS_ROW + t.c_off * 16 + t.half;
+  }
+  __device__ __forceinline__ uint4 at(const uint8_t* tile, int kb) const {
+    const uint2 lo = tr8(tile, (uint32_t)(kb * DS_ROW) + o[0]);
+    const uint2 hi = tr8(tile, (uint32_t)(kb * DS_ROW) + o[1]);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+};
+
+// dK / dV of keys k0 .. kend-1 of KV block j (live keys: the first `live`);
+// AQ: also dQ += dS K of every chunk, added to a.dqacc with atomics
+template <class ET, int KS, bool AQ>
 __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b, int hk, int j,
                                           int k0, int kend, int nval, int live) {
   using E = Elem<ET>;
-  using S = DkdvShape<KS>;
-  using L = DkdvLds<KS>;
+  using S = DkdvShape<KS, AQ>;
+  using L = DkdvLds<KS, AQ>;
   constexpr int NW = S::NW, RG = S::RG, QC = S::QC, QT = S::QT, STAGE = S::STAGE, KW = S::KW;
   constexpr int NST = S::NST, LPC = S::LPC, LPC_ROWS = S::LPC_ROWS, VREG = DKDV_VREG;
   uint8_t* const ring = smem;  // slot s at ring + s * STAGE
@@ -214,6 +244,8 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
   uint4* const Vx = reinterpret_cast<uint4*>(smem + L::VX);
   int* const lst_i = reinterpret_cast<int*>(smem + L::LST);
   int* const lst_e = lst_i + DKDV_LIST_CAP;
+  uint8_t* const dsb = smem + L::DSB;                          // AQ: the chunk's dS
+  long long* const crow = reinterpret_cast<long long*>(smem + L::CROW);  // AQ
 
   const Geom& g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -326,6 +358,7 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       const int last = min(left, QC) - 1;  // rows past it repeat it
       slots |= (uint32_t)(last + 1) << (8 * s);
       uint8_t* st = ring + s * STAGE;
+      if (AQ && tid == 0) crow[s] = cq;
       stage_rows<QC, NW>(st, wave, lane, a.q + cq, qrs_bytes, last);
       stage_rows<QC, NW>(st + QT, wave, lane, a.dout + cq, qrs_bytes, last);
       // the row group's 32 rows of lse2 and dr, loaded by its first wave; rows
@@ -399,8 +432,17 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
         const int o = 8 * kt;
         const uint4 pp = make_uint4(E::pack(sv[o], sv[o + 1]), E::pack(sv[o + 2], sv[o + 3]),
                                     E::pack(sv[o + 4], sv[o + 5]), E::pack(sv[o + 6], sv[o + 7]));
-        const uint4 ps = make_uint4(E::pack(dp[o], dp[o + 1]), E::pack(dp[o + 2], dp[o + 3]),
-                                    E::pack(dp[o + 4], dp[o + 5]), E::pack(dp[o + 6], dp[o + 7]));
+        uint4 ps = make_uint4(E::pack(dp[o], dp[o + 1]), E::pack(dp[o + 2], dp[o + 3]),
+                              E::pack(dp[o + 4], dp[o + 5]), E::pack(dp[o + 6], dp[o + 7]));
+        if constexpr (AQ) {
+          // dQ contracts over keys, so a key past the live ones must add
+          // nothing there (its own dK column is dropped anyway); the tile
+          // stores this wave's 32 keys x 32 rows transposed ([key][row])
+          if (!key_live) ps = make_uint4(0, 0, 0, 0);
+          uint8_t* dsw = dsb + (rg * KW + 32 * kslot + (lane & 31)) * DS_ROW + 32 * kt + 8 * hl;
+          *reinterpret_cast<uint2*>(dsw) = make_uint2(ps.x, ps.y);
+          *reinterpret_cast<uint2*>(dsw + 16) = make_uint2(ps.z, ps.w);
+        }
         uint4 nv = to.at(Ds, rb + 16 * kt, 0), nk = to.at(Qs, rb + 16 * kt, 0);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -416,6 +458,70 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
     };
     // does this wave have work in a chunk with `rows` valid rows
     auto busy = [&](int rows) { return wave_keys && rows > rb; };
+
+    // AQ, after every wave wrote its dS: this wave's 32-row x 32-d block of the
+    // chunk's dQ = dS K (row block qb, d block db, keys k_lo .. of the span's
+    // live keys), added to the float accumulator. 256-key spans: two waves per
+    // block, one per half of the keys; 128-key spans: one wave per block.
+    const int qrb = KS == 8 ? 0 : (wave >> 2), qdb = wave & 3;
+    const int k_lo = KS == 8 ? 128 * (wave >> 2) : 0;
+    const int k_hi = min(k_lo + (KS == 8 ? 128 : KW), live);
+    const uint32_t qrs4 = (uint32_t)(qrs * 4);
+    auto dq_part = [&](int rows_valid, long long r0) {
+      if (rows_valid <= 32 * qrb || k_lo >= k_hi) return;
+      // The lane offsets below are rebuilt here from an opaque copy of the lane
+      // id rather than kept live over the walk: the walk's registers are full,
+      // and a spilled value reloaded in the fill would wait for every load in
+      // flight.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const DsTr dtr(ln);
+      // transposed reads of the K tile for this wave's d block (TrOffs at
+      // mb = qdb, computed for that block alone: a runtime index into TrOffs
+      // would put its table in scratch memory)
+      uint32_t kto[2];
+      {
+        const TrLane t(ln);
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+          kto[hi] = toff((int)t.row_off + 8 * hi, 4 * qdb + t.c_off) + t.half;
+      }
+      auto kt_at = [&](int kb) {
+        const uint2 lo = tr8(Kt, (uint32_t)(kb * 256) + kto[0]);
+        const uint2 hi = tr8(Kt, (uint32_t)(kb * 256) + kto[1]);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
+      const uint8_t* dt = dsb + qrb * KW * DS_ROW;
+      f32x16_t qa;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) qa[r] = 0.f;
+      // one key step of 16 at a time, the next step's operands read ahead
+      uint4 na = dtr.at(dt, k_lo), nb = kt_at(k_lo);
+#pragma nounroll
+      for (int kb = k_lo; kb < k_hi; kb += 16) {
+        const uint4 ca = na, cb = nb;
+        if (kb + 16 < k_hi) {
+          na = dtr.at(dt, kb + 16);
+          nb = kt_at(kb + 16);
+        }
+        qa = E::mfma(ca, cb, qa);
+      }
+      // lane: d = 32 qdb + lane % 32; register r: row 32 qrb + 8(r/4) + 4hl + r%4.
+      // The address is a uniform base (the chunk's row 0 plus the register's
+      // row step) and the lane's 32-bit offset, so no per-row address stays live.
+      const int vrow = 32 * qrb + 4 * (ln >> 5);  // the lane's first row
+      // byte offset of (row vrow, d = 32 qdb + lane % 32) from the chunk's row 0
+      const uint32_t aq_lane = (uint32_t)vrow * qrs4 + 4u * (uint32_t)(32 * qdb + (ln & 31));
+      const char* base = reinterpret_cast<const char*>(uniform_ptr(a.dqacc + r0));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int step = 8 * (r >> 2) + (r & 3);
+        if (vrow + step < rows_valid) {
+          const char* rb_ptr = base + (uint32_t)step * qrs4;
+          unsafeAtomicAdd((float*)(rb_ptr + aq_lane), qa[r]);
+        }
+      }
+    };
     // the chunk of slot s1 must have landed; the chunks loaded after it may
     // stay in flight
     auto wait_chunk = [&](int s1) {  // s1: slot of chunk n + 1
@@ -436,6 +542,10 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
         fill(s == 0 ? NST - 1 : s - 1);  // the slot freed by the previous step
         const int rows = rem_of(s);
         if (busy(rows)) compute(ring + s * STAGE, rows);
+        if constexpr (AQ) {
+          lds_barrier();  // the chunk's dS tile is complete
+          dq_part(rows, crow[s]);
+        }
         s = next(s);
         wait_chunk(s);
         lds_barrier();
@@ -519,9 +629,9 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
 // One launch for all three shapes: each work-group picks its span's shape, so
 // the memory-bound 64-key spans of partial tiles run next to the MFMA-bound
 // 256-key spans instead of after them.
-template <class ET>
+template <class ET, bool AQ>
 __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[DKDV_LDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[AQ ? DKDV_LDS_AQ : DKDV_LDS];
   const Geom& g = a.g;
   const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
   int id = xcd_group(blockIdx.x, gridDim.x, nspan);
@@ -536,9 +646,48 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
   const int nval = g.kv_val(b, j);
   const int live = max(0, min(kend, nval) - k0);  // live keys of the span
   const int shape = dkdv_shape(live);
-  if (shape == 8) dkdv_span<ET, 8>(a, smem, b, hk, j, k0, kend, nval, live);
-  else if (shape == 4) dkdv_span<ET, 4>(a, smem, b, hk, j, k0, kend, nval, live);
-  else dkdv_span<ET, 2>(a, smem, b, hk, j, k0, kend, nval, live);
+  if (shape == 8) dkdv_span<ET, 8, AQ>(a, smem, b, hk, j, k0, kend, nval, live);
+  else if (AQ || shape == 4) dkdv_span<ET, 4, AQ>(a, smem, b, hk, j, k0, kend, nval, live);
+  else dkdv_span<ET, 2, false>(a, smem, b, hk, j, k0, kend, nval, live);
+}
+
+// dq = scale * (the atomically accumulated dS K) + the unpooled compression
+// term on valid slots; one work-group per (b, h, Q block), 16 lanes per row.
+template <class ET>
+__global__ __launch_bounds__(256) void dq_cast_kernel(const BwdArgs a) {
+  using E = Elem<ET>;
+  const Geom& g = a.g;
+  int id = blockIdx.x;
+  const int i = id % g.Qb;
+  id /= g.Qb;
+  const int h = id % g.Hq, b = id / g.Hq;
+  const int qlen = g.q_len(b), blk0 = i * g.q_block;
+  if (blk0 >= qlen) return;
+  const int qexist = min(g.q_block, qlen - blk0);
+  const int tid = threadIdx.x, slot = tid >> 4, dg = tid & 15;
+  const long long qrs = g.q_rs(), qb = g.q_base(b, h);
+  const int nq = a.dqc ? g.q_val(b, i) : 0;
+  float cterm[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) cterm[u] = 0.f;
+  if (nq > 0) {
+    const float* c = a.dqc + g.pq(b, h, i) + 8 * dg;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cterm[u] = c[u] / (float)nq;
+  }
+  for (int s = slot; s < qexist; s += 16) {
+    const long long off = qb + (long long)(blk0 + s) * qrs + 8 * dg;
+    const float4 x0 = *reinterpret_cast<const float4*>(a.dqacc + off);
+    const float4 x1 = *reinterpret_cast<const float4*>(a.dqacc + off + 4);
+    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const bool valid = s < nq;
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = E::pack(g.scale * x[2 * u] + (valid ? cterm[2 * u] : 0.f),
+                     g.scale * x[2 * u + 1] + (valid ? cterm[2 * u + 1] : 0.f));
+    stg16(a.dq + off, make_uint4(w[0], w[1], w[2], w[3]));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -694,7 +843,16 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const long long n = (long long)g.B * g.Hkv * g.KVb * ((g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN);
   if (n == 0) return hipSuccess;
-  sparse_dkdv_kernel<ET><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
+  if (a.dqacc) sparse_dkdv_kernel<ET, true><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
+  else sparse_dkdv_kernel<ET, false><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <class ET>
+hipError_t launch_dq_cast_t(const BwdArgs& a, hipStream_t st) {
+  const long long n = (long long)a.g.B * a.g.Hq * a.g.Qb;
+  if (n == 0) return hipSuccess;
+  dq_cast_kernel<ET><<<(unsigned)n, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -721,6 +879,9 @@ hipError_t launch_sparse_dkdv(const BwdArgs& a, int dtype, hipStream_t st) {
 }
 hipError_t launch_sparse_dq(const BwdArgs& a, int dtype, hipStream_t st) {
   return dtype == VSA_BF16 ? launch_dq_t<bf16_tag>(a, st) : launch_dq_t<f16_tag>(a, st);
+}
+hipError_t launch_dq_cast(const BwdArgs& a, int dtype, hipStream_t st) {
+  return dtype == VSA_BF16 ? launch_dq_cast_t<bf16_tag>(a, st) : launch_dq_cast_t<f16_tag>(a, st);
 }
 
 }  // namespace vsa

@@ -41,6 +41,9 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
+  // atomic-dQ backward: float accumulator laid out like q (zeroed before the
+  // dK/dV launch, which adds dS K into it); null for the two-kernel backward
+  float* dqacc;
 };
 
 // Row term and gate-side reductions of the backward.
@@ -89,6 +92,7 @@ hipError_t launch_sparse_fwd(const FwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_bwd_pre(const PreArgs& a, int dtype, hipStream_t st);
 hipError_t launch_sparse_dkdv(const BwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_sparse_dq(const BwdArgs& a, int dtype, hipStream_t st);
+hipError_t launch_dq_cast(const BwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace vsa

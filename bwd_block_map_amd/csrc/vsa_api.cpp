@@ -181,6 +181,7 @@ struct BwdWs {
   float* dr;
   float* lse2;
   int32_t* qlive;
+  float* dqacc;  // VSA_FLAG_ATOMIC_DQ: dS K summed over KV blocks, laid out like q
   float* doc;
   float* dqc;
   float* dkc;
@@ -195,6 +196,7 @@ BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
   w.dr = c.take<float>(std::max(rows_total(p), 1LL));
   w.lse2 = c.take<float>(std::max(rows_total(p), 1LL));
   w.qlive = c.take<int32_t>(std::max((long long)p->B * p->Hq * p->Qb, 1LL));
+  if (p->flags & VSA_FLAG_ATOMIC_DQ) w.dqacc = c.take<float>(std::max(q_elems(p), 1LL));
   if (p->gate_mode != VSA_GATE_NONE) {
     w.doc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
     w.dqc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
@@ -258,6 +260,8 @@ int validate(const vsa_problem* p) {
   if (p->gate_mode < VSA_GATE_NONE || p->gate_mode > VSA_GATE_PER_ELEMENT)
     return fail(VSA_ERR_INVALID_ARG, "gate_mode must be NONE, PER_TOKEN or PER_ELEMENT");
   if (p->map_batch_stride < 0) return fail(VSA_ERR_INVALID_ARG, "map_batch_stride must be >= 0");
+  if (p->flags & ~VSA_FLAG_ATOMIC_DQ)
+    return fail(VSA_ERR_INVALID_ARG, "flags: unknown bits 0x%x", p->flags & ~VSA_FLAG_ATOMIC_DQ);
   if (p->layout == VSA_TND) {
     if (!p->cu_seqlens_q) return fail(VSA_ERR_INVALID_ARG, "actual_seq_lengths must be specified");
     if (!p->cu_seqlens_kv)
@@ -644,11 +648,24 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   ba.dv = (uint16_t*)dv;
   ba.row_ptr = s.kv_rp;
   ba.col = s.kv_col;
+  const bool atomic_dq = (p->flags & VSA_FLAG_ATOMIC_DQ) != 0;
+  ba.dqacc = atomic_dq ? w.dqacc : nullptr;
+  if (atomic_dq) {  // the accumulator starts at zero (a fill kernel: safe under graph capture)
+    Prof pr(VSA_KERNEL_DQ_ATOMIC, st);
+    e = vsa::launch_zero(w.dqacc, (size_t)qn * sizeof(float), st);
+    if (e != hipSuccess) return hip_fail(e, "dQ accumulator clear");
+  }
   {
     Prof pr(VSA_KERNEL_SPARSE_DKDV, st);
     e = vsa::launch_sparse_dkdv(ba, p->dtype, st);
   }
   if (e != hipSuccess) return hip_fail(e, "dK/dV");
+  if (atomic_dq) {
+    Prof pr(VSA_KERNEL_DQ_ATOMIC, st);
+    e = vsa::launch_dq_cast(ba, p->dtype, st);
+    if (e != hipSuccess) return hip_fail(e, "dQ cast");
+    return ok();
+  }
   ba.row_ptr = s.q_rp;
   ba.col = s.q_col;
   {

@@ -79,13 +79,17 @@ class Spec:
     scale: Optional[float] = None
     q_valid: Optional[torch.Tensor] = None
     kv_valid: Optional[torch.Tensor] = None
+    # False: the backward adds dQ inside the KV-owned pass with float atomics
+    # (faster or not, per workload; dq then varies in its last bits run to run)
+    deterministic: bool = True
 
     def problem(self, q, k, gate):
         B, Hq, Hkv, Sq, Skv, D = dims(q, k, self.layout)
         return make_problem(dtype=q.dtype, layout=self.layout, B=B, Hq=Hq, Hkv=Hkv, Sq=Sq,
                             Skv=Skv, D=D, q_block=self.q_block, kv_block=self.kv_block,
                             q_valid=self.q_valid, kv_valid=self.kv_valid, scale=self.scale,
-                            topk=self.topk, gate_mode=gate_mode_of(gate, q, self.layout))
+                            topk=self.topk, gate_mode=gate_mode_of(gate, q, self.layout),
+                            atomic_dq=not self.deterministic)
 
 
 def _contig(*ts):
@@ -142,8 +146,8 @@ def attention(q, k, v, spec: Spec, block_map: Optional[torch.Tensor] = None,
 
 def block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_map: torch.Tensor,
                       kv_valid: Counts = None, q_valid: Counts = None, *, layout: str = "bhsd",
-                      scale: Optional[float] = None,
-                      gate: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                      scale: Optional[float] = None, gate: Optional[torch.Tensor] = None,
+                      deterministic: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention restricted to a boolean [B, H, Qb, KVb] (or [H, Qb, KVb]) map
     of (Q block, KV block) pairs; block sizes are the sequence lengths over the
     map's extents. kv_valid / q_valid: valid tokens per KV / Q tile (padded
@@ -162,34 +166,39 @@ def block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_m
     if block_map.shape[0] != B:
         block_map = block_map.expand(B, -1, -1, -1)
     spec = Spec(layout=layout, q_block=Sq // Qb, kv_block=Skv // KVb, scale=scale,
-                q_valid=_counts(q_valid, q.device), kv_valid=_counts(kv_valid, q.device))
+                q_valid=_counts(q_valid, q.device), kv_valid=_counts(kv_valid, q.device),
+                deterministic=deterministic)
     out, lse = attention(q, k, v, spec, block_map=block_map, gate=gate)
     return out, lse.detach()
 
 
-def _video(q, k, v, kv_var, q_var, topk, block_size, gate, scale, layout):
+def _video(q, k, v, kv_var, q_var, topk, block_size, gate, scale, layout, deterministic):
     tile = 1
     for s in block_size:
         tile *= int(s)
     spec = Spec(layout=layout, q_block=tile, kv_block=tile, topk=int(topk), scale=scale,
-                q_valid=_counts(q_var, q.device), kv_valid=_counts(kv_var, q.device))
+                q_valid=_counts(q_var, q.device), kv_valid=_counts(kv_var, q.device),
+                deterministic=deterministic)
     return attention(q, k, v, spec, gate=gate)[0]
 
 
 def video_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_var: Counts,
                       q_var: Counts, topk: int, block_size: Sequence[int] = (4, 8, 8),
                       compress_attn_weight: Optional[torch.Tensor] = None,
-                      scale: Optional[float] = None) -> torch.Tensor:
+                      scale: Optional[float] = None, deterministic: bool = True) -> torch.Tensor:
     """Video sparse attention over [B, H, S, D] tensors laid out in tiles of
     prod(block_size) tokens: each Q tile attends to its `topk` KV tiles of
     highest pooled score (q_var / kv_var valid tokens per tile); with
     compress_attn_weight the gated pooled-tile branch is added. Returns out."""
-    return _video(q, k, v, kv_var, q_var, topk, block_size, compress_attn_weight, scale, "bhsd")
+    return _video(q, k, v, kv_var, q_var, topk, block_size, compress_attn_weight, scale, "bhsd",
+                  deterministic)
 
 
 def video_sparse_attn_bshd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_var: Counts,
                            q_var: Counts, topk: int, block_size: Sequence[int] = (4, 8, 8),
                            compress_attn_weight: Optional[torch.Tensor] = None,
-                           scale: Optional[float] = None) -> torch.Tensor:
+                           scale: Optional[float] = None,
+                           deterministic: bool = True) -> torch.Tensor:
     """video_sparse_attn for [B, S, H, D] tensors (the gate likewise in BSHD)."""
-    return _video(q, k, v, kv_var, q_var, topk, block_size, compress_attn_weight, scale, "bshd")
+    return _video(q, k, v, kv_var, q_var, topk, block_size, compress_attn_weight, scale, "bshd",
+                  deterministic)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 1
+#define VSA_ABI_VERSION 2
 
 enum vsa_status {
   VSA_OK = 0,
@@ -115,6 +115,18 @@ enum vsa_gate_mode {
  *                 tiles), broadcast to every slot of Q tile i.
  *   map_batch_stride  elements between batch entries of block_map;
  *                 0 = one [Hq, Qb, KVb] map shared by every batch entry
+ *   flags         0, or VSA_FLAG_ATOMIC_DQ: vsa_bwd computes dQ inside the
+ *                 KV-owned dK/dV pass (dS K of every selected block added to
+ *                 a float accumulator in the backward workspace with atomics,
+ *                 then scaled and cast) instead of in a second Q-owned pass
+ *                 that recomputes S and dP ([FV-cute] `_build_sparse_tensors`:
+ *                 the FA4 backward is KV-owned, one walk per KV tile over the
+ *                 query tiles that selected it, so its dQ comes out of that
+ *                 same walk). The float sums
+ *                 then depend on the order the atomics land in, so dq may
+ *                 differ between runs in the last bits; dk, dv and every
+ *                 forward output stay bit-reproducible. The default (0) is
+ *                 deterministic throughout.
  */
 typedef struct vsa_problem {
   int32_t abi_version;
@@ -134,7 +146,10 @@ typedef struct vsa_problem {
   int32_t topk;
   int32_t gate_mode;
   int64_t map_batch_stride;
+  int32_t flags;
 } vsa_problem;
+
+#define VSA_FLAG_ATOMIC_DQ 1
 
 /* Message of the last failed call on this thread ("" after a success). */
 const char* vsa_last_error(void);
@@ -268,7 +283,8 @@ enum vsa_kernel_id {
   VSA_KERNEL_COARSE_BWD = 5,  /* compression-branch backward          */
   VSA_KERNEL_SPARSE_DKDV = 6, /* KV-owned dK / dV                     */
   VSA_KERNEL_SPARSE_DQ = 7,   /* Q-owned dQ                           */
-  VSA_KERNEL_COUNT = 8
+  VSA_KERNEL_DQ_ATOMIC = 8,   /* atomic-dQ backward: accumulator clear and cast */
+  VSA_KERNEL_COUNT = 9
 };
 
 int vsa_profile_begin(void);

@@ -112,6 +112,47 @@ def test_fwd_bwd_parity_small(name, kw):
     _compare_case(case, res, orc)
 
 
+@pytest.mark.parametrize("name,kw", SMALL, ids=[f"{n}-{k.get('layout', '')}" for n, k in SMALL])
+def test_atomic_dq_parity_small(name, kw):
+    """The backward variant that adds dQ = dS K inside the KV-owned dK/dV walk
+    with float atomics (VSA_FLAG_ATOMIC_DQ), on every small case."""
+    case = make_case(name, **kw)
+    _say(f"[atomic dq {name} {kw}] B={case.B} Hq={case.Hq} Hkv={case.Hkv} Sq={case.Sq}")
+    res = run_case(case, atomic_dq=True)
+    orc = oracle.Oracle(case, np.float32)
+    if case.topk > 0:
+        assert _topk_agreement(orc, res["map"]).all(), "top-k near-tie in a small case"
+    _compare_case(case, res, orc)
+
+
+def test_atomic_dq_edge_cases():
+    """Atomic dQ on the cases that stress its masking: zero-q/zero-dO rows past
+    each block's live extent (61 and 199 valid rows, a tile without valid rows),
+    KV spans of 256, 100 and 64 live keys (the last two in the 128-key shape),
+    an empty KV tile, empty rows and block lists longer than one LDS page; the
+    gradient of a row with no live key must be zero."""
+    cases = [
+        build_case("aq_zero_rows", dtype="bf16", layout="bshd", B=1, Hq=2, Hkv=1, D=128,
+                   q_var=[61, 256, 199, 0], kv_var=[256, 100, 64, 256], map_kind="ones",
+                   seed=23),
+        build_case("aq_empty_kv", dtype="fp16", layout="bhsd", B=1, Hq=4, Hkv=2, D=128,
+                   q_var=[256, 130, 256], kv_var=[256, 0, 100, 0, 64], topk=4, map_kind="none",
+                   gate_mode="per_token", seed=37),
+        build_case("aq_empty_rows", dtype="bf16", B=1, Hq=2, Hkv=1, D=128, q_block=128,
+                   kv_block=128, Sq=384, Skv=512, map_kind="custom",
+                   map_fn=lambda c: torch.tensor([[[[1, 0, 1, 0], [0, 0, 0, 0], [0, 1, 0, 0]],
+                                                   [[0, 0, 0, 0], [1, 1, 0, 0], [1, 0, 0, 0]]]])),
+        build_case("aq_long_kv_list", dtype="bf16", layout="bhsd", B=1, Hq=2, Hkv=1, D=128,
+                   q_block=256, kv_block=64, Sq=256, Skv=64 * 1040, map_kind="ones", seed=23),
+    ]
+    for case in cases:
+        _say(f"[{case.name}]")
+        res = run_case(case, atomic_dq=True)
+        _compare_case(case, res, oracle.Oracle(case, np.float32))
+        if case.name == "aq_empty_rows":  # head 0, Q block 1 selects nothing
+            assert np.all(res["dq"][0, 0, 128:256] == 0)
+
+
 def _index_cases():
     for n in ("c1_vsa256_tiny", "c2_bnsd_mha", "c3_tnd_gqa", "c3_tnd_gqa_page", "p3_tnd_uneven",
               "p3_bnsd_sparse32", "p3_tnd_tail64", "p3_bnsd_q8", "p3_tnd_q8"):

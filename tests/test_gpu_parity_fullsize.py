@@ -66,10 +66,10 @@ def _rows_of(case, res_map_same, rng, n):
     return np.array(rows, np.int32)
 
 
-def _fullsize(name, heads, nrows):
+def _fullsize(name, heads, nrows, atomic_dq=False):
     case = make_case(name, device="cuda")
-    _say(f"[{name}] running fwd+bwd on the GPU")
-    res = run_case(case, keep_device=True)
+    _say(f"[{name}] running fwd+bwd on the GPU ({'atomic' if atomic_dq else 'two-pass'} dQ)")
+    res = run_case(case, keep_device=True, atomic_dq=atomic_dq)
     gmap = res["map"].cpu().numpy()
 
     # (d) identities over all heads (test-side float64 reductions of the inputs)
@@ -87,15 +87,17 @@ def _fullsize(name, heads, nrows):
     assert float(err.max()) < 2e-3, f"sum dv != sum dO: {float(err.max()):.2e}"
     _say(f"  identities ok (max rel {float(err.max()):.1e})")
 
-    # (a) the selection of every head, a few heads at a time (pooled q/k only)
+    # (a) the selection of every head, a few heads at a time (pooled q/k only);
+    # the forward is the same for both backward variants, so checked once
     near = 0
-    for h0 in range(0, case.Hq, 8):
+    for h0 in range(0, case.Hq if not atomic_dq else 0, 8):
         hs = list(range(h0, min(case.Hq, h0 + 8)))
         part = dataclasses.replace(_heads_subcase(case, hs), gate_mode="none", gate=None)
         po = oracle.Oracle(part, np.float32, threads=16,
                            tensors=dict(q=part.q, k=part.k, v=part.v, dout=None, gate=None))
         near += int((~_topk_agreement(po, gmap[:, hs])).sum())
-    _say(f"  top-k of all {case.Hq} heads valid ({near} rows are near-ties)")
+    if not atomic_dq:
+        _say(f"  top-k of all {case.Hq} heads valid ({near} rows are near-ties)")
 
     sub = _heads_subcase(case, heads)
     orc = oracle.Oracle(sub, np.float32, threads=16)
@@ -145,3 +147,8 @@ def test_c4_video_full_size():
 
 def test_c5_720p_gate_full_size():
     _fullsize("c5_vsa256_720p_gate", heads=[3, 21, 38], nrows=384)
+
+
+def test_c5_720p_gate_full_size_atomic_dq():
+    """The same checks on the backward that adds dQ inside the dK/dV walk."""
+    _fullsize("c5_vsa256_720p_gate", heads=[3, 21, 38], nrows=384, atomic_dq=True)
