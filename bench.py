@@ -201,12 +201,13 @@ STAGE_KERNELS = {"sparse_fwd": "sparse_fwd_kernel", "sparse_dkdv": "sparse_dkdv_
 
 
 def kernel_source_hash():
-    """sha256 over the kernel sources: a traffic figure is only reported for
-    the kernels it was measured on."""
+    """sha256 over the device sources (.hip kernels and their headers; the
+    host-side C ABI is left out): a traffic figure is only reported for the
+    kernels it was measured on."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
+        if name.endswith((".hip", ".hpp")):
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()

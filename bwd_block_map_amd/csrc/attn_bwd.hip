@@ -741,14 +741,6 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
   const int e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[rid]);  // uniform: the walk stays scalar
   const int cnt = __builtin_amdgcn_readfirstlane(a.row_ptr[rid + 1]) - e0;
 
-  // A wave whose query rows are all zero (the padded slots of partial video
-  // tiles) has S = 0 exactly for finite K: it skips the score MFMAs and runs
-  // the rest of the step on S = 0, which gives the same P and dS bit for bit.
-  uint32_t nzq = 0;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) nzq |= (qr[ks].x | qr[ks].y | qr[ks].z | qr[ks].w) & 0x7fff7fffu;
-  const bool zq = __ballot(nzq != 0) == 0ull;
-
   // Rows past the block's live extent have q = 0 and dO = 0 (the padded slots
   // of partial video tiles, where callers pass a zero gradient), so dS = 0: a
   // wave made only of them skips the walk's arithmetic (its dq rows are the
@@ -768,15 +760,10 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
       f32x16_t sv, pv;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = pv[r] = 0.f;
-      if (zq) {  // all-zero query rows: S = 0
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          sv = E::mfma(ro.at(Ks, 32 * hf, ks), qr[ks], sv);
-          pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
-        }
+      for (int ks = 0; ks < 8; ++ks) {
+        sv = E::mfma(ro.at(Ks, 32 * hf, ks), qr[ks], sv);
+        pv = E::mfma(ro.at(Vs, 32 * hf, ks), dor[ks], pv);
       }
       // lane holds keys 32hf + 8(r/4) + 4hl + (r%4) of its row; keys past the
       // valid ones get P = 0 through a -inf exponent
