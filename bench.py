@@ -406,6 +406,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--atomic-dq", action="store_true",
                     help="time the backward that adds dQ inside the dK/dV pass with atomics")
+    ap.add_argument("--dkdv-grid", choices=("auto", "persistent", "span"), default="auto",
+                    help="dK/dV grid: the library's choice, the persistent longest-first grid, "
+                         "or one work-group per span")
     ap.add_argument("--dout-unpadded", action="store_true",
                     help="draw dO without zeroing the padded slots of partial tiles")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -456,7 +459,8 @@ def main():
         q_valid=d["q_valid"], kv_valid=d["kv_valid"], cu_seqlens_q=d["cu_q"],
         cu_seqlens_kv=d["cu_kv"], max_seqlen_q=max(case.q_lens) if case.q_lens else 0,
         max_seqlen_kv=max(case.kv_lens) if case.kv_lens else 0, scale=case.scale,
-        topk=case.topk, gate_mode=case.gate_mode, atomic_dq=args.atomic_dq)
+        topk=case.topk, gate_mode=case.gate_mode, atomic_dq=args.atomic_dq,
+        persistent_bwd={"auto": None, "persistent": True, "span": False}[args.dkdv_grid])
     buf = vsa.Buffers(p, d["q"], training=True)
     bmap = d["map"] if case.topk == 0 else buf.map
     dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
@@ -533,7 +537,10 @@ def main():
                    "gate": case.gate_mode, "tokens_valid": int(np.sum(case.q_var))
                    if case.q_var is not None else case.Sq,
                    "dout": "unpadded" if args.dout_unpadded else "zero in padded slots",
-                   "dq": "atomic in the dK/dV pass" if args.atomic_dq else "separate Q-owned pass"},
+                   "dq": "atomic in the dK/dV pass" if args.atomic_dq else "separate Q-owned pass",
+                   "dkdv_grid": {"auto": "library's choice (persistent at >= 8 spans per CU)",
+                                 "persistent": "persistent, longest first",
+                                 "span": "one work-group per span"}[args.dkdv_grid]},
         "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
         "fwd_ms_min": round(float(min(fwd_all)), 3), "bwd_ms_min": round(float(min(bwd_all)), 3),
         "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2),

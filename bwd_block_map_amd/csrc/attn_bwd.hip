@@ -232,8 +232,8 @@ struct DsTr {
 // dK / dV of keys k0 .. kend-1 of KV block j (live keys: the first `live`);
 // AQ: also dQ += dS K of every chunk, added to a.dqacc with atomics
 template <class ET, int KS, bool AQ>
-__device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b, int hk, int j,
-                                          int k0, int kend, int nval, int live) {
+__device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int tid, int b, int hk,
+                                          int j, int k0, int kend, int nval, int live) {
   using E = Elem<ET>;
   using S = DkdvShape<KS, AQ>;
   using L = DkdvLds<KS, AQ>;
@@ -248,7 +248,7 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
   long long* const crow = reinterpret_cast<long long*>(smem + L::CROW);  // AQ
 
   const Geom& g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level values stay scalar
   const int hl = lane >> 5;
   const int kslot = wave % KS, rg = wave / KS;
@@ -362,8 +362,12 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
       stage_rows<QC, NW>(st, wave, lane, a.q + cq, qrs_bytes, last);
       stage_rows<QC, NW>(st + QT, wave, lane, a.dout + cq, qrs_bytes, last);
       // the row group's 32 rows of lse2 and dr, loaded by its first wave; rows
-      // past the chunk's last repeat it, so no load leaves the block
-      const uint32_t loff = 4u * (uint32_t)min(rb + lane, last);
+      // past the chunk's last repeat it, so no load leaves the block (the lane
+      // offset is rebuilt here: kept live over the walk it was spilled, and a
+      // reload in the fill waits for every load in flight)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const uint32_t loff = 4u * (uint32_t)min(rb + ln, last);
       const uint32_t lds_l = lds_addr(st + 2 * QT) + 4 * rb;
       if (kslot == 0 && lane < 32) {
         dma4(a.lse2 + cl, loff, lds_l);
@@ -626,15 +630,12 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int b
     }
 }
 
-// One launch for all three shapes: each work-group picks its span's shape, so
-// the memory-bound 64-key spans of partial tiles run next to the MFMA-bound
-// 256-key spans instead of after them.
+// One work item: the span `id` (span-minor order of (b, KV head, KV block,
+// span)), in the shape its live keys pick.
 template <class ET, bool AQ>
-__global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[AQ ? DKDV_LDS_AQ : DKDV_LDS];
+__device__ __forceinline__ void dkdv_item(const BwdArgs& a, uint8_t* smem, int tid, int id) {
   const Geom& g = a.g;
   const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
-  int id = xcd_group(blockIdx.x, gridDim.x, nspan);
   const int span = id % nspan;
   id /= nspan;
   const int j = id % g.KVb;
@@ -646,9 +647,88 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
   const int nval = g.kv_val(b, j);
   const int live = max(0, min(kend, nval) - k0);  // live keys of the span
   const int shape = dkdv_shape(live);
-  if (shape == 8) dkdv_span<ET, 8, AQ>(a, smem, b, hk, j, k0, kend, nval, live);
-  else if (AQ || shape == 4) dkdv_span<ET, 4, AQ>(a, smem, b, hk, j, k0, kend, nval, live);
-  else dkdv_span<ET, 2, false>(a, smem, b, hk, j, k0, kend, nval, live);
+  if (shape == 8) dkdv_span<ET, 8, AQ>(a, smem, tid, b, hk, j, k0, kend, nval, live);
+  else if (AQ || shape == 4) dkdv_span<ET, 4, AQ>(a, smem, tid, b, hk, j, k0, kend, nval, live);
+  else dkdv_span<ET, 2, false>(a, smem, tid, b, hk, j, k0, kend, nval, live);
+}
+
+// One launch for all three shapes: each work-group picks its span's shape, so
+// the memory-bound 64-key spans of partial tiles run next to the MFMA-bound
+// 256-key spans instead of after them.
+//   PERSIST = false: one work-group per span, in the XCD-aware order.
+//   PERSIST = true: a fixed grid (one work-group per CU); each work-group takes
+//   the next item of a.lpt_order (longest first within each KV head) from an
+//   atomic counter until the list is used up, so long spans start first and
+//   short ones fill the tail. Every wave of a work-group reads the same item
+//   and they leave the loop together.
+template <class ET, bool AQ, bool PERSIST>
+__global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[AQ ? DKDV_LDS_AQ : DKDV_LDS];
+  if constexpr (!PERSIST) {
+    const int nspan = (a.g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
+    dkdv_item<ET, AQ>(a, smem, threadIdx.x, xcd_group(blockIdx.x, gridDim.x, nspan));
+  } else {
+    __shared__ int next_item;
+    for (;;) {
+      __syncthreads();  // the previous item is done with the LDS
+      if (threadIdx.x == 0) next_item = atomicAdd(a.lpt_counter, 1);
+      __syncthreads();
+      const int it = next_item;
+      if (it >= a.n_items) break;
+      // an opaque copy of the thread id per item: values derived from the lane
+      // must not be hoisted out of the item loop (the three shapes' copies
+      // would then be live together and spill inside the chunk loop)
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      dkdv_item<ET, AQ>(a, smem, tid, a.lpt_order[it]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Longest-processing-time order of the dK/dV spans (persistent backward):
+// a span's work is estimated as (Q blocks that selected its KV block, over the
+// heads of the group) x (chunk steps per Q block of its shape: 8, 4 or 2), cut
+// into LPT_LEVELS levels; spans are ordered by KV head (b, hk) first, so the
+// grid still sweeps the heads in turn, then by decreasing work. A counting
+// sort: histogram, exclusive scan, scatter.
+// ---------------------------------------------------------------------------
+constexpr int LPT_LEVELS = 1024;
+
+__device__ __forceinline__ int lpt_bin(const BwdArgs& a, int id) {
+  const Geom& g = a.g;
+  const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
+  const int span = id % nspan;
+  int r = id / nspan;
+  const int j = r % g.KVb;
+  r /= g.KVb;
+  const int hk = r % g.Hkv, b = r / g.Hkv;
+  const int k0 = span * DKDV_SPAN;
+  const int kend = min(g.kv_exist(b, j), min(g.kv_block, k0 + DKDV_SPAN));
+  const int live = max(0, min(kend, g.kv_val(b, j)) - k0);
+  long long cnt = 0;
+  for (int hh = 0; hh < g.group; ++hh) {
+    const long long row = ((long long)b * g.Hq + hk * g.group + hh) * g.KVb + j;
+    cnt += a.row_ptr[row + 1] - a.row_ptr[row];
+  }
+  const int steps = dkdv_shape(live);  // 8, 4 or 2 chunk steps per Q block
+  const long long work = live > 0 ? cnt * steps : 0;
+  const long long wmax = (long long)g.group * g.Qb * 8;
+  const int level = (int)min<long long>(LPT_LEVELS - 1, work * (LPT_LEVELS - 1) / max(wmax, 1LL));
+  return (b * g.Hkv + hk) * LPT_LEVELS + (LPT_LEVELS - 1 - level);
+}
+
+// hist[bin + 1] counts the spans of each bin (hist zeroed before)
+__global__ __launch_bounds__(256) void lpt_count_kernel(const BwdArgs a, int32_t* hist) {
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id < a.n_items) atomicAdd(&hist[lpt_bin(a, id) + 1], 1);
+}
+
+// after the scan hist[bin] is the first position of the bin
+__global__ __launch_bounds__(256) void lpt_scatter_kernel(const BwdArgs a, int32_t* hist,
+                                                           int32_t* order) {
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id < a.n_items) order[atomicAdd(&hist[lpt_bin(a, id)], 1)] = id;
 }
 
 // dq = scale * (the atomically accumulated dS K) + the unpooled compression
@@ -828,10 +908,17 @@ hipError_t launch_pre_t(const PreArgs& a, hipStream_t st) {
 template <class ET>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
-  const long long n = (long long)g.B * g.Hkv * g.KVb * ((g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN);
+  const long long n = dkdv_items(g);
   if (n == 0) return hipSuccess;
-  if (a.dqacc) sparse_dkdv_kernel<ET, true><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
-  else sparse_dkdv_kernel<ET, false><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
+  if (a.lpt_order) {
+    const unsigned grid = (unsigned)(n < a.persist_grid ? n : a.persist_grid);
+    if (a.dqacc) sparse_dkdv_kernel<ET, true, true><<<grid, DKDV_NW * 64, 0, st>>>(a);
+    else sparse_dkdv_kernel<ET, false, true><<<grid, DKDV_NW * 64, 0, st>>>(a);
+  } else if (a.dqacc) {
+    sparse_dkdv_kernel<ET, true, false><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
+  } else {
+    sparse_dkdv_kernel<ET, false, false><<<(unsigned)n, DKDV_NW * 64, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -867,6 +954,22 @@ hipError_t launch_sparse_dkdv(const BwdArgs& a, int dtype, hipStream_t st) {
 hipError_t launch_sparse_dq(const BwdArgs& a, int dtype, hipStream_t st) {
   return dtype == VSA_BF16 ? launch_dq_t<bf16_tag>(a, st) : launch_dq_t<f16_tag>(a, st);
 }
+long long dkdv_items(const Geom& g) {
+  return (long long)g.B * g.Hkv * g.KVb * ((g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN);
+}
+long long lpt_hist_entries(const Geom& g) { return (long long)g.B * g.Hkv * LPT_LEVELS + 2; }
+
+hipError_t launch_lpt_order(const BwdArgs& a, int32_t* hist, int32_t* order, hipStream_t st) {
+  const long long n = a.n_items, nb = (long long)a.g.B * a.g.Hkv * LPT_LEVELS;
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  lpt_count_kernel<<<grid, 256, 0, st>>>(a, hist);
+  hipError_t e = launch_exclusive_scan(hist, nb, st);
+  if (e != hipSuccess) return e;
+  lpt_scatter_kernel<<<grid, 256, 0, st>>>(a, hist, order);
+  return hipGetLastError();
+}
+
 hipError_t launch_dq_cast(const BwdArgs& a, int dtype, hipStream_t st) {
   return dtype == VSA_BF16 ? launch_dq_cast_t<bf16_tag>(a, st) : launch_dq_cast_t<f16_tag>(a, st);
 }

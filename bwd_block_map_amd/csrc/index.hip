@@ -123,6 +123,12 @@ __global__ __launch_bounds__(1024) void index_scan(int32_t* __restrict__ row_ptr
   if (t == 0) row_ptr[0] = 0;
 }
 
+// a[1 .. n] holds counts; afterwards a[0] = 0 and a[r] = the sum of the first r
+hipError_t launch_exclusive_scan(int32_t* a, long long n, hipStream_t st) {
+  index_scan<<<1, 1024, 0, st>>>(a, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_index(const Geom& g, const uint8_t* map, int kv_owned, int32_t* row_ptr,
                         int32_t* col, long long cap, hipStream_t st) {
   const long long rows = (long long)g.B * g.Hq * (kv_owned ? g.KVb : g.Qb);

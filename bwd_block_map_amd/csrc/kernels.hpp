@@ -44,6 +44,13 @@ struct BwdArgs {
   // atomic-dQ backward: float accumulator laid out like q (zeroed before the
   // dK/dV launch, which adds dS K into it); null for the two-kernel backward
   float* dqacc;
+  // persistent dK/dV: the spans in longest-first order, the item counter
+  // (zeroed before the launch), the number of spans and the grid; lpt_order
+  // null for one work-group per span
+  const int32_t* lpt_order;
+  int32_t* lpt_counter;
+  int n_items;
+  int persist_grid;
 };
 
 // Row term and gate-side reductions of the backward.
@@ -93,6 +100,12 @@ hipError_t launch_bwd_pre(const PreArgs& a, int dtype, hipStream_t st);
 hipError_t launch_sparse_dkdv(const BwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_sparse_dq(const BwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_dq_cast(const BwdArgs& a, int dtype, hipStream_t st);
+long long dkdv_items(const Geom& g);        // dK/dV spans of a problem
+long long lpt_hist_entries(const Geom& g);  // int32 entries of the order's histogram
+// longest-first order of the dK/dV spans into `order` (a.n_items entries);
+// `hist` (lpt_hist_entries) must be zero
+hipError_t launch_lpt_order(const BwdArgs& a, int32_t* hist, int32_t* order, hipStream_t st);
+hipError_t launch_exclusive_scan(int32_t* a, long long n, hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace vsa

@@ -177,11 +177,15 @@ FwdWs carve_fwd(const vsa_problem* p, void* base, size_t* bytes) {
   return w;
 }
 
+vsa::Geom make_geom(const vsa_problem* p);
+
 struct BwdWs {
   float* dr;
   float* lse2;
   int32_t* qlive;
   float* dqacc;  // VSA_FLAG_ATOMIC_DQ: dS K summed over KV blocks, laid out like q
+  int32_t* lpt_hist;   // VSA_FLAG_PERSISTENT_BWD: sort histogram, then the item counter
+  int32_t* lpt_order;  // VSA_FLAG_PERSISTENT_BWD: the dK/dV spans, longest first
   float* doc;
   float* dqc;
   float* dkc;
@@ -197,6 +201,11 @@ BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
   w.lse2 = c.take<float>(std::max(rows_total(p), 1LL));
   w.qlive = c.take<int32_t>(std::max((long long)p->B * p->Hq * p->Qb, 1LL));
   if (p->flags & VSA_FLAG_ATOMIC_DQ) w.dqacc = c.take<float>(std::max(q_elems(p), 1LL));
+  if (!(p->flags & VSA_FLAG_SPAN_GRID_BWD)) {  // the persistent grid may be used
+    const vsa::Geom g = make_geom(p);
+    w.lpt_hist = c.take<int32_t>(vsa::lpt_hist_entries(g));
+    w.lpt_order = c.take<int32_t>(std::max(vsa::dkdv_items(g), 1LL));
+  }
   if (p->gate_mode != VSA_GATE_NONE) {
     w.doc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
     w.dqc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
@@ -260,8 +269,11 @@ int validate(const vsa_problem* p) {
   if (p->gate_mode < VSA_GATE_NONE || p->gate_mode > VSA_GATE_PER_ELEMENT)
     return fail(VSA_ERR_INVALID_ARG, "gate_mode must be NONE, PER_TOKEN or PER_ELEMENT");
   if (p->map_batch_stride < 0) return fail(VSA_ERR_INVALID_ARG, "map_batch_stride must be >= 0");
-  if (p->flags & ~VSA_FLAG_ATOMIC_DQ)
-    return fail(VSA_ERR_INVALID_ARG, "flags: unknown bits 0x%x", p->flags & ~VSA_FLAG_ATOMIC_DQ);
+  constexpr int kFlags = VSA_FLAG_ATOMIC_DQ | VSA_FLAG_PERSISTENT_BWD | VSA_FLAG_SPAN_GRID_BWD;
+  if (p->flags & ~kFlags)
+    return fail(VSA_ERR_INVALID_ARG, "flags: unknown bits 0x%x", p->flags & ~kFlags);
+  if ((p->flags & VSA_FLAG_PERSISTENT_BWD) && (p->flags & VSA_FLAG_SPAN_GRID_BWD))
+    return fail(VSA_ERR_INVALID_ARG, "flags: VSA_FLAG_PERSISTENT_BWD and VSA_FLAG_SPAN_GRID_BWD exclude each other");
   if (p->layout == VSA_TND) {
     if (!p->cu_seqlens_q) return fail(VSA_ERR_INVALID_ARG, "actual_seq_lengths must be specified");
     if (!p->cu_seqlens_kv)
@@ -431,6 +443,31 @@ int fwd_impl(const vsa_problem* p, const void* q, const void* k, const void* v, 
   }
   if (e != hipSuccess) return hip_fail(e, "sparse forward");
   return ok();
+}
+
+// Compute units of the device that owns `st` (cached per device).
+std::mutex g_cu_mu;
+int g_cu_count[64] = {};
+int compute_units(hipStream_t st, int* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (st) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(st, &sd);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= 64) return fail(VSA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_cu_mu);
+  if (!g_cu_count[dev]) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n < 1) return hip_fail(e, "compute unit count");
+    g_cu_count[dev] = n;
+  }
+  *out = g_cu_count[dev];
+  return VSA_OK;
 }
 
 // ---- scratch of the entry point that allocates nothing ----------------------
@@ -650,6 +687,25 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   ba.col = s.kv_col;
   const bool atomic_dq = (p->flags & VSA_FLAG_ATOMIC_DQ) != 0;
   ba.dqacc = atomic_dq ? w.dqacc : nullptr;
+  bool persistent = false;
+  int cus = 0;
+  if (!(p->flags & VSA_FLAG_SPAN_GRID_BWD)) {
+    rc = compute_units((hipStream_t)stream, &cus);
+    if (rc != VSA_OK) return rc;
+    persistent = (p->flags & VSA_FLAG_PERSISTENT_BWD) ||
+                 vsa::dkdv_items(g) >= (long long)VSA_PERSISTENT_MIN_SPANS_PER_CU * cus;
+  }
+  if (persistent) {  // longest-first list of the dK/dV spans
+    ba.n_items = (int)vsa::dkdv_items(g);
+    ba.persist_grid = cus;
+    const long long nh = vsa::lpt_hist_entries(g);
+    Prof pr(VSA_KERNEL_DKDV_ORDER, st);
+    e = vsa::launch_zero(w.lpt_hist, (size_t)nh * sizeof(int32_t), st);
+    if (e == hipSuccess) e = vsa::launch_lpt_order(ba, w.lpt_hist, w.lpt_order, st);
+    if (e != hipSuccess) return hip_fail(e, "dK/dV order");
+    ba.lpt_order = w.lpt_order;
+    ba.lpt_counter = w.lpt_hist + (nh - 1);
+  }
   if (atomic_dq) {  // the accumulator starts at zero (a fill kernel: safe under graph capture)
     Prof pr(VSA_KERNEL_DQ_ATOMIC, st);
     e = vsa::launch_zero(w.dqacc, (size_t)qn * sizeof(float), st);

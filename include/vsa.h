@@ -127,6 +127,8 @@ enum vsa_gate_mode {
  *                 differ between runs in the last bits; dk, dv and every
  *                 forward output stay bit-reproducible. The default (0) is
  *                 deterministic throughout.
+ *                 VSA_FLAG_PERSISTENT_BWD, VSA_FLAG_SPAN_GRID_BWD (either may
+ *                 be combined with it): see below.
  */
 typedef struct vsa_problem {
   int32_t abi_version;
@@ -150,6 +152,18 @@ typedef struct vsa_problem {
 } vsa_problem;
 
 #define VSA_FLAG_ATOMIC_DQ 1
+/* How vsa_bwd lays out its KV-owned dK/dV pass. Persistent: a grid of one
+ * work-group per compute unit that takes the KV spans from a device list in
+ * longest-processing-time order (work estimated from the KV-owned index;
+ * ordered by KV head first, then by decreasing work). Span grid: one
+ * work-group per span. Results are the same bit for bit either way. By
+ * default the library picks the persistent grid when the pass has at least
+ * VSA_PERSISTENT_MIN_SPANS_PER_CU spans per compute unit (the list is built
+ * by three extra small launches, which only pays off on large problems);
+ * these flags force one or the other (setting both is INVALID_ARG). */
+#define VSA_FLAG_PERSISTENT_BWD 2
+#define VSA_FLAG_SPAN_GRID_BWD 4
+#define VSA_PERSISTENT_MIN_SPANS_PER_CU 8
 
 /* Message of the last failed call on this thread ("" after a success). */
 const char* vsa_last_error(void);
@@ -284,7 +298,8 @@ enum vsa_kernel_id {
   VSA_KERNEL_SPARSE_DKDV = 6, /* KV-owned dK / dV                     */
   VSA_KERNEL_SPARSE_DQ = 7,   /* Q-owned dQ                           */
   VSA_KERNEL_DQ_ATOMIC = 8,   /* atomic-dQ backward: accumulator clear and cast */
-  VSA_KERNEL_COUNT = 9
+  VSA_KERNEL_DKDV_ORDER = 9,  /* persistent dK/dV grid: the longest-first span list */
+  VSA_KERNEL_COUNT = 10
 };
 
 int vsa_profile_begin(void);

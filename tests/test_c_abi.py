@@ -131,3 +131,21 @@ def test_noalloc_forward_refuses_a_workspace_beyond_its_scratch():
                                    C.c_size_t(0), None)
     assert rc == vsa.ERR_WORKSPACE
     assert "scratch" in vsa.vsa_last_error()
+
+
+def test_backward_flags_are_checked():
+    """Unknown flag bits, and the two dK/dV grid choices together, are
+    INVALID_ARG; each flag alone is accepted and only the persistent grid's
+    span list adds to the backward workspace."""
+    ok = [_prob(atomic_dq=a, persistent_bwd=pb) for a in (False, True) for pb in (None, True, False)]
+    for p in ok:
+        vsa.vsa_validate(p)
+    p = _prob()
+    p.struct.flags = vsa.FLAG_PERSISTENT_BWD | vsa.FLAG_SPAN_GRID_BWD
+    assert _code(p)[0] == vsa.ERR_INVALID_ARG
+    p.struct.flags = 64
+    assert _code(p)[0] == vsa.ERR_INVALID_ARG
+    auto, span = vsa.vsa_sizes(_prob())["ws_bwd"], vsa.vsa_sizes(_prob(persistent_bwd=False))["ws_bwd"]
+    assert auto > span
+    atomic = vsa.vsa_sizes(_prob(atomic_dq=True, persistent_bwd=False))["ws_bwd"]
+    assert atomic >= span + 768 * 2 * 128 * 4  # the float dQ accumulator
