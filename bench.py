@@ -406,9 +406,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--atomic-dq", action="store_true",
                     help="time the backward that adds dQ inside the dK/dV pass with atomics")
-    ap.add_argument("--dkdv-grid", choices=("auto", "persistent", "span"), default="auto",
-                    help="dK/dV grid: the library's choice, the persistent longest-first grid, "
-                         "or one work-group per span")
+    ap.add_argument("--grid", choices=("auto", "persistent", "per-item"), default="auto",
+                    help="grid of the dK/dV pass: the library's choice, the persistent "
+                         "longest-first grid, or one work-group per span")
     ap.add_argument("--dout-unpadded", action="store_true",
                     help="draw dO without zeroing the padded slots of partial tiles")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -460,7 +460,7 @@ def main():
         cu_seqlens_kv=d["cu_kv"], max_seqlen_q=max(case.q_lens) if case.q_lens else 0,
         max_seqlen_kv=max(case.kv_lens) if case.kv_lens else 0, scale=case.scale,
         topk=case.topk, gate_mode=case.gate_mode, atomic_dq=args.atomic_dq,
-        persistent_bwd={"auto": None, "persistent": True, "span": False}[args.dkdv_grid])
+        persistent={"auto": None, "persistent": True, "per-item": False}[args.grid])
     buf = vsa.Buffers(p, d["q"], training=True)
     bmap = d["map"] if case.topk == 0 else buf.map
     dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
@@ -540,7 +540,7 @@ def main():
                    "dq": "atomic in the dK/dV pass" if args.atomic_dq else "separate Q-owned pass",
                    "dkdv_grid": {"auto": "library's choice (persistent at >= 8 spans per CU)",
                                  "persistent": "persistent, longest first",
-                                 "span": "one work-group per span"}[args.dkdv_grid]},
+                                 "per-item": "one work-group per span"}[args.grid]},
         "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
         "fwd_ms_min": round(float(min(fwd_all)), 3), "bwd_ms_min": round(float(min(bwd_all)), 3),
         "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2),

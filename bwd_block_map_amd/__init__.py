@@ -29,8 +29,8 @@ GATE_NONE, GATE_PER_TOKEN, GATE_PER_ELEMENT = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 ABI_VERSION = 2
 FLAG_ATOMIC_DQ = 1
-FLAG_PERSISTENT_BWD = 2
-FLAG_SPAN_GRID_BWD = 4
+FLAG_PERSISTENT = 2
+FLAG_NO_PERSISTENT = 4
 
 EXPORTS = ("vsa_last_error", "vsa_abi_version", "vsa_validate", "vsa_sizes",
            "block_map_to_index", "vsa_fwd", "vsa_fwd_noalloc", "vsa_bwd", "vsa_profile_begin",
@@ -135,13 +135,13 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
                  cu_seqlens_kv: Optional[torch.Tensor] = None, max_seqlen_q: int = 0,
                  max_seqlen_kv: int = 0, scale: Optional[float] = None, topk: int = 0,
                  gate_mode: str = "none", map_batch_stride: Optional[int] = None,
-                 atomic_dq: bool = False, persistent_bwd: Optional[bool] = None) -> Problem:
+                 atomic_dq: bool = False, persistent: Optional[bool] = None) -> Problem:
     """Fill a vsa_problem. q_valid / kv_valid / cu_seqlens are int32 device tensors.
     atomic_dq selects the backward that adds dQ inside the KV-owned pass
-    (VSA_FLAG_ATOMIC_DQ). persistent_bwd: None lets the library choose the
+    (VSA_FLAG_ATOMIC_DQ). persistent: None lets the library choose the
     dK/dV grid, True forces the persistent longest-first grid
-    (VSA_FLAG_PERSISTENT_BWD), False one work-group per span
-    (VSA_FLAG_SPAN_GRID_BWD)."""
+    (VSA_FLAG_PERSISTENT), False one work-group per span
+    (VSA_FLAG_NO_PERSISTENT)."""
     lay = _LAYOUTS[layout]
     if lay == TND:
         Qb = -(-max_seqlen_q // q_block)
@@ -179,7 +179,7 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
         scale=1.0 / math.sqrt(D) if scale is None else float(scale), topk=topk,
         gate_mode=_GATES[gate_mode], map_batch_stride=map_batch_stride,
         flags=(FLAG_ATOMIC_DQ if atomic_dq else 0)
-        | {None: 0, True: FLAG_PERSISTENT_BWD, False: FLAG_SPAN_GRID_BWD}[persistent_bwd])
+        | {None: 0, True: FLAG_PERSISTENT, False: FLAG_NO_PERSISTENT}[persistent])
     return Problem(s, keep)
 
 

@@ -146,6 +146,8 @@ Saved carve_saved(const vsa_problem* p, void* base, size_t* bytes) {
 
 // Forward workspace: the inference-mode index and coarse state, the pooled
 // tiles and the selection map of the top-k path.
+int compute_units(hipStream_t st, int* out);
+
 struct FwdWs {
   int32_t* q_rp;
   int32_t* q_col;
@@ -184,8 +186,8 @@ struct BwdWs {
   float* lse2;
   int32_t* qlive;
   float* dqacc;  // VSA_FLAG_ATOMIC_DQ: dS K summed over KV blocks, laid out like q
-  int32_t* lpt_hist;   // VSA_FLAG_PERSISTENT_BWD: sort histogram, then the item counter
-  int32_t* lpt_order;  // VSA_FLAG_PERSISTENT_BWD: the dK/dV spans, longest first
+  int32_t* lpt_hist;   // VSA_FLAG_PERSISTENT: sort histogram, then the item counter
+  int32_t* lpt_order;  // VSA_FLAG_PERSISTENT: the dK/dV spans, longest first
   float* doc;
   float* dqc;
   float* dkc;
@@ -201,7 +203,7 @@ BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
   w.lse2 = c.take<float>(std::max(rows_total(p), 1LL));
   w.qlive = c.take<int32_t>(std::max((long long)p->B * p->Hq * p->Qb, 1LL));
   if (p->flags & VSA_FLAG_ATOMIC_DQ) w.dqacc = c.take<float>(std::max(q_elems(p), 1LL));
-  if (!(p->flags & VSA_FLAG_SPAN_GRID_BWD)) {  // the persistent grid may be used
+  if (!(p->flags & VSA_FLAG_NO_PERSISTENT)) {  // the persistent grid may be used
     const vsa::Geom g = make_geom(p);
     w.lpt_hist = c.take<int32_t>(vsa::lpt_hist_entries(g));
     w.lpt_order = c.take<int32_t>(std::max(vsa::dkdv_items(g), 1LL));
@@ -269,11 +271,11 @@ int validate(const vsa_problem* p) {
   if (p->gate_mode < VSA_GATE_NONE || p->gate_mode > VSA_GATE_PER_ELEMENT)
     return fail(VSA_ERR_INVALID_ARG, "gate_mode must be NONE, PER_TOKEN or PER_ELEMENT");
   if (p->map_batch_stride < 0) return fail(VSA_ERR_INVALID_ARG, "map_batch_stride must be >= 0");
-  constexpr int kFlags = VSA_FLAG_ATOMIC_DQ | VSA_FLAG_PERSISTENT_BWD | VSA_FLAG_SPAN_GRID_BWD;
+  constexpr int kFlags = VSA_FLAG_ATOMIC_DQ | VSA_FLAG_PERSISTENT | VSA_FLAG_NO_PERSISTENT;
   if (p->flags & ~kFlags)
     return fail(VSA_ERR_INVALID_ARG, "flags: unknown bits 0x%x", p->flags & ~kFlags);
-  if ((p->flags & VSA_FLAG_PERSISTENT_BWD) && (p->flags & VSA_FLAG_SPAN_GRID_BWD))
-    return fail(VSA_ERR_INVALID_ARG, "flags: VSA_FLAG_PERSISTENT_BWD and VSA_FLAG_SPAN_GRID_BWD exclude each other");
+  if ((p->flags & VSA_FLAG_PERSISTENT) && (p->flags & VSA_FLAG_NO_PERSISTENT))
+    return fail(VSA_ERR_INVALID_ARG, "flags: VSA_FLAG_PERSISTENT and VSA_FLAG_NO_PERSISTENT exclude each other");
   if (p->layout == VSA_TND) {
     if (!p->cu_seqlens_q) return fail(VSA_ERR_INVALID_ARG, "actual_seq_lengths must be specified");
     if (!p->cu_seqlens_kv)
@@ -689,10 +691,10 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   ba.dqacc = atomic_dq ? w.dqacc : nullptr;
   bool persistent = false;
   int cus = 0;
-  if (!(p->flags & VSA_FLAG_SPAN_GRID_BWD)) {
+  if (!(p->flags & VSA_FLAG_NO_PERSISTENT)) {
     rc = compute_units((hipStream_t)stream, &cus);
     if (rc != VSA_OK) return rc;
-    persistent = (p->flags & VSA_FLAG_PERSISTENT_BWD) ||
+    persistent = (p->flags & VSA_FLAG_PERSISTENT) ||
                  vsa::dkdv_items(g) >= (long long)VSA_PERSISTENT_MIN_SPANS_PER_CU * cus;
   }
   if (persistent) {  // longest-first list of the dK/dV spans

@@ -127,7 +127,7 @@ enum vsa_gate_mode {
  *                 differ between runs in the last bits; dk, dv and every
  *                 forward output stay bit-reproducible. The default (0) is
  *                 deterministic throughout.
- *                 VSA_FLAG_PERSISTENT_BWD, VSA_FLAG_SPAN_GRID_BWD (either may
+ *                 VSA_FLAG_PERSISTENT, VSA_FLAG_NO_PERSISTENT (either may
  *                 be combined with it): see below.
  */
 typedef struct vsa_problem {
@@ -152,17 +152,17 @@ typedef struct vsa_problem {
 } vsa_problem;
 
 #define VSA_FLAG_ATOMIC_DQ 1
-/* How vsa_bwd lays out its KV-owned dK/dV pass. Persistent: a grid of one
- * work-group per compute unit that takes the KV spans from a device list in
- * longest-processing-time order (work estimated from the KV-owned index;
- * ordered by KV head first, then by decreasing work). Span grid: one
+/* Grid of vsa_bwd's KV-owned dK/dV pass. Persistent: one work-group per
+ * compute unit, taking the KV spans from a device list in longest-processing-
+ * time order (work estimated from the KV-owned index; ordered by KV head
+ * first, then by decreasing work) until none is left. Otherwise: one
  * work-group per span. Results are the same bit for bit either way. By
- * default the library picks the persistent grid when the pass has at least
- * VSA_PERSISTENT_MIN_SPANS_PER_CU spans per compute unit (the list is built
- * by three extra small launches, which only pays off on large problems);
- * these flags force one or the other (setting both is INVALID_ARG). */
-#define VSA_FLAG_PERSISTENT_BWD 2
-#define VSA_FLAG_SPAN_GRID_BWD 4
+ * default the persistent grid is used when the pass has at least
+ * VSA_PERSISTENT_MIN_SPANS_PER_CU spans per compute unit (the list costs three
+ * small extra launches, which pay off only on large problems); these flags
+ * force one or the other (setting both is INVALID_ARG). */
+#define VSA_FLAG_PERSISTENT 2
+#define VSA_FLAG_NO_PERSISTENT 4
 #define VSA_PERSISTENT_MIN_SPANS_PER_CU 8
 
 /* Message of the last failed call on this thread ("" after a success). */

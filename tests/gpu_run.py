@@ -31,7 +31,7 @@ def device_inputs(case, device="cuda"):
     return d
 
 
-def problem_for(case, d, map_batch_stride=None, atomic_dq=False, persistent_bwd=None):
+def problem_for(case, d, map_batch_stride=None, atomic_dq=False, persistent=None):
     return vsa.make_problem(
         dtype=case.torch_dtype, layout=case.layout, B=case.B, Hq=case.Hq, Hkv=case.Hkv,
         Sq=case.Sq, Skv=case.Skv, D=case.D, q_block=case.q_block, kv_block=case.kv_block,
@@ -40,13 +40,13 @@ def problem_for(case, d, map_batch_stride=None, atomic_dq=False, persistent_bwd=
         max_seqlen_q=max(case.q_lens) if case.q_lens else 0,
         max_seqlen_kv=max(case.kv_lens) if case.kv_lens else 0,
         scale=case.scale, topk=case.topk, gate_mode=case.gate_mode,
-        map_batch_stride=map_batch_stride, atomic_dq=atomic_dq, persistent_bwd=persistent_bwd)
+        map_batch_stride=map_batch_stride, atomic_dq=atomic_dq, persistent=persistent)
 
 
 def run_case(case, training=True, backward=True, dout_none=False, device="cuda", d=None,
-             keep_device=False, atomic_dq=False, persistent_bwd=None):
+             keep_device=False, atomic_dq=False, persistent=None):
     d = device_inputs(case, device) if d is None else d
-    p = problem_for(case, d, atomic_dq=atomic_dq, persistent_bwd=persistent_bwd)
+    p = problem_for(case, d, atomic_dq=atomic_dq, persistent=persistent)
     buf = vsa.Buffers(p, d["q"], training=training or backward)
     bmap = d["map"] if case.topk == 0 else buf.map
     vsa.vsa_fwd(p, d["q"], d["k"], d["v"], bmap, d["gate"], buf.out, buf.lse,

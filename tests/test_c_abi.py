@@ -137,15 +137,15 @@ def test_backward_flags_are_checked():
     """Unknown flag bits, and the two dK/dV grid choices together, are
     INVALID_ARG; each flag alone is accepted and only the persistent grid's
     span list adds to the backward workspace."""
-    ok = [_prob(atomic_dq=a, persistent_bwd=pb) for a in (False, True) for pb in (None, True, False)]
+    ok = [_prob(atomic_dq=a, persistent=pb) for a in (False, True) for pb in (None, True, False)]
     for p in ok:
         vsa.vsa_validate(p)
     p = _prob()
-    p.struct.flags = vsa.FLAG_PERSISTENT_BWD | vsa.FLAG_SPAN_GRID_BWD
+    p.struct.flags = vsa.FLAG_PERSISTENT | vsa.FLAG_NO_PERSISTENT
     assert _code(p)[0] == vsa.ERR_INVALID_ARG
     p.struct.flags = 64
     assert _code(p)[0] == vsa.ERR_INVALID_ARG
-    auto, span = vsa.vsa_sizes(_prob())["ws_bwd"], vsa.vsa_sizes(_prob(persistent_bwd=False))["ws_bwd"]
+    auto, span = vsa.vsa_sizes(_prob())["ws_bwd"], vsa.vsa_sizes(_prob(persistent=False))["ws_bwd"]
     assert auto > span
-    atomic = vsa.vsa_sizes(_prob(atomic_dq=True, persistent_bwd=False))["ws_bwd"]
+    atomic = vsa.vsa_sizes(_prob(atomic_dq=True, persistent=False))["ws_bwd"]
     assert atomic >= span + 768 * 2 * 128 * 4  # the float dQ accumulator

@@ -153,12 +153,12 @@ def test_atomic_dq_edge_cases():
             assert np.all(res["dq"][0, 0, 128:256] == 0)
 
 
-def test_persistent_backward_is_bit_identical():
-    """The persistent, longest-first dK/dV grid (VSA_FLAG_PERSISTENT_BWD) gives
-    exactly the gradients of one work-group per span: every span is computed
-    by the same code whichever work-group takes it. Spans of all three shapes,
-    GQA, TND, empty tiles, skipped rows, the atomic-dQ combination and the two
-    video workloads at full size."""
+def test_persistent_dkdv_grid_is_bit_identical():
+    """The persistent, longest-first dK/dV grid (VSA_FLAG_PERSISTENT) gives
+    exactly the outputs and gradients of one work-group per span: every span
+    is computed by the same code whichever work-group takes it. Spans of all
+    three shapes, GQA, TND, empty tiles, skipped rows, the atomic-dQ
+    combination and the two video workloads at full size."""
     cases = [make_case(n, **kw) for n, kw in (("p1_gated", dict(layout="bshd")),
                                               ("p3_tnd_kv320", {}), ("c3_tnd_gqa", {}),
                                               ("c2_bnsd_mha", {}))]
@@ -168,25 +168,25 @@ def test_persistent_backward_is_bit_identical():
     for case in cases:
         d = device_inputs(case)
         for atomic in (False, True):  # each against the same variant with one group per span
-            ref = run_case(case, d=d, keep_device=True, atomic_dq=atomic, persistent_bwd=False)
-            got = run_case(case, d=d, keep_device=True, persistent_bwd=True, atomic_dq=atomic)
-            names = ("dk", "dv") if atomic else ("dq", "dk", "dv", "dgate")
+            ref = run_case(case, d=d, keep_device=True, atomic_dq=atomic, persistent=False)
+            got = run_case(case, d=d, keep_device=True, persistent=True, atomic_dq=atomic)
+            names = ("out", "lse", "dk", "dv") if atomic else ("out", "lse", "dq", "dk", "dv", "dgate")
             for n in names:
                 if ref[n] is not None:
                     assert torch.equal(ref[n], got[n]), (case.name, atomic, n)
             if atomic:  # dq differs only by the order of the float additions
                 a = metrics(ref["dq"].float().cpu().numpy(), got["dq"].float().cpu().numpy())
                 assert a[0] < 1e-4 and a[1] < 1e-2, (case.name, a)
-        _say(f"[{case.name}] persistent backward identical")
+        _say(f"[{case.name}] persistent dK/dV grid identical")
     for name in ("c4_vsa256_video", "c5_vsa256_720p_gate"):
         case = make_case(name, device="cuda")
         d = device_inputs(case)
-        ref = run_case(case, d=d, keep_device=True, persistent_bwd=False)
-        got = run_case(case, d=d, keep_device=True, persistent_bwd=True)
-        for n in ("dq", "dk", "dv", "dgate"):
+        ref = run_case(case, d=d, keep_device=True, persistent=False)
+        got = run_case(case, d=d, keep_device=True, persistent=True)
+        for n in ("out", "lse", "dq", "dk", "dv", "dgate"):
             if ref[n] is not None:
                 assert torch.equal(ref[n], got[n]), (name, n)
-        _say(f"[{name}] persistent backward identical")
+        _say(f"[{name}] persistent dK/dV grid identical")
         del d, ref, got, case
         torch.cuda.empty_cache()
 
