@@ -26,7 +26,7 @@ _LIB_OVERRIDE = os.environ.get("ORACLE_LIB")
 _LIB = None
 
 _LAYOUT = {"bhsd": 0, "bshd": 1, "tnd": 2}
-_GATE = {"none": 0, "per_token": 1, "per_element": 2}
+_GATE = {"none": 0, "per_token": 1, "per_element": 2, "projected": 3}
 
 
 class OracleProblem(C.Structure):

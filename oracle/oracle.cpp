@@ -35,7 +35,10 @@
 //  * compression: softmax of C over all non-empty KV tiles, Oc = P_c Vc;
 //    out = O_sel + gate (.) Oc[tile of the row] on every slot of the tile;
 //  * the gradient flows through the pooled q/k/v (valid slots get grad/count)
-//    but not through the top-k choice.
+//    but not through the top-k choice;
+//  * a projected gate (mode 3) is sigmoid(<q_s, w_h> + b_h) per token and
+//    head, a learnable projection of the row's own query; its gradient reaches
+//    w, b and q.
 
 #include <algorithm>
 #include <cmath>
@@ -58,7 +61,10 @@ typedef struct oracle_problem {
   const int32_t* q_lens;  // [B] packed layout only
   const int32_t* kv_lens;
   double scale;
-  int32_t gate_mode;  // 0 none, 1 one gate per (token, head), 2 one gate per element
+  // 0 none, 1 one gate per (token, head), 2 one gate per element, 3 one gate
+  // per (token, head) projected from the query row: sigmoid(<q, w_h> + b_h),
+  // with the gate argument holding the parameters [w (Hq x D) | b (Hq)]
+  int32_t gate_mode;
   int32_t threads;    // OpenMP threads, 0 = runtime default
 } oracle_problem;
 }
@@ -145,6 +151,34 @@ T dot(const T* a, const T* b, int n) {
   T s = 0;
   for (int d = 0; d < n; ++d) s += a[d] * b[d];
   return s;
+}
+
+// ---------------------------------------------------------------------------
+// The gate of row (b, h, s), element d: given per token (1) or per element
+// (2), or projected from the row's query (3): z = <q_s, w_h> + b_h,
+// gate = 1 / (1 + exp(-z)).
+// ---------------------------------------------------------------------------
+template <class T>
+T proj_gate(const Geo& g, const T* q, const T* theta, int b, int h, int s) {
+  const int D = g.p.D;
+  const T z = dot(q + g.q_off(b, h, s), theta + (int64_t)h * D, D) + theta[(int64_t)g.p.Hq * D + h];
+  return T(1) / (T(1) + std::exp(-z));
+}
+
+template <class T>
+T gate_at(const Geo& g, const T* q, const T* gate, int b, int h, int s, int d) {
+  if (g.p.gate_mode == 1) return gate[g.gate_tok(b, h, s)];
+  if (g.p.gate_mode == 2) return gate[g.q_off(b, h, s) + d];
+  return proj_gate(g, q, gate, b, h, s);
+}
+
+// dL/dz of a projected gate: (sum_e dO_e Oc_e) * gate * (1 - gate), with Oc
+// the coarse output of the row's Q tile.
+template <class T>
+T proj_dlogit(const Geo& g, const T* q, const T* theta, const T* dout, const T* oc, int b, int h,
+              int s) {
+  const T gv = proj_gate(g, q, theta, b, h, s);
+  return dot(dout + g.q_off(b, h, s), oc + g.pq(b, h, s / g.p.q_block), g.p.D) * gv * (T(1) - gv);
 }
 
 // ---------------------------------------------------------------------------
@@ -321,10 +355,7 @@ void fwd_row(const Geo& g, const T* q, const T* k, const T* v, const T* gate, co
     for (int d = 0; d < D; ++d) osel_row[d] = o[d];
   if (g.p.gate_mode != 0) {
     const T* ocr = oc + g.pq(b, h, s / g.p.q_block);
-    for (int d = 0; d < D; ++d) {
-      const T gv = g.p.gate_mode == 1 ? gate[g.gate_tok(b, h, s)] : gate[g.q_off(b, h, s) + d];
-      o[d] += gv * ocr[d];
-    }
+    for (int d = 0; d < D; ++d) o[d] += gate_at(g, q, gate, b, h, s, d) * ocr[d];
   }
   if (out_row)
     for (int d = 0; d < D; ++d) out_row[d] = o[d];
@@ -384,7 +415,7 @@ struct Coarse {
 };
 
 template <class T>
-void coarse_bwd(const Geo& g, const T* gate, const T* dout, Coarse<T>& c, T* dgate,
+void coarse_bwd(const Geo& g, const T* q, const T* gate, const T* dout, Coarse<T>& c, T* dgate,
                 const uint8_t* group_mask) {
   const auto& p = g.p;
   const int D = p.D;
@@ -405,7 +436,7 @@ void coarse_bwd(const Geo& g, const T* gate, const T* dout, Coarse<T>& c, T* dga
         const T* o = c.oc.data() + g.pq(b, h, i);
         T tok = 0;
         for (int e = 0; e < D; ++e) {
-          const T gv = p.gate_mode == 1 ? gate[g.gate_tok(b, h, s)] : gate[qo + e];
+          const T gv = gate_at(g, q, gate, b, h, s, e);
           d[e] += gv * dout[qo + e];
           if (p.gate_mode == 2 && dgate) dgate[qo + e] = dout[qo + e] * o[e];
           tok += dout[qo + e] * o[e];
@@ -471,6 +502,30 @@ void coarse_bwd(const Geo& g, const T* gate, const T* dout, Coarse<T>& c, T* dga
     }
 }
 
+// Gradient of the projection parameters of a projected gate (mode 3):
+// dw_h = sum over rows of dL/dz q_s, db_h = sum of dL/dz; dtheta = [dw | db].
+template <class T>
+void proj_bwd(const Geo& g, const T* q, const T* theta, const T* dout, const T* oc, T* dtheta,
+              const uint8_t* group_mask) {
+  const auto& p = g.p;
+  const int D = p.D;
+  std::fill(dtheta, dtheta + (int64_t)p.Hq * D + p.Hq, T(0));
+#pragma omp parallel for schedule(dynamic)
+  for (int h = 0; h < p.Hq; ++h) {
+    T* dw = dtheta + (int64_t)h * D;
+    T& db = dtheta[(int64_t)p.Hq * D + h];
+    for (int b = 0; b < p.B; ++b) {
+      if (group_mask && !group_mask[b * p.Hkv + g.kv_head(h)]) continue;
+      for (int s = 0; s < g.q_len(b); ++s) {
+        const T dl = proj_dlogit(g, q, theta, dout, oc, b, h, s);
+        const T* qs = q + g.q_off(b, h, s);
+        for (int e = 0; e < D; ++e) dw[e] += dl * qs[e];
+        db += dl;
+      }
+    }
+  }
+}
+
 template <class T>
 void bwd(const Geo& g, const T* q, const T* k, const T* v, const T* gate, const T* dout,
          const uint8_t* map, const uint8_t* group_mask, T* dq, T* dk, T* dv, T* dgate) {
@@ -487,7 +542,8 @@ void bwd(const Geo& g, const T* q, const T* k, const T* v, const T* gate, const 
     c.lse_c.assign((int64_t)p.B * p.Hq * p.Qb, 0);
     pool(g, q, k, v, c.qc.data(), c.kc.data(), c.vc.data());
     coarse_fwd(g, c.qc.data(), c.kc.data(), c.vc.data(), c.oc.data(), c.lse_c.data());
-    coarse_bwd(g, gate, dout, c, dgate, group_mask);
+    coarse_bwd(g, q, gate, dout, c, p.gate_mode == 3 ? (T*)nullptr : dgate, group_mask);
+    if (p.gate_mode == 3 && dgate) proj_bwd(g, q, gate, dout, c.oc.data(), dgate, group_mask);
   }
   // row pass
   std::vector<T> lse(g.rows_total(), 0), dr(g.rows_total(), 0);
@@ -523,6 +579,10 @@ void bwd(const Geo& g, const T* q, const T* k, const T* v, const T* gate, const 
           const T* a = c.dqc.data() + g.pq(b, h, i);
           for (int e = 0; e < D; ++e) o[e] += a[e] / (T)n;
         }
+      }
+      if (p.gate_mode == 3) {  // the projected gate's own path: dq += dL/dz w_h
+        const T dl = proj_dlogit(g, q, gate, dout, c.oc.data(), b, h, s);
+        for (int e = 0; e < D; ++e) o[e] += dl * gate[(int64_t)h * D + e];
       }
     }
   }
@@ -589,7 +649,7 @@ void dq_rows(const Geo& g, const T* q, const T* k, const T* v, const T* gate, co
     coarse_fwd(g, c.qc.data(), c.kc.data(), c.vc.data(), c.oc.data(), c.lse_c.data());
     std::vector<uint8_t> gm((size_t)p.B * p.Hkv, 0);
     for (int64_t u = 0; u < nrows; ++u) gm[rows[3 * u] * p.Hkv + g.kv_head(rows[3 * u + 1])] = 1;
-    coarse_bwd(g, gate, dout, c, (T*)nullptr, gm.data());
+    coarse_bwd(g, q, gate, dout, c, (T*)nullptr, gm.data());
   }
 #pragma omp parallel
   {
@@ -617,6 +677,10 @@ void dq_rows(const Geo& g, const T* q, const T* k, const T* v, const T* gate, co
           for (int e = 0; e < D; ++e) o[e] += a[e] / (T)n;
         }
       }
+      if (p.gate_mode == 3) {
+        const T dl = proj_dlogit(g, q, gate, dout, c.oc.data(), b, h, s);
+        for (int e = 0; e < D; ++e) o[e] += dl * gate[(int64_t)h * D + e];
+      }
     }
   }
 }
@@ -642,7 +706,7 @@ void dkdv_tiles(const Geo& g, const T* q, const T* k, const T* v, const T* gate,
     coarse_fwd(g, c.qc.data(), c.kc.data(), c.vc.data(), c.oc.data(), c.lse_c.data());
     std::vector<uint8_t> gm((size_t)p.B * p.Hkv, 0);
     for (int64_t u = 0; u < ntiles; ++u) gm[tiles[3 * u] * p.Hkv + tiles[3 * u + 1]] = 1;
-    coarse_bwd(g, gate, dout, c, (T*)nullptr, gm.data());
+    coarse_bwd(g, q, gate, dout, c, (T*)nullptr, gm.data());
   }
   // rows attending any requested tile
   std::vector<uint8_t> need(g.rows_total(), 0);

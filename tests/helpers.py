@@ -132,7 +132,8 @@ def torch_vsa_reference(case, bmap, dout=None):
         each tile) applied to q, k and v;
       * coarse scores C = scale Qc Kc^T, KV tiles without a valid token set to
         -inf; O_c = softmax(C) Vc, spread over every slot of its Q tile;
-      * out = O_sel + gate * O_c (per-token gates broadcast over D).
+      * out = O_sel + gate * O_c (per-token gates broadcast over D; a
+        projected gate is sigmoid(<q_s, w_h> + b_h) with gate = [w | b]).
     Returns numpy out, dq, dk, dv, dgate (None without a gate) in the case
     layout; the backward is torch autograd of sum(out * dout).
     """
@@ -159,6 +160,10 @@ def torch_vsa_reference(case, bmap, dout=None):
         oc_tok = oc.repeat_interleave(case.q_block, dim=2)[:, :, :case.Sq]
         if case.gate_mode == "per_token":
             g = (gate if case.layout == "bhsd" else gate.transpose(1, 2)).unsqueeze(-1)
+        elif case.gate_mode == "projected":  # sigmoid(<q_s, w_h> + b_h), gate = [w | b]
+            w = gate[:case.Hq * case.D].view(case.Hq, case.D)
+            z = (qh * w[None, :, None, :]).sum(-1) + gate[case.Hq * case.D:][None, :, None]
+            g = torch.sigmoid(z).unsqueeze(-1)
         else:
             g = _to_bhsd(gate, case.layout)
         out = out + g * oc_tok

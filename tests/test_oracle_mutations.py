@@ -62,7 +62,15 @@ MUTANTS = [
     ("dv_uses_q_not_dout",
      "dvo[e] += P * dout[qo + e];", "dvo[e] += P * q[qo + e];"),
     ("gate_blend_convex",
-     "o[d] += gv * ocr[d];", "o[d] = (1 - gv) * o[d] + gv * ocr[d];"),
+     "o[d] += gate_at(g, q, gate, b, h, s, d) * ocr[d];",
+     "o[d] = (1 - gate_at(g, q, gate, b, h, s, d)) * o[d] + gate_at(g, q, gate, b, h, s, d) * ocr[d];"),
+    ("projected_gate_sigmoid_sign",
+     "return T(1) / (T(1) + std::exp(-z));", "return T(1) / (T(1) + std::exp(z));"),
+    ("projected_gate_dq_term_missing",
+     "for (int e = 0; e < D; ++e) o[e] += dl * gate[(int64_t)h * D + e];",
+     "for (int e = 0; e < D; ++e) o[e] += 0 * dl;"),
+    ("projected_gate_dlogit_without_sigmoid_derivative",
+     "* gv * (T(1) - gv);", "* gv;"),
     ("coarse_grad_ignores_gate",
      "d[e] += gv * dout[qo + e];", "d[e] += dout[qo + e];"),
     ("coarse_dv_missing_softmax_weight",

@@ -126,6 +126,7 @@ FD_CASES = [
     dict(name="fd_gate_token", layout="bhsd", topk=2, map_kind="none", gate_mode="per_token"),
     dict(name="fd_gate_elem", layout="bshd", topk=3, map_kind="none", gate_mode="per_element",
          pad_dout=False),
+    dict(name="fd_gate_proj", layout="bshd", topk=2, map_kind="none", gate_mode="projected"),
 ]
 
 
@@ -297,6 +298,10 @@ def _gated_cases():
     yield build_case("gated_map_mqa", dtype="fp16", layout="bshd", B=1, Hq=3, Hkv=1, D=16,
                      q_block=8, kv_block=8, q_var=[5, 8, 8], kv_var=[8, 7, 8], map_kind="per_row",
                      map_per_row=2, gate_mode="per_token", pad_inputs=False, seed=33)
+    # the gate projected from the query rows, GQA, top-k, two batch entries
+    yield build_case("gated_proj_gqa", dtype="bf16", layout="bshd", B=2, Hq=4, Hkv=2, D=16,
+                     q_block=8, kv_block=8, q_var=[8, 3, 8, 6], kv_var=[8, 1, 0, 8, 5, 8],
+                     topk=3, map_kind="none", gate_mode="projected", seed=34)
 
 
 @pytest.mark.parametrize("case", list(_gated_cases()), ids=lambda c: c.name)
@@ -329,6 +334,36 @@ def test_zero_gate_reduces_to_the_ungated_path():
     assert np.array_equal(lse, r_lse)
     for got, want in zip(orc.bwd()[:3], ref.bwd()[:3]):
         assert np.array_equal(got, want)
+
+
+def test_projected_gate_with_zero_weights_is_a_constant_gate():
+    """w = 0: the projected gate is sigmoid(b_h) on every token of head h, so
+    out, dq, dk and dv are those of a per-token gate holding that constant, and
+    the parameter gradients follow from that case's dgate by the chain rule:
+    db_h = sum_s dgate_s g(1-g), dw_h = sum_s dgate_s g(1-g) q_s."""
+    case = next(c for c in _gated_cases() if c.name == "gated_proj_gqa")
+    Hq, D = case.Hq, case.D
+    theta = case.gate.clone()
+    theta[:Hq * D] = 0
+    case.gate = theta
+    gh = torch.sigmoid(theta[Hq * D:].double())  # [Hq]
+    const = np.ascontiguousarray(np.broadcast_to(gh.numpy(), (case.B, case.Sq, Hq)))
+    tok = dataclasses.replace(case, gate_mode="per_token", gate=None)
+    orc = oracle.Oracle(case)
+    ref = oracle.Oracle(tok, tensors=dict(q=case.q, k=case.k, v=case.v, dout=case.dout,
+                                          gate=const))  # float64, not through a float32 cast
+    assert np.array_equal(orc.block_map(), ref.block_map())
+    np.testing.assert_allclose(orc.fwd()[0], ref.fwd()[0], atol=1e-14)
+    dq, dk, dv, dth = orc.bwd()
+    r_dq, r_dk, r_dv, r_dg = ref.bwd()
+    for got, want in ((dq, r_dq), (dk, r_dk), (dv, r_dv)):
+        np.testing.assert_allclose(got, want, atol=1e-13)
+    g = gh.numpy()
+    dl = r_dg * g * (1 - g)                   # [B, S, H]
+    q = case.q.double().numpy()               # [B, S, H, D]
+    np.testing.assert_allclose(dth[Hq * D:], dl.sum((0, 1)), atol=1e-12)
+    np.testing.assert_allclose(dth[:Hq * D].reshape(Hq, D), np.einsum("bsh,bshd->hd", dl, q),
+                               atol=1e-12)
 
 
 def test_one_live_kv_tile_compression_closed_form():

@@ -48,7 +48,7 @@ class Case:
     KVb: int
     scale: float
     topk: int = 0              # 0: the block map below is the selection
-    gate_mode: str = "none"    # "none" | "per_token" | "per_element"
+    gate_mode: str = "none"    # "none" | "per_token" | "per_element" | "projected"
     q_var: Optional[np.ndarray] = None    # int32 [Qb] valid tokens per Q tile
     kv_var: Optional[np.ndarray] = None   # int32 [KVb] valid tokens per KV tile
     q_lens: Optional[List[int]] = None    # TND per-sequence lengths
@@ -170,7 +170,13 @@ def build_case(
     v = _randn(gen, ks, tdt, device)
     dout = _randn(gen, qs, tdt, device)
     gate = None
-    if gate_mode != "none":
+    if gate_mode == "projected":
+        # parameters of the projected gate sigmoid(<q, w_h> + b_h), fp32
+        # [w (Hq x D) | b (Hq)]; w ~ N(0, 1/D) keeps <q, w_h> near N(0, 1)
+        w = torch.randn(Hq, D, generator=gen, device=device, dtype=torch.float32) / math.sqrt(D)
+        bias = torch.randn(Hq, generator=gen, device=device, dtype=torch.float32)
+        gate = torch.cat([w.reshape(-1), bias])
+    elif gate_mode != "none":
         if gate_mode == "per_token":
             gs = (B, Hq, Sq) if layout == "bhsd" else (B, Sq, Hq)
         else:
@@ -187,7 +193,7 @@ def build_case(
         v = v * km.to(tdt)
         if pad_dout:
             dout = dout * qm.to(tdt)
-            if gate is not None:
+            if gate is not None and gate_mode != "projected":
                 gm = qm if gate.dim() == 4 else qm.squeeze(-1)
                 gate = gate * gm.to(tdt)
 
