@@ -25,9 +25,9 @@ LIB_PATH = os.path.join(_PKG, "libvsa.so")
 
 BF16, FP16 = 0, 1
 BHSD, BSHD, TND = 0, 1, 2
-GATE_NONE, GATE_PER_TOKEN, GATE_PER_ELEMENT = 0, 1, 2
+GATE_NONE, GATE_PER_TOKEN, GATE_PER_ELEMENT, GATE_PROJECTED = 0, 1, 2, 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ABI_VERSION = 2
+ABI_VERSION = 3
 FLAG_ATOMIC_DQ = 1
 FLAG_PERSISTENT = 2
 FLAG_NO_PERSISTENT = 4
@@ -41,7 +41,8 @@ KERNELS = ("index", "pool", "coarse_fwd", "sparse_fwd", "bwd_pre", "coarse_bwd",
 
 _DTYPES = {torch.bfloat16: BF16, torch.float16: FP16}
 _LAYOUTS = {"bhsd": BHSD, "bshd": BSHD, "tnd": TND}
-_GATES = {"none": GATE_NONE, "per_token": GATE_PER_TOKEN, "per_element": GATE_PER_ELEMENT}
+_GATES = {"none": GATE_NONE, "per_token": GATE_PER_TOKEN, "per_element": GATE_PER_ELEMENT,
+          "projected": GATE_PROJECTED}
 
 
 class VsaError(RuntimeError):
@@ -61,7 +62,7 @@ class VsaProblem(C.Structure):
         ("cu_seqlens_q", C.c_void_p), ("cu_seqlens_kv", C.c_void_p),
         ("max_seqlen_q", C.c_int32), ("max_seqlen_kv", C.c_int32),
         ("scale", C.c_float), ("topk", C.c_int32), ("gate_mode", C.c_int32),
-        ("map_batch_stride", C.c_int64), ("flags", C.c_int32),
+        ("map_batch_stride", C.c_int64), ("flags", C.c_int32), ("gate_proj", C.c_void_p),
     ]
 
 
@@ -135,8 +136,11 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
                  cu_seqlens_kv: Optional[torch.Tensor] = None, max_seqlen_q: int = 0,
                  max_seqlen_kv: int = 0, scale: Optional[float] = None, topk: int = 0,
                  gate_mode: str = "none", map_batch_stride: Optional[int] = None,
-                 atomic_dq: bool = False, persistent: Optional[bool] = None) -> Problem:
+                 atomic_dq: bool = False, persistent: Optional[bool] = None,
+                 gate_proj: Optional[torch.Tensor] = None) -> Problem:
     """Fill a vsa_problem. q_valid / kv_valid / cu_seqlens are int32 device tensors.
+    gate_proj (gate_mode "projected"): the gate's parameters, a contiguous
+    float32 device tensor [w (Hq x D) | b (Hq)].
     atomic_dq selects the backward that adds dQ inside the KV-owned pass
     (VSA_FLAG_ATOMIC_DQ). persistent: None lets the library choose the
     dK/dV grid, True forces the persistent longest-first grid
@@ -155,6 +159,12 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
     for t in keep:
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise ValueError("valid counts and cu_seqlens must be contiguous int32 tensors")
+    if gate_proj is not None:
+        if gate_proj.dtype != torch.float32 or not gate_proj.is_contiguous() \
+                or gate_proj.numel() != Hq * D + Hq:
+            raise ValueError(f"gate_proj must be a contiguous float32 tensor of Hq*D+Hq = "
+                             f"{Hq * D + Hq} elements")
+        keep = keep + (gate_proj,)
     for t, n, name in ((q_valid, Qb, "q_valid"), (kv_valid, KVb, "kv_valid")):
         if t is not None and t.numel() != n:
             raise ValueError(f"{name} needs {n} entries, got {t.numel()}")
@@ -179,7 +189,8 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
         scale=1.0 / math.sqrt(D) if scale is None else float(scale), topk=topk,
         gate_mode=_GATES[gate_mode], map_batch_stride=map_batch_stride,
         flags=(FLAG_ATOMIC_DQ if atomic_dq else 0)
-        | {None: 0, True: FLAG_PERSISTENT, False: FLAG_NO_PERSISTENT}[persistent])
+        | {None: 0, True: FLAG_PERSISTENT, False: FLAG_NO_PERSISTENT}[persistent],
+        gate_proj=None if gate_proj is None else gate_proj.data_ptr())
     return Problem(s, keep)
 
 
@@ -233,7 +244,7 @@ def _expect(t, n, name, dtype=None):
 def _check_tensors(p, q, k, v, gate, qlike=(), kvlike=(), lse=None, block_map=None):
     for t in p.keep:
         if not t.is_cuda:
-            raise ValueError("valid counts and cu_seqlens must be device tensors")
+            raise ValueError("valid counts, cu_seqlens and gate_proj must be device tensors")
     dt = torch.bfloat16 if p.dtype == BF16 else torch.float16
     nq, nk = _numel_q(p), _numel_kv(p)
     _expect(q, nq, "q", dt)
@@ -244,7 +255,8 @@ def _check_tensors(p, q, k, v, gate, qlike=(), kvlike=(), lse=None, block_map=No
     for name, t in kvlike:
         _expect(t, nk, name, dt)
     if gate is not None:
-        _expect(gate, nq // p.D if p.gate_mode == GATE_PER_TOKEN else nq, "gate", dt)
+        per_tok = p.gate_mode in (GATE_PER_TOKEN, GATE_PROJECTED)
+        _expect(gate, nq // p.D if per_tok else nq, "gate", dt)
     if lse is not None:
         _expect(lse, (p.Sq if p.layout == TND else p.B * p.Sq) * p.Hq, "lse", torch.float32)
     if block_map is not None:
@@ -279,7 +291,9 @@ def vsa_bwd(p: Problem, q, k, v, gate, dout, out, lse, saved, dq, dk, dv, dgate,
     if q is not None:
         _check_tensors(p, q, k, v, gate, qlike=(("dout", dout), ("out", out), ("dq", dq)),
                        kvlike=(("dk", dk), ("dv", dv)), lse=lse)
-        if dgate is not None:
+        if dgate is not None and p.gate_mode == GATE_PROJECTED:
+            _expect(dgate, p.Hq * p.D + p.Hq, "dgate", torch.float32)
+        elif dgate is not None:
             if gate is None:
                 raise ValueError("dgate needs the gate it is the gradient of")
             _expect(dgate, gate.numel(), "dgate", gate.dtype)

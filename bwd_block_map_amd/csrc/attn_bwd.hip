@@ -30,9 +30,10 @@ namespace vsa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Row term Dr = rowsum(dO * O_sel); gate: dO_c and dgate.
+// Row term Dr = rowsum(dO * O_sel); gate: dO_c and dgate. PROJ: the gate is
+// projected from q (its dL/dz per row and the partial sums of dw, db).
 // ---------------------------------------------------------------------------
-template <class ET>
+template <class ET, bool PROJ>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
   using E = Elem<ET>;
   __shared__ float red[16][HD];
@@ -52,9 +53,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
   if (tid == 0) live_end = 0;
   __syncthreads();
   int lend = 0;
-  float gacc[8];
+  float gacc[8], wacc[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) gacc[u] = 0.f;
+  for (int u = 0; u < 8; ++u) gacc[u] = wacc[u] = 0.f;
+  float bacc = 0.f;
+  constexpr bool proj = PROJ;
+  float wv[8];  // projected gate: this lane's 8 elements of w_h
+  if constexpr (proj) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) wv[u] = a.gproj[h * HD + 8 * dg + u];
+  }
   float ocv[8];
   if (gated) {
     const float* ocp = a.oc + g.pq(b, h, i) + 8 * dg;
@@ -92,8 +100,26 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
       a.lse2[lr] = l == -INFINITY ? INFINITY : l * LOG2E;  // exp2 domain; empty rows give P = 0
     }
     if (gated) {
-      if (a.gate_mode == VSA_GATE_PER_TOKEN) {
-        const float gt = E::lo(a.gate[g.gtok_base(b, h) + (long long)(blk0 + s) * g.gtok_rs()]);
+      if (proj || a.gate_mode == VSA_GATE_PER_TOKEN) {
+        float gt;
+        float qf[8];
+        if constexpr (proj) {  // the gate again from the query row: sigmoid(<q, w_h> + b_h)
+          const uint32_t* qw = reinterpret_cast<const uint32_t*>(&qv);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            qf[2 * w] = E::lo(qw[w]);
+            qf[2 * w + 1] = E::hi(qw[w]);
+          }
+          float z = 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) z = __builtin_fmaf(qf[u], wv[u], z);
+#pragma unroll
+          for (int m = 8; m >= 1; m >>= 1) z += __shfl_xor(z, m, 16);
+          z += a.gproj[g.Hq * HD + h];
+          gt = 1.f / (1.f + __builtin_amdgcn_exp2f(-z * LOG2E));
+        } else {
+          gt = E::lo(a.gate[g.gtok_base(b, h) + (long long)(blk0 + s) * g.gtok_rs()]);
+        }
         float dgp = 0.f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -102,9 +128,18 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
         }
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) dgp += __shfl_xor(dgp, m, 16);
-        if (a.dgate && dg == 0)
+        if constexpr (proj) {  // dL/dz = dL/dgate * gate (1 - gate); its sums for dw and db
+          const float dl = dgp * gt * (1.f - gt);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) wacc[u] = __builtin_fmaf(dl, qf[u], wacc[u]);
+          if (dg == 0) {
+            a.dlogit[g.lse_base(b, h) + blk0 + s] = dl;
+            bacc += dl;
+          }
+        } else if (a.dgate && dg == 0) {
           a.dgate[g.gtok_base(b, h) + (long long)(blk0 + s) * g.gtok_rs()] =
               (uint16_t)(E::pack(dgp, 0.f) & 0xffffu);
+        }
       } else {
         const uint4 gv = ldg16(a.gate + off);
         const uint32_t* gw = reinterpret_cast<const uint32_t*>(&gv);
@@ -132,6 +167,41 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
     for (int r = 0; r < 16; ++r) s += red[r][tid];
     a.doc[g.pq(b, h, i) + tid] = s;
   }
+  if constexpr (!proj) return;
+  __syncthreads();  // red is reused for the dw partial sums
+#pragma unroll
+  for (int u = 0; u < 8; ++u) red[slot][8 * dg + u] = wacc[u];
+  __shared__ float bred[16];
+  if (dg == 0) bred[slot] = bacc;
+  __syncthreads();
+  if (tid < HD) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += red[r][tid];
+    a.dwp[g.pq(b, h, i) + tid] = s;
+  }
+  if (tid == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += bred[r];
+    a.dbp[((long long)b * g.Hq + h) * g.Qb + i] = s;
+  }
+}
+
+// [dw | db] of the projected gate: sums of bwd_pre's per-Q-block partials over
+// batch entries and Q blocks; one work-group per head, one thread per element.
+__global__ __launch_bounds__(HD) void gate_proj_grad_kernel(const Geom g, const float* dwp,
+                                                            const float* dbp, float* dtheta) {
+  const int h = blockIdx.x, d = threadIdx.x;
+  float sw = 0.f, sb = 0.f;
+  for (int b = 0; b < g.B; ++b)
+    for (int i = 0; i < g.Qb; ++i) {
+      const long long r = ((long long)b * g.Hq + h) * g.Qb + i;
+      sw += dwp[r * HD + d];
+      if (d == 0) sb += dbp[r];
+    }
+  dtheta[h * HD + d] = sw;
+  if (d == 0) dtheta[g.Hq * HD + h] = sb;
 }
 
 // ---------------------------------------------------------------------------
@@ -755,17 +825,22 @@ __global__ __launch_bounds__(256) void dq_cast_kernel(const BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) cterm[u] = c[u] / (float)nq;
   }
+  float wv[8];  // projected gate: this lane's 8 elements of w_h
+#pragma unroll
+  for (int u = 0; u < 8; ++u) wv[u] = a.gproj ? a.gproj[h * HD + 8 * dg + u] : 0.f;
   for (int s = slot; s < qexist; s += 16) {
     const long long off = qb + (long long)(blk0 + s) * qrs + 8 * dg;
     const float4 x0 = *reinterpret_cast<const float4*>(a.dqacc + off);
     const float4 x1 = *reinterpret_cast<const float4*>(a.dqacc + off + 4);
     const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     const bool valid = s < nq;
+    const float dl = a.gproj ? a.dlogit[g.lse_base(b, h) + blk0 + s] : 0.f;
+    float y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) y[u] = __builtin_fmaf(dl, wv[u], g.scale * x[u] + (valid ? cterm[u] : 0.f));
     uint32_t w[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      w[u] = E::pack(g.scale * x[2 * u] + (valid ? cterm[2 * u] : 0.f),
-                     g.scale * x[2 * u + 1] + (valid ? cterm[2 * u + 1] : 0.f));
+    for (int u = 0; u < 4; ++u) w[u] = E::pack(y[2 * u], y[2 * u + 1]);
     stg16(a.dq + off, make_uint4(w[0], w[1], w[2], w[3]));
   }
 }
@@ -877,6 +952,9 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
       invn = 1.f / (float)nq;
     }
   }
+  // projected gate: every row adds dL/dz w_h
+  const float dl = a.gproj ? a.dlogit[lrow] : 0.f;
+  const float* wh = a.gproj ? a.gproj + h * HD : nullptr;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -892,6 +970,13 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
         x[2] += cq.z * invn;
         x[3] += cq.w * invn;
       }
+      if (wh) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wh + d0);
+        x[0] = __builtin_fmaf(dl, w4.x, x[0]);
+        x[1] = __builtin_fmaf(dl, w4.y, x[1]);
+        x[2] = __builtin_fmaf(dl, w4.z, x[2]);
+        x[3] = __builtin_fmaf(dl, w4.w, x[3]);
+      }
       *reinterpret_cast<uint2*>(a.dq + qoff + d0) =
           make_uint2(E::pack(x[0], x[1]), E::pack(x[2], x[3]));
     }
@@ -901,7 +986,8 @@ template <class ET>
 hipError_t launch_pre_t(const PreArgs& a, hipStream_t st) {
   const long long n = (long long)a.g.B * a.g.Hq * a.g.Qb;
   if (n == 0) return hipSuccess;
-  bwd_pre_kernel<ET><<<(unsigned)n, 256, 0, st>>>(a);
+  if (a.gate_mode == VSA_GATE_PROJECTED) bwd_pre_kernel<ET, true><<<(unsigned)n, 256, 0, st>>>(a);
+  else bwd_pre_kernel<ET, false><<<(unsigned)n, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -967,6 +1053,13 @@ hipError_t launch_lpt_order(const BwdArgs& a, int32_t* hist, int32_t* order, hip
   hipError_t e = launch_exclusive_scan(hist, nb, st);
   if (e != hipSuccess) return e;
   lpt_scatter_kernel<<<grid, 256, 0, st>>>(a, hist, order);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_proj_grad(const Geom& g, const float* dwp, const float* dbp, float* dtheta,
+                                 hipStream_t st) {
+  if (g.Hq == 0) return hipSuccess;
+  gate_proj_grad_kernel<<<(unsigned)g.Hq, HD, 0, st>>>(g, dwp, dbp, dtheta);
   return hipGetLastError();
 }
 

@@ -196,8 +196,32 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
     a.lse[g.lse_base(b, h) + blk0 + myrow] =
         l_run > 0.f ? (msc + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f : -INFINITY;
   float gt = 0.f;
-  if (a.gate_mode == VSA_GATE_PER_TOKEN)
+  if (a.gate_mode == VSA_GATE_PER_TOKEN) {
     gt = E::lo(a.gate[g.gtok_base(b, h) + (long long)(blk0 + myrow) * g.gtok_rs()]);
+  } else if (a.gate_mode == VSA_GATE_PROJECTED) {
+    // sigmoid(<q row, w_h> + b_h): this lane's 64 elements of the row (d =
+    // 16ks + 8hl + 0..7, already in registers), then the other lane half's
+    const float* w = a.gproj + h * HD + 8 * hl;
+    float z = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const float4 w0 = *reinterpret_cast<const float4*>(w + 16 * ks);
+      const float4 w1 = *reinterpret_cast<const float4*>(w + 16 * ks + 4);
+      z = __builtin_fmaf(E::lo(qr[ks].x), w0.x, z);
+      z = __builtin_fmaf(E::hi(qr[ks].x), w0.y, z);
+      z = __builtin_fmaf(E::lo(qr[ks].y), w0.z, z);
+      z = __builtin_fmaf(E::hi(qr[ks].y), w0.w, z);
+      z = __builtin_fmaf(E::lo(qr[ks].z), w1.x, z);
+      z = __builtin_fmaf(E::hi(qr[ks].z), w1.y, z);
+      z = __builtin_fmaf(E::lo(qr[ks].w), w1.z, z);
+      z = __builtin_fmaf(E::hi(qr[ks].w), w1.w, z);
+    }
+    z = xhalf_sum(z) + a.gproj[g.Hq * HD + h];
+    gt = 1.f / (1.f + __builtin_amdgcn_exp2f(-z * LOG2E));
+    if (a.gate_out && hl == 0)
+      a.gate_out[g.gtok_base(b, h) + (long long)(blk0 + myrow) * g.gtok_rs()] =
+          (uint16_t)(E::pack(gt, 0.f) & 0xffffu);
+  }
   const float* ocp = a.gate_mode != VSA_GATE_NONE ? a.oc + g.pq(b, h, i) : nullptr;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)

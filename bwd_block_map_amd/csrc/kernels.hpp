@@ -11,9 +11,11 @@ struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const uint16_t* gate;  // gate_mode != NONE
+  const uint16_t* gate;  // PER_TOKEN / PER_ELEMENT gate
   const float* oc;       // pooled coarse output [B,Hq,Qb,HD] (gate only)
   int gate_mode;
+  const float* gproj;    // PROJECTED: [w (Hq x HD) | b (Hq)]
+  uint16_t* gate_out;    // PROJECTED: per-token gate values, or null
   uint16_t* out;
   uint16_t* osel;  // un-gated sparse output (gate + training), else null
   float* lse;
@@ -38,6 +40,10 @@ struct BwdArgs {
   const float* dqc;  // gate: pooled-tile gradients added to valid slots, else null
   const float* dkc;
   const float* dvc;
+  // projected gate: [w | b] and dL/dz per row (laid out like lse), else null;
+  // every row's dq gets dL/dz w_h
+  const float* gproj;
+  const float* dlogit;
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -66,8 +72,14 @@ struct PreArgs {
   float* dr;
   float* lse2;
   float* doc;       // gate: [B,Hq,Qb,HD] sum over the tile of gate * dO
-  uint16_t* dgate;  // gate: optional
+  uint16_t* dgate;  // PER_TOKEN / PER_ELEMENT gate: optional
   int32_t* qlive;  // [B,Hq,Qb] live extents (see BwdArgs)
+  // projected gate: [w | b]; out: dL/dz per row (laid out like lse) and, per
+  // Q block, the partial sums of dL/dz q ([B,Hq,Qb,HD]) and of dL/dz ([B,Hq,Qb])
+  const float* gproj;
+  float* dlogit;
+  float* dwp;
+  float* dbp;
 };
 
 // Pooled tiles, coarse scores, top-k and coarse attention.
@@ -107,5 +119,8 @@ long long lpt_hist_entries(const Geom& g);  // int32 entries of the order's hist
 hipError_t launch_lpt_order(const BwdArgs& a, int32_t* hist, int32_t* order, hipStream_t st);
 hipError_t launch_exclusive_scan(int32_t* a, long long n, hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+// gradient of the projected gate's parameters [dw | db] from bwd_pre's partials
+hipError_t launch_gate_proj_grad(const Geom& g, const float* dwp, const float* dbp, float* dtheta,
+                                 hipStream_t st);
 
 }  // namespace vsa

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -194,6 +195,9 @@ struct BwdWs {
   float* dvc;
   float* ps;
   float* dss;
+  float* dlogit;  // VSA_GATE_PROJECTED: dL/dz per row, laid out like lse
+  float* dwp;     // VSA_GATE_PROJECTED: per-Q-block partial sums of dL/dz q
+  float* dbp;     // VSA_GATE_PROJECTED: per-Q-block partial sums of dL/dz
 };
 
 BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
@@ -215,6 +219,11 @@ BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
     w.dvc = c.take<float>((long long)p->B * p->Hkv * p->KVb * p->D);
     w.ps = c.take<float>((long long)p->B * p->Hq * p->Qb * p->KVb);
     w.dss = c.take<float>((long long)p->B * p->Hq * p->Qb * p->KVb);
+  }
+  if (p->gate_mode == VSA_GATE_PROJECTED) {
+    w.dlogit = c.take<float>(std::max(rows_total(p), 1LL));
+    w.dwp = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
+    w.dbp = c.take<float>((long long)p->B * p->Hq * p->Qb);
   }
   if (bytes) *bytes = c.off;
   return w;
@@ -268,8 +277,14 @@ int validate(const vsa_problem* p) {
   if (!(p->scale > 0.f) || !std::isfinite(p->scale))
     return fail(VSA_ERR_INVALID_ARG, "scale must be positive and finite");
   if (p->topk < 0) return fail(VSA_ERR_INVALID_ARG, "topk must be >= 0");
-  if (p->gate_mode < VSA_GATE_NONE || p->gate_mode > VSA_GATE_PER_ELEMENT)
-    return fail(VSA_ERR_INVALID_ARG, "gate_mode must be NONE, PER_TOKEN or PER_ELEMENT");
+  if (p->gate_mode < VSA_GATE_NONE || p->gate_mode > VSA_GATE_PROJECTED)
+    return fail(VSA_ERR_INVALID_ARG, "gate_mode must be NONE, PER_TOKEN, PER_ELEMENT or PROJECTED");
+  if (p->gate_mode == VSA_GATE_PROJECTED && !p->gate_proj)
+    return fail(VSA_ERR_INVALID_ARG, "gate_proj must be given with VSA_GATE_PROJECTED");
+  if (p->gate_mode != VSA_GATE_PROJECTED && p->gate_proj)
+    return fail(VSA_ERR_INVALID_ARG, "gate_proj is only read with VSA_GATE_PROJECTED (set it to NULL)");
+  if (p->gate_proj && ((uintptr_t)p->gate_proj & 15u))
+    return fail(VSA_ERR_INVALID_ARG, "gate_proj must be 16-byte aligned");
   if (p->map_batch_stride < 0) return fail(VSA_ERR_INVALID_ARG, "map_batch_stride must be >= 0");
   constexpr int kFlags = VSA_FLAG_ATOMIC_DQ | VSA_FLAG_PERSISTENT | VSA_FLAG_NO_PERSISTENT;
   if (p->flags & ~kFlags)
@@ -334,7 +349,8 @@ int check_device(const vsa_problem* p, std::initializer_list<Arg> args) {
   const Arg own[] = {{p->q_valid, "q_valid"},
                      {p->kv_valid, "kv_valid"},
                      {p->cu_seqlens_q, "cu_seqlens_q"},
-                     {p->cu_seqlens_kv, "cu_seqlens_kv"}};
+                     {p->cu_seqlens_kv, "cu_seqlens_kv"},
+                     {p->gate_proj, "gate_proj"}};
   for (const Arg& a : own)
     if (a.ptr && !device_accessible(a.ptr))
       return fail(VSA_ERR_INVALID_ARG, "%s must be a device tensor", a.name);
@@ -359,8 +375,9 @@ int fwd_impl(const vsa_problem* p, const void* q, const void* k, const void* v, 
   if (p->topk > 0 && block_map && p->map_batch_stride != (long long)p->Hq * p->Qb * p->KVb &&
       !(p->map_batch_stride == 0 && p->B == 1))
     return fail(VSA_ERR_INVALID_ARG, "an output block_map must be a dense [B,Hq,Qb,KVb] buffer");
-  if (p->gate_mode != VSA_GATE_NONE && !gate)
-    return fail(VSA_ERR_INVALID_ARG, "gate must be given when gate_mode != NONE");
+  const bool proj = p->gate_mode == VSA_GATE_PROJECTED;
+  if (p->gate_mode != VSA_GATE_NONE && !proj && !gate)
+    return fail(VSA_ERR_INVALID_ARG, "gate must be given with a PER_TOKEN or PER_ELEMENT gate");
   size_t need_ws = 0, need_saved = 0;
   carve_fwd(p, nullptr, &need_ws);
   carve_saved(p, nullptr, &need_saved);
@@ -431,9 +448,11 @@ int fwd_impl(const vsa_problem* p, const void* q, const void* k, const void* v, 
   fa.q = (const uint16_t*)q;
   fa.k = (const uint16_t*)k;
   fa.v = (const uint16_t*)v;
-  fa.gate = (const uint16_t*)gate;
+  fa.gate = proj ? nullptr : (const uint16_t*)gate;
   fa.oc = oc;
   fa.gate_mode = p->gate_mode;
+  fa.gproj = p->gate_proj;
+  fa.gate_out = proj ? (uint16_t*)const_cast<void*>(gate) : nullptr;
   fa.out = (uint16_t*)out;
   fa.osel = (gated && saved) ? s.osel : nullptr;
   fa.lse = lse;
@@ -599,7 +618,10 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
     return fail(VSA_ERR_INVALID_ARG, "q, k, v, lse, dq, dk and dv must be device buffers");
   if (!saved) return fail(VSA_ERR_INVALID_ARG, "saved must be the state of a training vsa_fwd");
   const bool gated = p->gate_mode != VSA_GATE_NONE;
-  if (gated && !gate) return fail(VSA_ERR_INVALID_ARG, "gate must be given when gate_mode != NONE");
+  const bool proj = p->gate_mode == VSA_GATE_PROJECTED;
+  if (gated && !proj && !gate)
+    return fail(VSA_ERR_INVALID_ARG, "gate must be given with a PER_TOKEN or PER_ELEMENT gate");
+  if (proj) gate = nullptr;  // the library recomputes it from q and gate_proj
   if (!gated && !out && dout) return fail(VSA_ERR_INVALID_ARG, "out must be given");
   size_t need_ws = 0, need_saved = 0;
   carve_bwd(p, nullptr, &need_ws);
@@ -622,7 +644,10 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
     if (e == hipSuccess) e = vsa::launch_zero(dk, (size_t)kn * 2, st);
     if (e == hipSuccess) e = vsa::launch_zero(dv, (size_t)kn * 2, st);
     if (e == hipSuccess && gated && dgate)
-      e = vsa::launch_zero(dgate, (size_t)(p->gate_mode == VSA_GATE_PER_TOKEN ? qn / p->D : qn) * 2, st);
+      e = vsa::launch_zero(dgate,
+                           proj ? (size_t)((long long)p->Hq * p->D + p->Hq) * sizeof(float)
+                                : (size_t)(p->gate_mode == VSA_GATE_PER_TOKEN ? qn / p->D : qn) * 2,
+                           st);
     if (e != hipSuccess) return hip_fail(e, "zero gradients");
     return ok();
   }
@@ -642,11 +667,17 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   pa.dr = w.dr;
   pa.lse2 = w.lse2;
   pa.doc = w.doc;
-  pa.dgate = (uint16_t*)dgate;
+  pa.dgate = proj ? nullptr : (uint16_t*)dgate;
   pa.qlive = w.qlive;
+  pa.gproj = p->gate_proj;
+  pa.dlogit = w.dlogit;
+  pa.dwp = w.dwp;
+  pa.dbp = w.dbp;
   {
     Prof pr(VSA_KERNEL_BWD_PRE, st);
     e = vsa::launch_bwd_pre(pa, p->dtype, st);
+    if (e == hipSuccess && proj && dgate)
+      e = vsa::launch_gate_proj_grad(g, w.dwp, w.dbp, (float*)dgate, st);
   }
   if (e != hipSuccess) return hip_fail(e, "backward preprocess");
 
@@ -682,6 +713,8 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   ba.dqc = gated ? w.dqc : nullptr;
   ba.dkc = gated ? w.dkc : nullptr;
   ba.dvc = gated ? w.dvc : nullptr;
+  ba.gproj = p->gate_proj;
+  ba.dlogit = w.dlogit;
   ba.dq = (uint16_t*)dq;
   ba.dk = (uint16_t*)dk;
   ba.dv = (uint16_t*)dv;

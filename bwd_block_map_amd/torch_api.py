@@ -13,7 +13,9 @@ test page (`video_sparse_attn` / `video_sparse_attn_bshd` usage):
 - BSHD is the native layout of the video path; BHSD goes through the same
   kernels with its own strides (no transposes);
 - the video wrappers build the tile map by pooled-score top-k inside the
-  library and add the gated compression branch when a gate is given.
+  library and add the gated compression branch when a gate is given;
+- a projected gate (weights w [H, D] and bias b [H]) has the library compute
+  each token's gate as sigmoid(<q, w_h> + b_h) and return dw, db.
 
 Everything here is argument marshalling: every step of the computation runs in
 the library's HIP kernels.
@@ -21,7 +23,7 @@ the library's HIP kernels.
 
 from __future__ import annotations
 
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import Optional, Sequence, Tuple, Union
 
 import torch
@@ -82,14 +84,17 @@ class Spec:
     # False: the backward adds dQ inside the KV-owned pass with float atomics
     # (faster or not, per workload; dq then varies in its last bits run to run)
     deterministic: bool = True
+    # True: the gate slot holds the projected gate's parameters [w | b] (fp32)
+    projected: bool = False
 
     def problem(self, q, k, gate):
         B, Hq, Hkv, Sq, Skv, D = dims(q, k, self.layout)
+        mode = "projected" if self.projected else gate_mode_of(gate, q, self.layout)
         return make_problem(dtype=q.dtype, layout=self.layout, B=B, Hq=Hq, Hkv=Hkv, Sq=Sq,
                             Skv=Skv, D=D, q_block=self.q_block, kv_block=self.kv_block,
                             q_valid=self.q_valid, kv_valid=self.kv_valid, scale=self.scale,
-                            topk=self.topk, gate_mode=gate_mode_of(gate, q, self.layout),
-                            atomic_dq=not self.deterministic)
+                            topk=self.topk, gate_mode=mode, atomic_dq=not self.deterministic,
+                            gate_proj=gate if self.projected else None)
 
 
 def _contig(*ts):
@@ -100,7 +105,8 @@ def _forward(spec: Spec, q, k, v, gate, block_map, training: bool):
     p = spec.problem(q, k, gate)
     buf = Buffers(p, q, training=training)
     bmap = block_map if spec.topk == 0 else buf.map
-    vsa_fwd(p, q, k, v, bmap, gate, buf.out, buf.lse, buf.saved if training else None, buf.ws_fwd)
+    vsa_fwd(p, q, k, v, bmap, None if spec.projected else gate, buf.out, buf.lse,
+            buf.saved if training else None, buf.ws_fwd)
     return p, buf, bmap
 
 
@@ -112,6 +118,7 @@ class _Attention(torch.autograd.Function):
         p, buf, bmap = _forward(spec, q, k, v, gate, block_map, training=True)
         ctx.save_for_backward(q, k, v, gate, buf.out, buf.lse)
         ctx.problem, ctx.buffers = p, buf  # saved state and workspace for the backward
+        ctx.projected = spec.projected
         ctx.mark_non_differentiable(buf.lse)
         ctx.set_materialize_grads(False)
         return buf.out, buf.lse
@@ -124,15 +131,34 @@ class _Attention(torch.autograd.Function):
         dgate = torch.empty_like(gate) if gate is not None and ctx.needs_input_grad[3] else None
         # a missing output gradient counts as zeros (the library takes dout = NULL)
         dout = None if grad_out is None else grad_out.contiguous()
-        vsa_bwd(ctx.problem, q, k, v, gate, dout, out, lse, ctx.buffers.saved, dq, dk, dv, dgate,
-                ctx.buffers.ws_bwd)
+        vsa_bwd(ctx.problem, q, k, v, None if ctx.projected else gate, dout, out, lse,
+                ctx.buffers.saved, dq, dk, dv, dgate, ctx.buffers.ws_bwd)
         return dq, dk, dv, dgate, None, None
 
 
+def _theta(gate_proj, Hq: int, D: int) -> torch.Tensor:
+    """[w | b] of a projected gate as one fp32 vector (autograd splits the
+    gradient back into w and b)."""
+    w, b = gate_proj
+    if tuple(w.shape) != (Hq, D) or tuple(b.shape) != (Hq,):
+        raise ValueError(f"gate projection: w must be [{Hq}, {D}] and b [{Hq}], got "
+                         f"{tuple(w.shape)} and {tuple(b.shape)}")
+    return torch.cat([w.float().reshape(-1), b.float().reshape(-1)])
+
+
 def attention(q, k, v, spec: Spec, block_map: Optional[torch.Tensor] = None,
-              gate: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+              gate: Optional[torch.Tensor] = None,
+              gate_proj: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
     """(out, lse) of block-sparse attention; autograd when any input needs a
-    gradient, else the inference path."""
+    gradient, else the inference path. gate_proj = (w [H, D], b [H]) selects
+    the projected gate (then `gate` must be None)."""
+    if gate_proj is not None:
+        if gate is not None:
+            raise ValueError("give either a gate or a gate projection, not both")
+        _, Hq, _, _, _, D = dims(q, k, spec.layout)
+        gate = _theta(gate_proj, Hq, D)
+        spec = replace(spec, projected=True)
     q, k, v, gate = _contig(q, k, v, gate)
     if block_map is not None:
         block_map = block_map.to(torch.uint8).contiguous()
@@ -172,33 +198,39 @@ def block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_m
     return out, lse.detach()
 
 
-def _video(q, k, v, kv_var, q_var, topk, block_size, gate, scale, layout, deterministic):
+def _video(q, k, v, kv_var, q_var, topk, block_size, gate, scale, layout, deterministic,
+           gate_proj=None):
     tile = 1
     for s in block_size:
         tile *= int(s)
     spec = Spec(layout=layout, q_block=tile, kv_block=tile, topk=int(topk), scale=scale,
                 q_valid=_counts(q_var, q.device), kv_valid=_counts(kv_var, q.device),
                 deterministic=deterministic)
-    return attention(q, k, v, spec, gate=gate)[0]
+    return attention(q, k, v, spec, gate=gate, gate_proj=gate_proj)[0]
 
 
 def video_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_var: Counts,
                       q_var: Counts, topk: int, block_size: Sequence[int] = (4, 8, 8),
                       compress_attn_weight: Optional[torch.Tensor] = None,
-                      scale: Optional[float] = None, deterministic: bool = True) -> torch.Tensor:
+                      scale: Optional[float] = None, deterministic: bool = True,
+                      gate_proj: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+                      ) -> torch.Tensor:
     """Video sparse attention over [B, H, S, D] tensors laid out in tiles of
     prod(block_size) tokens: each Q tile attends to its `topk` KV tiles of
     highest pooled score (q_var / kv_var valid tokens per tile); with
-    compress_attn_weight the gated pooled-tile branch is added. Returns out."""
+    compress_attn_weight (or the projected gate gate_proj = (w, b)) the gated
+    pooled-tile branch is added. Returns out."""
     return _video(q, k, v, kv_var, q_var, topk, block_size, compress_attn_weight, scale, "bhsd",
-                  deterministic)
+                  deterministic, gate_proj)
 
 
 def video_sparse_attn_bshd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_var: Counts,
                            q_var: Counts, topk: int, block_size: Sequence[int] = (4, 8, 8),
                            compress_attn_weight: Optional[torch.Tensor] = None,
                            scale: Optional[float] = None,
-                           deterministic: bool = True) -> torch.Tensor:
+                           deterministic: bool = True,
+                           gate_proj: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+                           ) -> torch.Tensor:
     """video_sparse_attn for [B, S, H, D] tensors (the gate likewise in BSHD)."""
     return _video(q, k, v, kv_var, q_var, topk, block_size, compress_attn_weight, scale, "bshd",
-                  deterministic)
+                  deterministic, gate_proj)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 2
+#define VSA_ABI_VERSION 3
 
 enum vsa_status {
   VSA_OK = 0,
@@ -68,8 +68,13 @@ enum vsa_layout { VSA_BHSD = 0, VSA_BSHD = 1, VSA_TND = 2 };
  * the video workloads: one gate per token and head). */
 enum vsa_gate_mode {
   VSA_GATE_NONE = 0,
-  VSA_GATE_PER_TOKEN = 1,  /* [B, Hq, Sq] next to BHSD, [B, Sq, Hq] next to BSHD */
-  VSA_GATE_PER_ELEMENT = 2 /* q-shaped                                          */
+  VSA_GATE_PER_TOKEN = 1,   /* [B, Hq, Sq] next to BHSD, [B, Sq, Hq] next to BSHD */
+  VSA_GATE_PER_ELEMENT = 2, /* q-shaped                                          */
+  /* one gate per token and head computed by the library from the token's query
+   * row, sigmoid(<q, w_h> + b_h), with learnable parameters gate_proj (see
+   * vsa_problem); vsa_fwd writes the gate values to `gate` (per-token layout)
+   * when it is not NULL, and vsa_bwd returns their gradient in `dgate` */
+  VSA_GATE_PROJECTED = 3
 };
 
 /*
@@ -113,6 +118,9 @@ enum vsa_gate_mode {
  *                 output and O_c[i] = softmax_j(C[i, j]) V_c[j] is attention
  *                 over the pooled tiles (C as for topk, over all non-empty KV
  *                 tiles), broadcast to every slot of Q tile i.
+ *   gate_proj     VSA_GATE_PROJECTED only: device fp32 [Hq * D + Hq], the
+ *                 projection weights w ([Hq, D], row h for Q head h) followed
+ *                 by the biases b ([Hq]); NULL otherwise
  *   map_batch_stride  elements between batch entries of block_map;
  *                 0 = one [Hq, Qb, KVb] map shared by every batch entry
  *   flags         0, or VSA_FLAG_ATOMIC_DQ: vsa_bwd computes dQ inside the
@@ -149,6 +157,7 @@ typedef struct vsa_problem {
   int32_t gate_mode;
   int64_t map_batch_stride;
   int32_t flags;
+  const float* gate_proj;
 } vsa_problem;
 
 #define VSA_FLAG_ATOMIC_DQ 1
@@ -219,7 +228,8 @@ int block_map_to_index(const vsa_problem* p, const uint8_t* block_map, int kv_ow
  *   block_map   topk == 0: the selection (input).
  *               topk > 0: NULL, or a uint8 [B, Hq, Qb, KVb] buffer that receives
  *               the selection (map_batch_stride must then be Hq*Qb*KVb or 0 with B == 1)
- *   gate        gate_mode != NONE: the gate, else NULL
+ *   gate        PER_TOKEN / PER_ELEMENT: the gate; PROJECTED: NULL, or a
+ *               per-token buffer that receives the gate values; NONE: NULL
  *   out         q-shaped output (the gated output when a gate is given)
  *   lse         fp32 natural-log LSE of the sparse branch; -inf for a row with
  *               no live key (whose output is then 0)
@@ -265,13 +275,15 @@ int vsa_fwd_noalloc(const vsa_problem* p, const void* q, const void* k, const vo
  * through the top-k choice. Rows whose q and dout are both zero (the padded
  * slots of video tiles in training) have dS = 0 and are skipped; for finite
  * inputs the results are those of the full computation.
- *   q, k, v, gate  the forward's inputs
+ *   q, k, v, gate  the forward's inputs (PROJECTED: gate is not read)
  *   dout        q-shaped upstream gradient; NULL means zeros
  *   out         the forward's output (read only when gate_mode == NONE; with a
  *               gate the un-gated sparse output kept in `saved` is used)
  *   lse         the forward's lse
  *   saved       the buffer a training vsa_fwd filled
- *   dq          q-shaped; dk, dv kv-shaped (Hkv heads); dgate gate-shaped or NULL
+ *   dq          q-shaped; dk, dv kv-shaped (Hkv heads); dgate gate-shaped or
+ *               NULL (PROJECTED: fp32 [Hq * D + Hq], the gradient of gate_proj;
+ *               the projection's own term dL/dz w_h is part of dq)
  *   ws          workspace of at least ws_bwd bytes
  */
 int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, const void* gate,

@@ -214,6 +214,16 @@ class Oracle:
                        self._p(out), self._p(osel), self._p(lse))
         return out, osel, lse
 
+    def gate_values(self):
+        """The projected gate of every token, in the per-token gate layout
+        ([B, Hq, S] for BHSD, [B, S, Hq] for BSHD)."""
+        c = self.case
+        assert c.gate_mode == "projected"
+        shape = (c.B, c.Hq, c.Sq) if c.layout == "bhsd" else (c.B, c.Sq, c.Hq)
+        out = np.zeros(shape, self.dt)
+        self._f("gate_values")(self.P.ref, self._p(self.q), self._p(self.gate), self._p(out))
+        return out
+
     def fwd_rows(self, rows: np.ndarray):
         """rows: int32 [n, 3] of (b, h, s). Returns out [n, D], lse [n]."""
         c = self.case

@@ -864,6 +864,18 @@ int64_t oracle_block_index(const oracle_problem* p, const uint8_t* map, int32_t 
     dq_rows(g, q, k, v, gate, dout, map, nrows, rows, dq_rows_out);                             \
   }
 
+// The projected gate's values (mode 3) in the per-token layout of a gate.
+#define ORACLE_GATE_ENTRY(SUF, T)                                                              \
+  void oracle_gate_values_##SUF(const oracle_problem* p, const T* q, const T* theta, T* out) { \
+    Geo g(*p);                                                                                 \
+    for (int b = 0; b < p->B; ++b)                                                             \
+      for (int h = 0; h < p->Hq; ++h)                                                          \
+        for (int s = 0; s < g.q_len(b); ++s)                                                   \
+          out[g.gate_tok(b, h, s)] = proj_gate(g, q, theta, b, h, s);                          \
+  }
+ORACLE_GATE_ENTRY(f32, float)
+ORACLE_GATE_ENTRY(f64, double)
+
 #define ORACLE_TILE_ENTRY(SUF, T)                                                                \
   void oracle_dkdv_tiles_##SUF(const oracle_problem* p, const T* q, const T* k, const T* v,      \
                                const T* gate, const T* dout, const uint8_t* map, int64_t ntiles, \

@@ -32,6 +32,7 @@ def device_inputs(case, device="cuda"):
 
 
 def problem_for(case, d, map_batch_stride=None, atomic_dq=False, persistent=None):
+    proj = case.gate_mode == "projected"
     return vsa.make_problem(
         dtype=case.torch_dtype, layout=case.layout, B=case.B, Hq=case.Hq, Hkv=case.Hkv,
         Sq=case.Sq, Skv=case.Skv, D=case.D, q_block=case.q_block, kv_block=case.kv_block,
@@ -40,7 +41,8 @@ def problem_for(case, d, map_batch_stride=None, atomic_dq=False, persistent=None
         max_seqlen_q=max(case.q_lens) if case.q_lens else 0,
         max_seqlen_kv=max(case.kv_lens) if case.kv_lens else 0,
         scale=case.scale, topk=case.topk, gate_mode=case.gate_mode,
-        map_batch_stride=map_batch_stride, atomic_dq=atomic_dq, persistent=persistent)
+        map_batch_stride=map_batch_stride, atomic_dq=atomic_dq, persistent=persistent,
+        gate_proj=d["gate"] if proj else None)
 
 
 def run_case(case, training=True, backward=True, dout_none=False, device="cuda", d=None,
@@ -49,14 +51,28 @@ def run_case(case, training=True, backward=True, dout_none=False, device="cuda",
     p = problem_for(case, d, atomic_dq=atomic_dq, persistent=persistent)
     buf = vsa.Buffers(p, d["q"], training=training or backward)
     bmap = d["map"] if case.topk == 0 else buf.map
-    vsa.vsa_fwd(p, d["q"], d["k"], d["v"], bmap, d["gate"], buf.out, buf.lse,
+    proj = case.gate_mode == "projected"
+    # a projected gate: its parameters go into the problem, `gate` receives
+    # the per-token gate values the forward computes
+    gate = d["gate"]
+    if proj:
+        shape = (case.B, case.Hq, case.Sq) if case.layout == "bhsd" else (case.B, case.Sq, case.Hq)
+        gate = torch.full(shape, float("nan"), dtype=case.torch_dtype, device=device)
+    vsa.vsa_fwd(p, d["q"], d["k"], d["v"], bmap, gate, buf.out, buf.lse,
                 buf.saved if training or backward else None, buf.ws_fwd)
     res = dict(out=buf.out, lse=buf.lse, map=bmap)
+    if proj:
+        res["gate_vals"] = gate
     if backward:
         dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
-        dg = torch.empty_like(d["gate"]) if d["gate"] is not None else None
-        vsa.vsa_bwd(p, d["q"], d["k"], d["v"], d["gate"], None if dout_none else d["dout"],
-                    buf.out, buf.lse, buf.saved, dq, dk, dv, dg, buf.ws_bwd)
+        if proj:
+            dg = torch.full((case.Hq * case.D + case.Hq,), float("nan"), dtype=torch.float32,
+                            device=device)
+        else:
+            dg = torch.empty_like(d["gate"]) if d["gate"] is not None else None
+        vsa.vsa_bwd(p, d["q"], d["k"], d["v"], None if proj else d["gate"],
+                    None if dout_none else d["dout"], buf.out, buf.lse, buf.saved, dq, dk, dv, dg,
+                    buf.ws_bwd)
         res.update(dq=dq, dk=dk, dv=dv, dgate=dg)
     torch.cuda.synchronize()
     if keep_device:

@@ -149,3 +149,31 @@ def test_backward_flags_are_checked():
     assert auto > span
     atomic = vsa.vsa_sizes(_prob(atomic_dq=True, persistent=False))["ws_bwd"]
     assert atomic >= span + 768 * 2 * 128 * 4  # the float dQ accumulator
+
+
+def test_projected_gate_problem_is_checked():
+    """VSA_GATE_PROJECTED needs gate_proj (16-byte aligned, [Hq*D + Hq] fp32)
+    and BHSD/BSHD; gate_proj with any other gate mode is INVALID_ARG; the
+    backward workspace grows by the per-row dL/dz and the per-Q-block
+    partial sums of dw and db."""
+    theta = torch.zeros(2 * 128 + 2, dtype=torch.float32)
+    vsa.vsa_validate(_prob(gate_mode="projected", gate_proj=theta))
+    vsa.vsa_validate(_prob(layout="bshd", gate_mode="projected", gate_proj=theta, topk=2))
+    p = _prob(gate_mode="projected", gate_proj=theta)
+    p.struct.gate_proj = None
+    assert _code(p)[0] == vsa.ERR_INVALID_ARG
+    p.struct.gate_proj = theta.data_ptr() + 4
+    c, m = _code(p)
+    assert c == vsa.ERR_INVALID_ARG and "aligned" in m
+    p = _prob(gate_mode="per_token")
+    p.struct.gate_proj = theta.data_ptr()
+    assert _code(p)[0] == vsa.ERR_INVALID_ARG
+    p = _prob(gate_mode="projected", gate_proj=theta)
+    p.struct.gate_mode = 4
+    assert _code(p)[0] == vsa.ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        _prob(gate_mode="projected", gate_proj=theta[:-1])
+    tok = vsa.vsa_sizes(_prob(gate_mode="per_token"))["ws_bwd"]
+    proj = vsa.vsa_sizes(_prob(gate_mode="projected", gate_proj=theta))["ws_bwd"]
+    rows, blocks = 2 * 768, 2 * 3
+    assert proj - tok >= 4 * (rows + blocks * 128 + blocks)

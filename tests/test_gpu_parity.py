@@ -457,3 +457,55 @@ def test_empty_kv_tiles_and_topk_above_the_live_tiles():
         for j in (1, 3):
             assert np.all(dk[:, :, j * 256:(j + 1) * 256] == 0) and \
                 np.all(dv[:, :, j * 256:(j + 1) * 256] == 0), (layout, j)
+
+
+def _projected_cases():
+    # GQA, top-k, two batch entries, a partial Q tile, an empty and a short KV tile
+    yield build_case("proj_gqa_bshd", dtype="bf16", layout="bshd", B=2, Hq=4, Hkv=2, D=128,
+                     q_var=[256, 61, 256], kv_var=[256, 0, 200, 256, 17], topk=3,
+                     map_kind="none", gate_mode="projected", seed=51)
+    # BHSD fp16 with unpadded inputs: padded q rows are live and get their own gate
+    yield build_case("proj_bhsd_fp16", dtype="fp16", layout="bhsd", B=1, Hq=2, Hkv=2, D=128,
+                     q_var=[256, 100], kv_var=[256, 256, 31], topk=2, map_kind="none",
+                     gate_mode="projected", pad_inputs=False, seed=52)
+    # a caller-given map, MQA, a ragged Q tail (q_var not given: whole tiles)
+    yield build_case("proj_map_mqa", dtype="bf16", layout="bshd", B=1, Hq=3, Hkv=1, D=128,
+                     q_block=128, kv_block=128, Sq=300, Skv=520, map_kind="per_row",
+                     map_per_row=2, gate_mode="projected", seed=53)
+
+
+@pytest.mark.parametrize("atomic_dq", [False, True], ids=["two_pass", "atomic_dq"])
+@pytest.mark.parametrize("case", list(_projected_cases()), ids=lambda c: c.name)
+def test_projected_gate_parity(case, atomic_dq):
+    """The gate projected from the query rows, sigmoid(<q, w_h> + b_h): the
+    gate values the forward writes, out, lse and every gradient, the
+    parameter gradient [dw | db] included, against the oracle in fp32."""
+    _say(f"[{case.name} atomic_dq={atomic_dq}] B={case.B} Hq={case.Hq} Sq={case.Sq}")
+    res = run_case(case, atomic_dq=atomic_dq)
+    orc = oracle.Oracle(case, np.float32)
+    if case.topk > 0:
+        assert _topk_agreement(orc, res["map"]).all(), "top-k near-tie in a small case"
+    gv = orc.gate_values()
+    # the gate values are rounded to the element type once
+    check("gate", gv, res["gate_vals"], (2e-3, 1e-2))
+    _compare_case(case, res, orc)
+    # [dw | db] is an fp32 sum of fp32 terms on both sides: a much tighter bar
+    dth = orc.bwd()[3]
+    avg_abs, max_rel = metrics(dth, res["dgate"])
+    _say(f"  dtheta avg_abs={avg_abs:.3e} max_rel={max_rel:.3e}")
+    assert max_rel < 1e-4, (avg_abs, max_rel)
+
+
+def test_projected_gate_without_dout_and_gate_output():
+    """dout = NULL gives zero gradients, [dw | db] included; the forward may
+    leave the gate values unwritten (gate = NULL) and then gives the same out."""
+    case = next(_projected_cases())
+    res = run_case(case, dout_none=True)
+    for n in ("dq", "dk", "dv", "dgate"):
+        assert np.all(res[n] == 0), n
+    d = device_inputs(case)
+    p = problem_for(case, d)
+    buf = vsa.Buffers(p, d["q"], training=False)
+    vsa.vsa_fwd(p, d["q"], d["k"], d["v"], None, None, buf.out, buf.lse, None, buf.ws_fwd)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.out.float().cpu().numpy(), res["out"])

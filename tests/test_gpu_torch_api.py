@@ -140,3 +140,27 @@ def test_vsa128_video_entries_against_the_oracle():
         check("out", o_ref, back(out.detach()).float().cpu().numpy(), OUT_TOL)
         for name, ref, t in (("dq", dq_r, q), ("dk", dk_r, k), ("dv", dv_r, v), ("dgate", dg_r, g)):
             check(name, ref, back(t.grad).float().cpu().numpy(), GRAD_TOL)
+
+
+def test_projected_gate_through_autograd():
+    """video_sparse_attn with gate_proj = (w, b): autograd returns exactly the
+    C ABI's dq, dk, dv and its [dw | db] split into w.grad and b.grad."""
+    case = build_case("proj_api", dtype="bf16", layout="bshd", B=1, Hq=4, Hkv=2, D=128,
+                      q_var=[256, 90, 256], kv_var=[256, 256, 0, 140], topk=2, map_kind="none",
+                      gate_mode="projected", seed=54, device="cuda")
+    ref = run_case(case, keep_device=True)
+    Hq, D = case.Hq, case.D
+    w = case.gate[:Hq * D].reshape(Hq, D).clone().requires_grad_(True)
+    b = case.gate[Hq * D:].clone().requires_grad_(True)
+    q, k, v = (_leaf(t) for t in (case.q, case.k, case.v))
+    out = vsa.video_sparse_attn_bshd(q, k, v, case.kv_var, case.q_var, case.topk,
+                                     block_size=(4, 8, 8), scale=case.scale, gate_proj=(w, b))
+    (out * case.dout.cuda()).sum().backward()
+    for name, a, r in (("out", out.detach(), ref["out"]), ("dq", q.grad, ref["dq"]),
+                       ("dk", k.grad, ref["dk"]), ("dv", v.grad, ref["dv"])):
+        assert torch.equal(a, r), f"{name} differs from the direct C-ABI run"
+    assert torch.equal(w.grad.reshape(-1), ref["dgate"][:Hq * D])
+    assert torch.equal(b.grad, ref["dgate"][Hq * D:])
+    with pytest.raises(ValueError):
+        vsa.video_sparse_attn_bshd(q, k, v, case.kv_var, case.q_var, case.topk,
+                                   gate_proj=(w[:, :64], b))

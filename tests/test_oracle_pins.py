@@ -366,6 +366,29 @@ def test_projected_gate_with_zero_weights_is_a_constant_gate():
                                atol=1e-12)
 
 
+def test_projected_gate_values():
+    """The oracle's projected gate values: with w = 0 they are sigmoid(b_h) on
+    every token (closed form), and with the case's own parameters out - O_sel
+    equals value * O_c of the token's Q tile (the composition of the gated
+    output, read back through the oracle's forward)."""
+    case = next(c for c in _gated_cases() if c.name == "gated_proj_gqa")
+    Hq, D = case.Hq, case.D
+    orc = oracle.Oracle(case)
+    gv = orc.gate_values()                      # [B, S, H]
+    out, osel, _ = orc.fwd()
+    oc = orc.coarse()[0]                        # [B, H, Qb, D]
+    tile = np.arange(case.Sq) // case.q_block
+    oc_tok = oc[:, :, tile, :].transpose(0, 2, 1, 3)  # [B, S, H, D]
+    np.testing.assert_allclose(out - osel, gv[..., None] * oc_tok, atol=1e-14)
+    assert np.all((gv > 0) & (gv < 1))
+    theta = case.gate.clone()
+    theta[:Hq * D] = 0
+    zero = dataclasses.replace(case, gate=theta)
+    gh = 1.0 / (1.0 + np.exp(-theta[Hq * D:].double().numpy()))
+    np.testing.assert_allclose(oracle.Oracle(zero).gate_values(),
+                               np.broadcast_to(gh, gv.shape), rtol=1e-15)
+
+
 def test_one_live_kv_tile_compression_closed_form():
     """A single KV tile with valid tokens: P_c = 1, so O_c = Vc (the mean of its
     valid v rows), dgate_s = <dO_s, Vc>, dS_c = 0 (no pooled term in dq, dk)
