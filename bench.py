@@ -154,19 +154,24 @@ def cpu_baseline(case, gpu_valid_pairs, target_s=12.0):
         o.bwd()
         return time.perf_counter() - t
 
-    # forward: calibrate on one tile, then size the sample to the time target
-    t0 = time.perf_counter()
+    # forward: a warm-up tile (thread start-up), a calibration on four tiles,
+    # then a sample sized to 40 % of the time target
     orc.fwd_rows(rows_of(tiles[:1]))
-    one = time.perf_counter() - t0
-    nf = int(max(1, min(len(tiles) - 1, 0.4 * target_s / max(one, 1e-3))))
-    fs = tiles[1:1 + nf]
+    t0 = time.perf_counter()
+    orc.fwd_rows(rows_of(tiles[1:5]))
+    one = (time.perf_counter() - t0) / 4
+    nf = int(max(1, min(len(tiles) // 2, 0.4 * target_s / max(one, 1e-4))))
+    fs = tiles[5:5 + nf]
     t0 = time.perf_counter()
     orc.fwd_rows(rows_of(fs))
     t_f = time.perf_counter() - t0
-    # backward: the same, on other tiles (calibrated on two, since a backward
-    # call also has fixed costs: the head's pooling, coarse branch, key scan)
-    one = bwd_of(tiles[:2]) / 2
-    nb = int(max(1, min(len(tiles) - 1, 0.6 * target_s / max(one, 1e-3))))
+    # backward: a call has a fixed cost (the head's pooling, coarse branch and
+    # key scan) besides its per-tile one; two calibration calls (2 and 8 tiles)
+    # separate them, and the sample is sized to 60 % of the time target
+    c2, c8 = bwd_of(tiles[-2:]), bwd_of(tiles[-8:])
+    per = max((c8 - c2) / 6, 1e-4)
+    fixed = max(c2 - 2 * per, 0.0)
+    nb = int(max(1, min(len(tiles) // 2, (0.6 * target_s - fixed) / per)))
     bs = tiles[-nb:]
     t_b = bwd_of(bs)
     pf, pb = pairs(fs), pairs(bs)
