@@ -36,7 +36,7 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_fwd_kernel(const FwdArgs a)
   const int hl = lane >> 5, l32 = lane & 31;
 
   const int nsub = max(1, g.q_block / (32 * NW));  // Q blocks of 8 or 16 rows: one wave
-  int id = xcd_group(blockIdx.x, gridDim.x, nsub);
+  int id = xcd_group(blockIdx.x, gridDim.x, nsub * XCD_QBLOCKS);
   const int sub = id % nsub;
   id /= nsub;
   const int i = id % g.Qb;
