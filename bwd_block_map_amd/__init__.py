@@ -27,7 +27,7 @@ BF16, FP16 = 0, 1
 BHSD, BSHD, TND = 0, 1, 2
 GATE_NONE, GATE_PER_TOKEN, GATE_PER_ELEMENT, GATE_PROJECTED = 0, 1, 2, 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-ABI_VERSION = 3
+ABI_VERSION = 4
 FLAG_ATOMIC_DQ = 1
 FLAG_PERSISTENT = 2
 FLAG_NO_PERSISTENT = 4
@@ -63,6 +63,7 @@ class VsaProblem(C.Structure):
         ("max_seqlen_q", C.c_int32), ("max_seqlen_kv", C.c_int32),
         ("scale", C.c_float), ("topk", C.c_int32), ("gate_mode", C.c_int32),
         ("map_batch_stride", C.c_int64), ("flags", C.c_int32), ("gate_proj", C.c_void_p),
+        ("q_valid_batch_stride", C.c_int64), ("kv_valid_batch_stride", C.c_int64),
     ]
 
 
@@ -138,7 +139,9 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
                  gate_mode: str = "none", map_batch_stride: Optional[int] = None,
                  atomic_dq: bool = False, persistent: Optional[bool] = None,
                  gate_proj: Optional[torch.Tensor] = None) -> Problem:
-    """Fill a vsa_problem. q_valid / kv_valid / cu_seqlens are int32 device tensors.
+    """Fill a vsa_problem. q_valid / kv_valid / cu_seqlens are int32 device tensors;
+    q_valid / kv_valid are [Qb] / [KVb] (one set for every batch entry) or
+    [B, Qb] / [B, KVb] (per entry).
     gate_proj (gate_mode "projected"): the gate's parameters, a contiguous
     float32 device tensor [w (Hq x D) | b (Hq)].
     atomic_dq selects the backward that adds dQ inside the KV-owned pass
@@ -165,9 +168,16 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
             raise ValueError(f"gate_proj must be a contiguous float32 tensor of Hq*D+Hq = "
                              f"{Hq * D + Hq} elements")
         keep = keep + (gate_proj,)
+    strides = []
     for t, n, name in ((q_valid, Qb, "q_valid"), (kv_valid, KVb, "kv_valid")):
+        if t is not None and t.dim() == 2:
+            if tuple(t.shape) != (B, n):
+                raise ValueError(f"{name} must be [{n}] or [{B}, {n}], got {tuple(t.shape)}")
+            strides.append(n)
+            continue
         if t is not None and t.numel() != n:
             raise ValueError(f"{name} needs {n} entries, got {t.numel()}")
+        strides.append(0)
     for t, total, mx, name in ((cu_seqlens_q, Sq, max_seqlen_q, "cu_seqlens_q"),
                                (cu_seqlens_kv, Skv, max_seqlen_kv, "cu_seqlens_kv")):
         if t is not None and lay == TND and t.is_cuda:
@@ -190,7 +200,8 @@ def make_problem(*, dtype: torch.dtype, layout: str, B: int, Hq: int, Hkv: int, 
         gate_mode=_GATES[gate_mode], map_batch_stride=map_batch_stride,
         flags=(FLAG_ATOMIC_DQ if atomic_dq else 0)
         | {None: 0, True: FLAG_PERSISTENT, False: FLAG_NO_PERSISTENT}[persistent],
-        gate_proj=None if gate_proj is None else gate_proj.data_ptr())
+        gate_proj=None if gate_proj is None else gate_proj.data_ptr(),
+        q_valid_batch_stride=strides[0], kv_valid_batch_stride=strides[1])
     return Problem(s, keep)
 
 

@@ -73,6 +73,7 @@ struct Geom {
   int layout, B, Hq, Hkv, Sq, Skv, q_block, kv_block, Qb, KVb, group;
   const int32_t* q_valid;
   const int32_t* kv_valid;
+  long long qv_bs, kvv_bs;  // entries between batch entries of the counts (0: shared)
   const int32_t* cu_q;
   const int32_t* cu_kv;
   float scale;
@@ -100,11 +101,11 @@ struct Geom {
   // valid rows / keys of a block: the tile count when given, never more than exist
   __device__ __forceinline__ int q_val(int b, int i) const {
     const int e = q_exist(b, i);
-    return q_valid ? min(q_valid[i], e) : e;
+    return q_valid ? min(q_valid[b * qv_bs + i], e) : e;
   }
   __device__ __forceinline__ int kv_val(int b, int j) const {
     const int e = kv_exist(b, j);
-    return kv_valid ? min(kv_valid[j], e) : e;
+    return kv_valid ? min(kv_valid[b * kvv_bs + j], e) : e;
   }
   // element offset of row 0 of (b, head) and the distance between rows
   __device__ __forceinline__ long long q_base(int b, int h) const {

@@ -36,13 +36,11 @@ __device__ __forceinline__ void walk_kv(const Geom& g, int b, int hk, const int3
   const int tid = wave * 64 + lane;
   const long long kvb = uniform_i64(g.kv_base(b, hk)), krs = g.kv_rs();
   const uint32_t krs_bytes = (uint32_t)(krs * 2);
-  const int kvlen = g.kv_len(b);
   auto load_page = [&](int base) {
     for (int t = tid; t < KV_LIST_CAP && base + t < cnt; t += NW * 64) {
       const int j = col[e0 + base + t];
-      const int ex = max(0, min(g.kv_block, kvlen - j * g.kv_block));
       lst_j[t] = j;
-      lst_v[t] = g.kv_valid ? min(g.kv_valid[j], ex) : ex;
+      lst_v[t] = g.kv_val(b, j);
     }
   };
   load_page(0);

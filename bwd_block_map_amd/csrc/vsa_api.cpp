@@ -244,6 +244,8 @@ vsa::Geom make_geom(const vsa_problem* p) {
   g.group = p->Hq / p->Hkv;
   g.q_valid = p->q_valid;
   g.kv_valid = p->kv_valid;
+  g.qv_bs = p->q_valid_batch_stride;
+  g.kvv_bs = p->kv_valid_batch_stride;
   g.cu_q = p->cu_seqlens_q;
   g.cu_kv = p->cu_seqlens_kv;
   g.scale = p->scale;
@@ -286,6 +288,15 @@ int validate(const vsa_problem* p) {
   if (p->gate_proj && ((uintptr_t)p->gate_proj & 15u))
     return fail(VSA_ERR_INVALID_ARG, "gate_proj must be 16-byte aligned");
   if (p->map_batch_stride < 0) return fail(VSA_ERR_INVALID_ARG, "map_batch_stride must be >= 0");
+  if (p->q_valid_batch_stride < 0 || p->kv_valid_batch_stride < 0)
+    return fail(VSA_ERR_INVALID_ARG, "q_valid_batch_stride / kv_valid_batch_stride must be >= 0");
+  if ((p->q_valid_batch_stride && !p->q_valid) || (p->kv_valid_batch_stride && !p->kv_valid))
+    return fail(VSA_ERR_INVALID_ARG, "a valid-count batch stride needs the counts it strides");
+  if ((p->q_valid_batch_stride && p->q_valid_batch_stride < p->Qb) ||
+      (p->kv_valid_batch_stride && p->kv_valid_batch_stride < p->KVb))
+    return fail(VSA_ERR_INVALID_ARG,
+                "a valid-count batch stride must be 0 or at least Qb / KVb (got %lld / %lld)",
+                (long long)p->q_valid_batch_stride, (long long)p->kv_valid_batch_stride);
   constexpr int kFlags = VSA_FLAG_ATOMIC_DQ | VSA_FLAG_PERSISTENT | VSA_FLAG_NO_PERSISTENT;
   if (p->flags & ~kFlags)
     return fail(VSA_ERR_INVALID_ARG, "flags: unknown bits 0x%x", p->flags & ~kFlags);

@@ -34,11 +34,13 @@ Counts = Optional[Union[torch.Tensor, Sequence[int]]]
 
 
 def _counts(x: Counts, device) -> Optional[torch.Tensor]:
-    """Per-tile valid counts as a contiguous int32 tensor on `device`."""
+    """Per-tile valid counts as a contiguous int32 tensor on `device`: [tiles]
+    (shared by the batch) or [B, tiles] (per batch entry)."""
     if x is None:
         return None
     t = torch.as_tensor(x, dtype=torch.int32)
-    return t.to(device).contiguous().view(-1)
+    t = t.to(device).contiguous()
+    return t if t.dim() == 2 else t.view(-1)
 
 
 def gate_mode_of(gate: Optional[torch.Tensor], q: torch.Tensor, layout: str) -> str:
@@ -217,7 +219,8 @@ def video_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_var:
                       ) -> torch.Tensor:
     """Video sparse attention over [B, H, S, D] tensors laid out in tiles of
     prod(block_size) tokens: each Q tile attends to its `topk` KV tiles of
-    highest pooled score (q_var / kv_var valid tokens per tile); with
+    highest pooled score (q_var / kv_var valid tokens per tile, [tiles] for the
+    whole batch or [B, tiles] per video); with
     compress_attn_weight (or the projected gate gate_proj = (w, b)) the gated
     pooled-tile branch is added. Returns out."""
     return _video(q, k, v, kv_var, q_var, topk, block_size, compress_attn_weight, scale, "bhsd",

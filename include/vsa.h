@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 3
+#define VSA_ABI_VERSION 4
 
 enum vsa_status {
   VSA_OK = 0,
@@ -101,8 +101,9 @@ enum vsa_gate_mode {
  *   kv_block      keys per KV block, a multiple of 64
  *   Qb, KVb       blocks per batch entry: ceil(Sq/q_block), ceil(Skv/kv_block)
  *                 (TND: of the longest sequence)
- *   q_valid       device int32 [Qb] valid rows per Q tile, or NULL (= all rows)
- *   kv_valid      device int32 [KVb] valid keys per KV tile, or NULL
+ *   q_valid       device int32 [Qb] valid rows per Q tile, or NULL (= all rows);
+ *                 [B, q_valid_batch_stride] with a per-entry stride (below)
+ *   kv_valid      device int32 [KVb] valid keys per KV tile, or NULL; likewise
  *   cu_seqlens_q  TND only: device int32 [B+1], exclusive prefix sums of the
  *   cu_seqlens_kv per-sequence lengths (cu[0] = 0, cu[B] = Tq / Tkv)
  *   max_seqlen_q  TND only: the longest q / kv sequence (sizes Qb, KVb)
@@ -123,6 +124,13 @@ enum vsa_gate_mode {
  *                 by the biases b ([Hq]); NULL otherwise
  *   map_batch_stride  elements between batch entries of block_map;
  *                 0 = one [Hq, Qb, KVb] map shared by every batch entry
+ *   q_valid_batch_stride, kv_valid_batch_stride  entries between the batch
+ *                 entries of q_valid / kv_valid: 0 = one set of counts shared
+ *                 by every batch entry (videos of one shape), else at least
+ *                 Qb / KVb (a batch of videos with different tile fill, e.g.
+ *                 different latent sizes padded to one tile grid; entry b's
+ *                 counts start at b * stride). BHSD/BSHD only; the counts
+ *                 must then be given.
  *   flags         0, or VSA_FLAG_ATOMIC_DQ: vsa_bwd computes dQ inside the
  *                 KV-owned dK/dV pass (dS K of every selected block added to
  *                 a float accumulator in the backward workspace with atomics,
@@ -158,6 +166,8 @@ typedef struct vsa_problem {
   int64_t map_batch_stride;
   int32_t flags;
   const float* gate_proj;
+  int64_t q_valid_batch_stride;
+  int64_t kv_valid_batch_stride;
 } vsa_problem;
 
 #define VSA_FLAG_ATOMIC_DQ 1

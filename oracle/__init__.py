@@ -37,6 +37,7 @@ class OracleProblem(C.Structure):
         ("q_var", C.POINTER(C.c_int32)), ("kv_var", C.POINTER(C.c_int32)),
         ("q_lens", C.POINTER(C.c_int32)), ("kv_lens", C.POINTER(C.c_int32)),
         ("scale", C.c_double), ("gate_mode", C.c_int32), ("threads", C.c_int32),
+        ("q_var_bstride", C.c_int64), ("kv_var_bstride", C.c_int64),
     ]
 
 
@@ -71,6 +72,10 @@ def _ptr(a: Optional[np.ndarray], ct):
     return a.ctypes.data_as(C.POINTER(ct))
 
 
+def _bstride(var) -> int:
+    return 0 if var is None or np.ndim(var) < 2 else int(np.shape(var)[1])
+
+
 class Prob:
     """ctypes problem for a workload case, keeping its int arrays alive."""
 
@@ -90,7 +95,9 @@ class Prob:
             Skv=case.Skv, D=case.D, q_block=case.q_block, kv_block=case.kv_block, Qb=case.Qb,
             KVb=case.KVb, q_var=arr(case.q_var), kv_var=arr(case.kv_var), q_lens=arr(case.q_lens),
             kv_lens=arr(case.kv_lens), scale=float(case.scale), gate_mode=_GATE[case.gate_mode],
-            threads=int(threads))
+            threads=int(threads),
+            # [B, tiles] counts: one row per batch entry
+            q_var_bstride=_bstride(case.q_var), kv_var_bstride=_bstride(case.kv_var))
 
     @property
     def ref(self):

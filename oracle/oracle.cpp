@@ -66,6 +66,9 @@ typedef struct oracle_problem {
   // with the gate argument holding the parameters [w (Hq x D) | b (Hq)]
   int32_t gate_mode;
   int32_t threads;    // OpenMP threads, 0 = runtime default
+  // entries between the batch entries of q_var / kv_var: 0 = one set of
+  // counts for every batch entry, else entry b's counts start at b * stride
+  int64_t q_var_bstride, kv_var_bstride;
 } oracle_problem;
 }
 
@@ -100,11 +103,11 @@ struct Geo {
   // valid tokens: the tile count when given, never beyond what exists
   int q_valid(int b, int i) const {
     int e = q_exist(b, i);
-    return p.q_var ? std::min(p.q_var[i], e) : e;
+    return p.q_var ? std::min(p.q_var[b * p.q_var_bstride + i], e) : e;
   }
   int kv_valid(int b, int j) const {
     int e = kv_exist(b, j);
-    return p.kv_var ? std::min(p.kv_var[j], e) : e;
+    return p.kv_var ? std::min(p.kv_var[b * p.kv_var_bstride + j], e) : e;
   }
   // offset of element (b, h, s, 0) of a q-shaped / kv-shaped tensor
   int64_t q_off(int b, int h, int s) const {

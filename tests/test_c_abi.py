@@ -177,3 +177,24 @@ def test_projected_gate_problem_is_checked():
     proj = vsa.vsa_sizes(_prob(gate_mode="projected", gate_proj=theta))["ws_bwd"]
     rows, blocks = 2 * 768, 2 * 3
     assert proj - tok >= 4 * (rows + blocks * 128 + blocks)
+
+
+def test_per_entry_valid_counts_are_checked():
+    """[B, tiles] counts set the batch strides to Qb / KVb; a stride below the
+    tile count, a negative one, or one without its counts is INVALID_ARG."""
+    qv = torch.full((1, 3), 256, dtype=torch.int32)
+    kv = torch.full((1, 4), 256, dtype=torch.int32)
+    p = _prob(q_valid=qv, kv_valid=kv)
+    assert (p.struct.q_valid_batch_stride, p.struct.kv_valid_batch_stride) == (3, 4)
+    vsa.vsa_validate(p)
+    assert _prob(q_valid=qv[0], kv_valid=kv[0]).struct.q_valid_batch_stride == 0
+    p.struct.q_valid_batch_stride = 2
+    assert _code(p)[0] == vsa.ERR_INVALID_ARG
+    p.struct.q_valid_batch_stride = -3
+    assert _code(p)[0] == vsa.ERR_INVALID_ARG
+    p = _prob()
+    p.struct.kv_valid_batch_stride = 4
+    c, m = _code(p)
+    assert c == vsa.ERR_INVALID_ARG and "needs the counts" in m
+    with pytest.raises(ValueError):
+        _prob(B=2, q_valid=torch.full((3, 3), 256, dtype=torch.int32))

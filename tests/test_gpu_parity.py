@@ -509,3 +509,26 @@ def test_projected_gate_without_dout_and_gate_output():
     vsa.vsa_fwd(p, d["q"], d["k"], d["v"], None, None, buf.out, buf.lse, None, buf.ws_fwd)
     torch.cuda.synchronize()
     assert np.array_equal(buf.out.float().cpu().numpy(), res["out"])
+
+
+def test_per_entry_valid_counts():
+    """Valid counts per batch entry ([B, tiles], the stride fields of the
+    problem): pooled top-k with the gate in BSHD, and a caller map in BHSD
+    fp16 with an entry whose Q tile and KV tile are empty."""
+    cases = [
+        build_case("per_entry_gated", dtype="bf16", layout="bshd", B=2, Hq=4, Hkv=2, D=128,
+                   q_var=[[256, 61, 256], [100, 256, 17]],
+                   kv_var=[[256, 0, 200, 256, 17], [64, 256, 256, 0, 130]], topk=3,
+                   map_kind="none", gate_mode="per_token", seed=71),
+        build_case("per_entry_map", dtype="fp16", layout="bhsd", B=3, Hq=2, Hkv=1, D=128,
+                   q_var=[[256, 256], [0, 200], [31, 256]],
+                   kv_var=[[256, 99, 256], [256, 256, 0], [1, 256, 64]], map_kind="per_row",
+                   map_per_row=2, seed=72),
+    ]
+    for case in cases:
+        _say(f"[{case.name}] B={case.B} q_var={case.q_var.tolist()} kv_var={case.kv_var.tolist()}")
+        res = run_case(case)
+        orc = oracle.Oracle(case, np.float32)
+        if case.topk > 0:
+            assert _topk_agreement(orc, res["map"]).all(), "top-k near-tie in a small case"
+        _compare_case(case, res, orc)

@@ -164,3 +164,17 @@ def test_projected_gate_through_autograd():
     with pytest.raises(ValueError):
         vsa.video_sparse_attn_bshd(q, k, v, case.kv_var, case.q_var, case.topk,
                                    gate_proj=(w[:, :64], b))
+
+
+def test_per_video_counts_through_the_video_entry():
+    """video_sparse_attn with [B, tiles] counts (one row per video) gives
+    exactly the C ABI's outputs and gradients for the same problem."""
+    case = build_case("per_video", dtype="bf16", layout="bhsd", B=2, Hq=2, D=128,
+                      q_var=[[256, 90, 256], [256, 256, 40]],
+                      kv_var=[[256, 256, 0, 140], [70, 256, 256, 256]], topk=2, map_kind="none",
+                      gate_mode="per_token", seed=73, device="cuda")
+    ref = run_case(case, keep_device=True)
+    out, dq, dk, dv, dgate = _video_autograd(case, "bhsd", gate_grad=True)
+    for name, a, b in (("out", out, ref["out"]), ("dq", dq, ref["dq"]), ("dk", dk, ref["dk"]),
+                       ("dv", dv, ref["dv"]), ("dgate", dgate, ref["dgate"])):
+        assert torch.equal(a, b), f"{name} differs from the direct C-ABI run"

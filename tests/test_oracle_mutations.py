@@ -75,6 +75,8 @@ MUTANTS = [
      "d[e] += gv * dout[qo + e];", "d[e] += dout[qo + e];"),
     ("coarse_dv_missing_softmax_weight",
      "dv[e] += pc * dO[e];", "dv[e] += dO[e];"),
+    ("per_entry_counts_ignore_the_batch_entry",
+     "p.kv_var[b * p.kv_var_bstride + j]", "p.kv_var[j]"),
     ("tnd_blocks_not_clipped_to_sequence",
      "if (i >= nqb(b) || j >= nkb(b)) return false;", "if (i >= p.Qb || j >= p.KVb) return false;"),
 ]

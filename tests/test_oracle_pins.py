@@ -660,3 +660,31 @@ def test_sampled_tiles_match_full_backward():
         for n, (b, hk, j) in enumerate(tiles):
             np.testing.assert_allclose(tk[n], dk[b, j * 8:(j + 1) * 8, hk], atol=1e-14)  # BSHD
             np.testing.assert_allclose(tv[n], dv[b, j * 8:(j + 1) * 8, hk], atol=1e-14)
+
+
+def test_per_entry_valid_counts_equal_separate_runs():
+    """Valid counts given per batch entry ([B, tiles]): each entry's out, lse,
+    selection and gradients are those of that entry run alone (B = 1) with its
+    own counts -- batch entries share nothing but the launch."""
+    q_var = [[8, 3, 8], [5, 8, 2]]
+    kv_var = [[8, 1, 0, 8, 5], [6, 8, 8, 3, 0]]
+    case = build_case("per_entry", dtype="bf16", layout="bshd", B=2, Hq=4, Hkv=2, D=16,
+                      q_block=8, kv_block=8, q_var=q_var, kv_var=kv_var, topk=2,
+                      map_kind="none", gate_mode="per_token", seed=61)
+    orc = oracle.Oracle(case)
+    full = orc.fwd()
+    grads = orc.bwd()
+    m = orc.block_map()
+    for b in range(2):
+        one = dataclasses.replace(
+            case, B=1, q_var=np.asarray(q_var[b], np.int32), kv_var=np.asarray(kv_var[b], np.int32),
+            q=case.q[b:b + 1], k=case.k[b:b + 1], v=case.v[b:b + 1], dout=case.dout[b:b + 1],
+            gate=case.gate[b:b + 1])
+        ref = oracle.Oracle(one)
+        assert np.array_equal(m[b:b + 1], ref.block_map()), b
+        for got, want in zip(full, ref.fwd()):
+            np.testing.assert_allclose(got[b:b + 1], want, rtol=0, atol=1e-15)
+        for got, want in zip(grads, ref.bwd()):
+            np.testing.assert_allclose(got[b:b + 1], want, rtol=0, atol=1e-15)
+    # and the two entries really differ in their counts' effect
+    assert not np.array_equal(m[0], m[1])

@@ -49,8 +49,8 @@ class Case:
     scale: float
     topk: int = 0              # 0: the block map below is the selection
     gate_mode: str = "none"    # "none" | "per_token" | "per_element" | "projected"
-    q_var: Optional[np.ndarray] = None    # int32 [Qb] valid tokens per Q tile
-    kv_var: Optional[np.ndarray] = None   # int32 [KVb] valid tokens per KV tile
+    q_var: Optional[np.ndarray] = None    # int32 [Qb] (or [B, Qb]) valid tokens per Q tile
+    kv_var: Optional[np.ndarray] = None   # int32 [KVb] (or [B, KVb]) valid tokens per KV tile
     q_lens: Optional[List[int]] = None    # TND per-sequence lengths
     kv_lens: Optional[List[int]] = None
     block_map: Optional[torch.Tensor] = None  # uint8 [B, Hq, Qb, KVb], CPU
@@ -90,13 +90,14 @@ def _randn(gen: torch.Generator, shape, dtype: torch.dtype, device) -> torch.Ten
 
 def _tile_valid_mask(var: np.ndarray, block: int, layout: str, device) -> torch.Tensor:
     """1 where a slot of the tile buffer holds a token, broadcastable to the
-    tensor layout ([B,H,S,D] or [B,S,H,D])."""
-    idx = torch.arange(block, device=device).view(1, -1)
-    valid = idx < torch.as_tensor(var, device=device).view(-1, 1).to(torch.int64)
-    valid = valid.reshape(-1)
+    tensor layout ([B,H,S,D] or [B,S,H,D]); var is [tiles] or [B, tiles]."""
+    cnt = torch.as_tensor(var, device=device).to(torch.int64)
+    cnt = cnt.view(1, -1) if cnt.dim() == 1 else cnt
+    idx = torch.arange(block, device=device).view(1, 1, -1)
+    valid = (idx < cnt.unsqueeze(-1)).reshape(cnt.shape[0], -1)
     if layout == "bhsd":
-        return valid.view(1, 1, -1, 1)
-    return valid.view(1, -1, 1, 1)
+        return valid.view(cnt.shape[0], 1, -1, 1)
+    return valid.view(cnt.shape[0], -1, 1, 1)
 
 
 def build_case(
@@ -131,7 +132,8 @@ def build_case(
 ) -> Case:
     """Draw one case. Exactly one of (Sq/Skv, q_var/kv_var, q_lens/kv_lens)
     describes the sequence geometry:
-      * q_var / kv_var: video tiles, Sq = len(q_var) * q_block (tile buffer);
+      * q_var / kv_var: video tiles, Sq = tiles * q_block (tile buffer); one
+        count per tile ([tiles]) or per batch entry and tile ([B, tiles]);
       * q_lens / kv_lens: packed TND sequences;
       * Sq / Skv: plain BHSD/BSHD sequences (the last block may be partial).
     map_kind: "bernoulli" (p = map_p, at least one block per Q block),
@@ -152,7 +154,9 @@ def build_case(
     elif q_var is not None:
         q_var = np.asarray(q_var, dtype=np.int32)
         kv_var = np.asarray(kv_var, dtype=np.int32)
-        Qb, KVb = len(q_var), len(kv_var)
+        for var in (q_var, kv_var):
+            assert var.ndim == 1 or var.shape[0] == B, "per-entry counts need one row per batch entry"
+        Qb, KVb = q_var.shape[-1], kv_var.shape[-1]
         Sq, Skv = Qb * q_block, KVb * kv_block
     else:
         Skv = Sq if Skv is None else Skv
