@@ -123,6 +123,79 @@ __global__ __launch_bounds__(1024) void index_scan(int32_t* __restrict__ row_ptr
   if (t == 0) row_ptr[0] = 0;
 }
 
+// Small maps in one launch (the three launches above cost more than the work
+// for, e.g., a [2, 8, 32, 32] map): one work-group stages the map in LDS with
+// coalesced loads, counts every row there (a thread per row), scans the counts,
+// writes row_ptr and fills col. Same CSR as the three-kernel path.
+constexpr int SMALL_ROWS = 8192;       // rows whose counts fit in LDS
+constexpr int SMALL_MAP = 64 * 1024;   // map bytes staged in LDS
+
+__global__ __launch_bounds__(1024) void index_small(Geom g, const uint8_t* __restrict__ map,
+                                                    int kv_owned, int32_t* __restrict__ row_ptr,
+                                                    int32_t* __restrict__ col, long long cap) {
+  __shared__ uint8_t mp[SMALL_MAP];
+  __shared__ int32_t start[SMALL_ROWS];
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int nr = kv_owned ? g.KVb : g.Qb;
+  const int rows = g.B * g.Hq * nr;
+  const int per_b = g.Hq * g.Qb * g.KVb;
+  const int staged = (g.map_bstride ? g.B : 1) * per_b;
+  for (int x = t; x < staged; x += 1024) mp[x] = map[(x / per_b) * g.map_bstride + x % per_b];
+  __syncthreads();
+  // the live entries of row r in ascending column order: fn(column)
+  auto walk = [&](int r, auto&& fn) {
+    const int x = r % nr, bh = r / nr;
+    const int h = bh % g.Hq, b = bh / g.Hq;
+    const uint8_t* m = mp + (g.map_bstride ? b : 0) * per_b + h * g.Qb * g.KVb;
+    if (!kv_owned) {
+      if (x >= g.nqb(b)) return;
+      const int nk = g.nkb(b);
+      for (int j = 0; j < nk; ++j)
+        if (m[x * g.KVb + j] != 0 && g.kv_val(b, j) > 0) fn(j);
+    } else {
+      if (x >= g.nkb(b) || g.kv_val(b, x) == 0) return;
+      const int nq = g.nqb(b);
+      for (int i = 0; i < nq; ++i)
+        if (m[i * g.KVb + x] != 0) fn(i);
+    }
+  };
+  for (int r = t; r < rows; r += 1024) {
+    int c = 0;
+    walk(r, [&](int) { ++c; });
+    start[r] = c;
+  }
+  __syncthreads();
+  // exclusive scan: contiguous segments per thread, their sums scanned in LDS
+  const int per = (rows + 1023) / 1024, beg = min(t * per, rows), end = min(beg + per, rows);
+  int32_t s = 0;
+  for (int r = beg; r < end; ++r) s += start[r];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int32_t acc = part[t] - s;
+  for (int r = beg; r < end; ++r) {
+    const int32_t c = start[r];
+    start[r] = acc;
+    acc += c;
+  }
+  __syncthreads();
+  for (int r = t; r < rows; r += 1024) {
+    row_ptr[r] = start[r];
+    long long pos = start[r];
+    walk(r, [&](int c) {
+      if (pos < cap) col[pos] = c;
+      ++pos;
+    });
+  }
+  if (t == 0) row_ptr[rows] = part[1023];
+}
+
 // a[1 .. n] holds counts; afterwards a[0] = 0 and a[r] = the sum of the first r
 hipError_t launch_exclusive_scan(int32_t* a, long long n, hipStream_t st) {
   index_scan<<<1, 1024, 0, st>>>(a, n);
@@ -136,7 +209,10 @@ hipError_t launch_index(const Geom& g, const uint8_t* map, int kv_owned, int32_t
     index_scan<<<1, 1024, 0, st>>>(row_ptr, 0);
     return hipGetLastError();
   }
-  if (!kv_owned) {
+  const long long staged = (g.map_bstride ? g.B : 1LL) * g.Hq * g.Qb * g.KVb;
+  if (rows <= SMALL_ROWS && staged <= SMALL_MAP) {
+    index_small<<<1, 1024, 0, st>>>(g, map, kv_owned, row_ptr, col, cap);
+  } else if (!kv_owned) {
     const unsigned grid = (unsigned)((rows + 3) / 4);
     index_count_q<<<grid, 256, 0, st>>>(g, map, row_ptr);
     index_scan<<<1, 1024, 0, st>>>(row_ptr, rows);

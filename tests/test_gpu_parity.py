@@ -199,6 +199,10 @@ def _index_cases():
     yield build_case("idx_empty", B=2, Hq=2, D=128, q_block=64, kv_block=64,
                      q_var=[64, 64, 10], kv_var=[64, 0, 7, 0, 64], map_kind="bernoulli",
                      map_p=0.6, seed=3)
+    # over 8192 rows and a million map entries in both directions: the
+    # multi-launch build (the cases above take the one-launch one)
+    yield build_case("idx_big", B=1, Hq=8, D=128, q_block=8, kv_block=64, Sq=8800, Skv=8800,
+                     map_kind="bernoulli", map_p=0.1, seed=5)
 
 
 @pytest.mark.parametrize("case", list(_index_cases()), ids=lambda c: c.name)
