@@ -11,17 +11,23 @@
 // gfx950 design.
 //  * bwd_pre: one work-group per (b, h, Q block); coalesced 16-byte loads of
 //    dO and O_sel, 16-lane shuffles for the row dot products; with a gate it
-//    also sums gate * dO over the tile (LDS) and forms dgate; it also writes
+//    also sums gate * dO over the tile (LDS) and forms dgate (a projected gate
+//    is recomputed from the query row: dL/dz per row and per-block partial
+//    sums of dw, db, summed per head by gate_proj_grad_kernel); it also writes
 //    lse * log2(e) for the exp2-based recomputation of P.
 //  * dK/dV: one 8-wave work-group per span of up to 256 keys of a KV block, in
-//    one of three shapes picked by the span's live keys (below). The K tile
-//    stays in LDS, V^T columns and the dK^T / dV^T accumulators in registers;
-//    the heads of the group and the Q blocks of the KV-owned list are walked
-//    in row chunks that arrive in LDS through a ring of direct loads. No
-//    atomics: one plain store per element at the end.
+//    one of three shapes picked by the span's live keys (below); on large
+//    problems a persistent grid takes the spans longest first from a device
+//    list. The K tile stays in LDS, V^T columns and the dK^T / dV^T
+//    accumulators in registers; the heads of the group and the Q blocks of the
+//    KV-owned list are walked in row chunks that arrive in LDS through a ring
+//    of direct loads. No atomics: one plain store per element at the end
+//    (the opt-in atomic-dQ variant adds dS K of every chunk to a float dQ
+//    accumulator instead of running the dQ pass).
 //  * dQ: like the forward (Q-owned list, 64-key chunks through the shared
 //    K/V ring walker, S^T and dP^T with lane = query row); dQ^T += K^T dS^T
-//    with K^T read transposed from the K tile.
+//    with K^T read transposed from the K tile; the epilogue adds the pooled
+//    compression term and, for a projected gate, dL/dz * w_h.
 #include "kernels.hpp"
 #include "kv_walk.hpp"
 

@@ -10,8 +10,8 @@
 // gfx950 design. One work-group = NW waves x 32 rows of one Q block; every
 // wave keeps its 32 query rows in registers as MFMA B operands and walks the
 // block's KV list in chunks of 64 keys. K and V chunks go global -> LDS with
-// direct 16-byte loads (no staging registers), double-buffered: the next
-// chunk is in flight while this one is computed. Scores are formed
+// direct 16-byte loads (no staging registers) into a ring of NST slots, so
+// NST - 1 chunks are in flight while one is computed (kv_walk.hpp). Scores are formed
 // transposed, S^T = K Q^T with v_mfma_f32_32x32x16, so each lane owns one
 // query row and the row max / sum are in-lane plus one exchange with lane ^ 32.
 // P^T stays in registers as the B operand of O^T += V^T P^T; the V^T operand
