@@ -205,16 +205,26 @@ STAGE_KERNELS = {"sparse_fwd": "sparse_fwd_kernel", "sparse_dkdv": "sparse_dkdv_
                  "sparse_dq": "sparse_dq_kernel"}
 
 
-def kernel_source_hash():
-    """sha256 over the device sources (.hip kernels and their headers; the
-    host-side C ABI is left out): a traffic figure is only reported for the
-    kernels it was measured on."""
+def _code_only(text):
+    """C++ source without its comments and blank lines (a comment edit does not
+    change what the kernels do)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
+def kernel_source_hash(csrc=None):
+    """sha256 over the device sources (.hip kernels and their headers, comments
+    left out; the host-side C ABI is left out too): a traffic figure is only
+    reported for the kernels it was measured on."""
     import hashlib
+    csrc = CSRC if csrc is None else csrc
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name)) as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 
