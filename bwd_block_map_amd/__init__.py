@@ -37,7 +37,7 @@ EXPORTS = ("vsa_last_error", "vsa_abi_version", "vsa_validate", "vsa_sizes",
            "vsa_profile_end")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # VSA_NOALLOC_SCRATCH_BYTES
 KERNELS = ("index", "pool", "coarse_fwd", "sparse_fwd", "bwd_pre", "coarse_bwd", "sparse_dkdv",
-           "sparse_dq", "dq_atomic_aux", "dkdv_order")
+           "sparse_dq", "dq_atomic_aux", "dkdv_order", "pad")
 
 _DTYPES = {torch.bfloat16: BF16, torch.float16: FP16}
 _LAYOUTS = {"bhsd": BHSD, "bshd": BSHD, "tnd": TND}

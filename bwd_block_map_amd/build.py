@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvsa.so")
-SOURCES = ["index.hip", "coarse.hip", "attn_fwd.hip", "attn_bwd.hip", "vsa_api.cpp"]
+SOURCES = ["index.hip", "coarse.hip", "attn_fwd.hip", "attn_bwd.hip", "pad.hip", "vsa_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

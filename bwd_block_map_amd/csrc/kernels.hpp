@@ -119,6 +119,12 @@ long long lpt_hist_entries(const Geom& g);  // int32 entries of the order's hist
 hipError_t launch_lpt_order(const BwdArgs& a, int32_t* hist, int32_t* order, hipStream_t st);
 hipError_t launch_exclusive_scan(int32_t* a, long long n, hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+// rows of D elements (2 or 4 bytes) <-> rows of HD elements, the extra ones zero
+hipError_t launch_widen_rows(const void* src, void* dst, long long rows, int D, int elem_bytes,
+                             hipStream_t st);
+hipError_t launch_narrow_rows(const void* src, void* dst, long long rows, int D, int elem_bytes,
+                              hipStream_t st);
+hipError_t launch_copy_words(const void* src, void* dst, long long words, hipStream_t st);
 // gradient of the projected gate's parameters [dw | db] from bwd_pre's partials
 hipError_t launch_gate_proj_grad(const Geom& g, const float* dwp, const float* dbp, float* dtheta,
                                  hipStream_t st);

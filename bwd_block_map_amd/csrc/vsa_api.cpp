@@ -268,7 +268,8 @@ int validate(const vsa_problem* p) {
   if (p->Hq % p->Hkv != 0)
     return fail(VSA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
   if (p->D < 1) return fail(VSA_ERR_INVALID_ARG, "D must be positive");
-  if (p->D != vsa::HD) return fail(VSA_ERR_UNSUPPORTED, "head dimension %d: this build has D=128", p->D);
+  if (p->D > vsa::HD)
+    return fail(VSA_ERR_UNSUPPORTED, "head dimension %d: this build takes D <= 128", p->D);
   if (p->q_block < 1 || p->kv_block < 1)
     return fail(VSA_ERR_INVALID_ARG, "q_block and kv_block must be positive");
   if ((p->q_block % 32 != 0 && p->q_block != 8 && p->q_block != 16) || p->kv_block % 64 != 0)
@@ -371,6 +372,152 @@ int check_device(const vsa_problem* p, std::initializer_list<Arg> args) {
   return VSA_OK;
 }
 
+// ---- head dimensions below HD -------------------------------------------------
+// The kernels are built for D = HD. A problem with a smaller D runs them on
+// copies whose rows are widened with zero columns: a zero column adds nothing
+// to any score, pooled tile or coarse score, and the extra output columns are
+// dropped, so every result equals that of the D-column problem (the softmax
+// scale is an explicit parameter). The copies sit at the front of the caller's
+// workspace, ahead of the widened problem's own workspace; the saved state is
+// the widened problem's.
+bool narrow(const vsa_problem* p) { return p->D < vsa::HD; }
+
+vsa_problem widened(const vsa_problem* p) {
+  vsa_problem w = *p;
+  w.D = vsa::HD;
+  w.gate_proj = nullptr;  // set to the widened copy by the caller
+  return w;
+}
+
+long long rows_q(const vsa_problem* p) { return q_elems(p) / p->D; }
+long long rows_kv(const vsa_problem* p) {
+  return p->layout == VSA_TND ? (long long)p->Skv * p->Hkv : (long long)p->B * p->Skv * p->Hkv;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct PadBufs {
+  uint16_t *q, *k, *v, *dout, *out, *gate, *dq, *dk, *dv, *dgate;
+  float *theta, *dtheta;
+};
+
+// Widened copies: the forward needs q, k, v, out and a q-shaped gate or the
+// projection; the backward also dout, out (O_sel without a gate), dq, dk, dv
+// and dgate.
+PadBufs carve_pad(const vsa_problem* p, bool bwd, void* base, size_t* bytes) {
+  Carver c(base);
+  PadBufs b{};
+  const long long qn = rows_q(p) * vsa::HD, kn = rows_kv(p) * vsa::HD;
+  const long long tn = (long long)p->Hq * vsa::HD + p->Hq;
+  b.q = c.take<uint16_t>(qn);
+  b.k = c.take<uint16_t>(kn);
+  b.v = c.take<uint16_t>(kn);
+  b.out = c.take<uint16_t>(qn);
+  if (p->gate_mode == VSA_GATE_PER_ELEMENT) b.gate = c.take<uint16_t>(qn);
+  if (p->gate_mode == VSA_GATE_PROJECTED) b.theta = c.take<float>(tn);
+  if (bwd) {
+    b.dout = c.take<uint16_t>(qn);
+    b.dq = c.take<uint16_t>(qn);
+    b.dk = c.take<uint16_t>(kn);
+    b.dv = c.take<uint16_t>(kn);
+    if (p->gate_mode == VSA_GATE_PER_ELEMENT) b.dgate = c.take<uint16_t>(qn);
+    if (p->gate_mode == VSA_GATE_PROJECTED) b.dtheta = c.take<float>(tn);
+  }
+  if (bytes) *bytes = round256(c.off);
+  return b;
+}
+
+size_t ws_fwd_bytes(const vsa_problem* p) {
+  size_t inner = 0, pad = 0;
+  if (!narrow(p)) {
+    carve_fwd(p, nullptr, &inner);
+    return inner;
+  }
+  const vsa_problem w = widened(p);
+  carve_fwd(&w, nullptr, &inner);
+  carve_pad(p, false, nullptr, &pad);
+  return pad + inner;
+}
+
+size_t ws_bwd_bytes(const vsa_problem* p) {
+  size_t inner = 0, pad = 0;
+  if (!narrow(p)) {
+    carve_bwd(p, nullptr, &inner);
+    return inner;
+  }
+  const vsa_problem w = widened(p);
+  carve_bwd(&w, nullptr, &inner);
+  carve_pad(p, true, nullptr, &pad);
+  return pad + inner;
+}
+
+size_t saved_bytes_of(const vsa_problem* p) {
+  size_t s = 0;
+  if (narrow(p)) {
+    const vsa_problem w = widened(p);
+    carve_saved(&w, nullptr, &s);
+  } else {
+    carve_saved(p, nullptr, &s);
+  }
+  return s;
+}
+
+// widen the projection [w (Hq x D) | b (Hq)] to [w (Hq x HD) | b]
+hipError_t widen_theta(const vsa_problem* p, const float* src, float* dst, hipStream_t st) {
+  hipError_t e = vsa::launch_widen_rows(src, dst, p->Hq, p->D, 4, st);
+  if (e == hipSuccess) e = vsa::launch_copy_words(src + (long long)p->Hq * p->D, dst + (long long)p->Hq * vsa::HD, p->Hq, st);
+  return e;
+}
+
+hipError_t narrow_theta(const vsa_problem* p, const float* src, float* dst, hipStream_t st) {
+  hipError_t e = vsa::launch_narrow_rows(src, dst, p->Hq, p->D, 4, st);
+  if (e == hipSuccess) e = vsa::launch_copy_words(src + (long long)p->Hq * vsa::HD, dst + (long long)p->Hq * p->D, p->Hq, st);
+  return e;
+}
+
+int fwd_impl(const vsa_problem* p, const void* q, const void* k, const void* v, uint8_t* block_map,
+             const void* gate, void* out, float* lse, void* saved, size_t saved_bytes, void* ws,
+             size_t ws_bytes, void* stream, bool ws_scratch);
+
+// The forward of a D < HD problem: widen, run the HD forward, narrow out.
+int fwd_narrow(const vsa_problem* p, const void* q, const void* k, const void* v,
+               uint8_t* block_map, const void* gate, void* out, float* lse, void* saved,
+               size_t saved_bytes, void* ws, size_t ws_bytes, void* stream, bool ws_scratch) {
+  const size_t need = ws_fwd_bytes(p);
+  if (ws_bytes < need || !ws)
+    return fail(VSA_ERR_WORKSPACE, "forward workspace: %zu bytes needed, %zu given", need, ws_bytes);
+  if (int c = check_device(p, {{q, "q"}, {k, "k"}, {v, "v"}, {block_map, "block_map"}, {gate, "gate"},
+                               {out, "out"}, {lse, "lse"}, {saved, "saved"},
+                               {ws_scratch ? nullptr : ws, "ws"}}))
+    return c;
+  hipStream_t st = (hipStream_t)stream;
+  size_t pad = 0;
+  const PadBufs b = carve_pad(p, false, ws, &pad);
+  const bool proj = p->gate_mode == VSA_GATE_PROJECTED;
+  const bool elem = p->gate_mode == VSA_GATE_PER_ELEMENT;
+  hipError_t e;
+  {
+    Prof pr(ws_scratch ? -1 : VSA_KERNEL_PAD, st);
+    e = vsa::launch_widen_rows(q, b.q, rows_q(p), p->D, 2, st);
+    if (e == hipSuccess) e = vsa::launch_widen_rows(k, b.k, rows_kv(p), p->D, 2, st);
+    if (e == hipSuccess) e = vsa::launch_widen_rows(v, b.v, rows_kv(p), p->D, 2, st);
+    if (e == hipSuccess && elem) e = vsa::launch_widen_rows(gate, b.gate, rows_q(p), p->D, 2, st);
+    if (e == hipSuccess && proj) e = widen_theta(p, p->gate_proj, b.theta, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "widening the inputs");
+  vsa_problem w = widened(p);
+  w.gate_proj = b.theta;
+  const int rc = fwd_impl(&w, b.q, b.k, b.v, block_map, elem ? b.gate : gate, b.out, lse, saved,
+                          saved_bytes, (char*)ws + pad, ws_bytes - pad, stream, ws_scratch);
+  if (rc != VSA_OK) return rc;
+  {
+    Prof pr(ws_scratch ? -1 : VSA_KERNEL_PAD, st);
+    e = vsa::launch_narrow_rows(b.out, out, rows_q(p), p->D, 2, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "narrowing out");
+  return ok();
+}
+
 // The forward launch sequence. ws_scratch: ws is the library's own scratch
 // (the no-alloc entry point): it is not checked as a caller pointer, and no
 // profiler events are recorded.
@@ -389,6 +536,9 @@ int fwd_impl(const vsa_problem* p, const void* q, const void* k, const void* v, 
   const bool proj = p->gate_mode == VSA_GATE_PROJECTED;
   if (p->gate_mode != VSA_GATE_NONE && !proj && !gate)
     return fail(VSA_ERR_INVALID_ARG, "gate must be given with a PER_TOKEN or PER_ELEMENT gate");
+  if (narrow(p))
+    return fwd_narrow(p, q, k, v, block_map, gate, out, lse, saved, saved_bytes, ws, ws_bytes, stream,
+                      ws_scratch);
   size_t need_ws = 0, need_saved = 0;
   carve_fwd(p, nullptr, &need_ws);
   carve_saved(p, nullptr, &need_saved);
@@ -556,10 +706,7 @@ int vsa_sizes(const vsa_problem* p, size_t* ws_fwd, size_t* ws_bwd, size_t* save
               int64_t* nnz_capacity) {
   const int rc = validate(p);
   if (rc != VSA_OK) return rc;
-  size_t f = 0, b = 0, s = 0;
-  carve_fwd(p, nullptr, &f);
-  carve_bwd(p, nullptr, &b);
-  carve_saved(p, nullptr, &s);
+  const size_t f = ws_fwd_bytes(p), b = ws_bwd_bytes(p), s = saved_bytes_of(p);
   if (ws_fwd) *ws_fwd = f;
   if (ws_bwd) *ws_bwd = b;
   if (saved_bytes) *saved_bytes = s;
@@ -603,8 +750,7 @@ int vsa_fwd_noalloc(const vsa_problem* p, const void* q, const void* k, const vo
                     size_t saved_bytes, void* stream) {
   int rc = validate(p);
   if (rc != VSA_OK) return rc;
-  size_t need = 0;
-  carve_fwd(p, nullptr, &need);
+  const size_t need = ws_fwd_bytes(p);
   if (need > kScratchBytes)
     return fail(VSA_ERR_WORKSPACE,
                 "vsa_fwd_noalloc: the forward workspace needs %zu bytes, more than its %zu-byte "
@@ -634,6 +780,53 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
     return fail(VSA_ERR_INVALID_ARG, "gate must be given with a PER_TOKEN or PER_ELEMENT gate");
   if (proj) gate = nullptr;  // the library recomputes it from q and gate_proj
   if (!gated && !out && dout) return fail(VSA_ERR_INVALID_ARG, "out must be given");
+  if (narrow(p)) {  // D < HD: widen, run the HD backward, narrow the gradients
+    const size_t need = ws_bwd_bytes(p), need_sv = saved_bytes_of(p);
+    if (saved_bytes < need_sv)
+      return fail(VSA_ERR_WORKSPACE, "saved state: %zu bytes needed, %zu given", need_sv, saved_bytes);
+    if (ws_bytes < need || !ws)
+      return fail(VSA_ERR_WORKSPACE, "backward workspace: %zu bytes needed, %zu given", need, ws_bytes);
+    if (int c = check_device(p, {{q, "q"}, {k, "k"}, {v, "v"}, {gate, "gate"}, {dout, "dout"},
+                                 {out, "out"}, {lse, "lse"}, {saved, "saved"}, {dq, "dq"},
+                                 {dk, "dk"}, {dv, "dv"}, {dgate, "dgate"}, {ws, "ws"}}))
+      return c;
+    hipStream_t st = (hipStream_t)stream;
+    size_t pad = 0;
+    const PadBufs b = carve_pad(p, true, ws, &pad);
+    const bool elem = p->gate_mode == VSA_GATE_PER_ELEMENT;
+    const bool with_out = !gated && out;  // the row term reads O_sel = out
+    hipError_t e;
+    {
+      Prof pr(VSA_KERNEL_PAD, st);
+      e = vsa::launch_widen_rows(q, b.q, rows_q(p), p->D, 2, st);
+      if (e == hipSuccess) e = vsa::launch_widen_rows(k, b.k, rows_kv(p), p->D, 2, st);
+      if (e == hipSuccess) e = vsa::launch_widen_rows(v, b.v, rows_kv(p), p->D, 2, st);
+      if (e == hipSuccess && dout) e = vsa::launch_widen_rows(dout, b.dout, rows_q(p), p->D, 2, st);
+      if (e == hipSuccess && with_out) e = vsa::launch_widen_rows(out, b.out, rows_q(p), p->D, 2, st);
+      if (e == hipSuccess && elem) e = vsa::launch_widen_rows(gate, b.gate, rows_q(p), p->D, 2, st);
+      if (e == hipSuccess && proj) e = widen_theta(p, p->gate_proj, b.theta, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "widening the inputs");
+    vsa_problem w = widened(p);
+    w.gate_proj = b.theta;
+    void* wdg = elem ? (dgate ? (void*)b.dgate : nullptr)
+                     : proj ? (dgate ? (void*)b.dtheta : nullptr) : dgate;  // per-token: as is
+    rc = vsa_bwd(&w, b.q, b.k, b.v, elem ? b.gate : gate, dout ? b.dout : nullptr,
+                 with_out ? b.out : nullptr, lse, saved, saved_bytes, b.dq, b.dk, b.dv, wdg,
+                 (char*)ws + pad, ws_bytes - pad, stream);
+    if (rc != VSA_OK) return rc;
+    {
+      Prof pr(VSA_KERNEL_PAD, st);
+      e = vsa::launch_narrow_rows(b.dq, dq, rows_q(p), p->D, 2, st);
+      if (e == hipSuccess) e = vsa::launch_narrow_rows(b.dk, dk, rows_kv(p), p->D, 2, st);
+      if (e == hipSuccess) e = vsa::launch_narrow_rows(b.dv, dv, rows_kv(p), p->D, 2, st);
+      if (e == hipSuccess && elem && dgate)
+        e = vsa::launch_narrow_rows(b.dgate, dgate, rows_q(p), p->D, 2, st);
+      if (e == hipSuccess && proj && dgate) e = narrow_theta(p, b.dtheta, (float*)dgate, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "narrowing the gradients");
+    return ok();
+  }
   size_t need_ws = 0, need_saved = 0;
   carve_bwd(p, nullptr, &need_ws);
   carve_saved(p, nullptr, &need_saved);

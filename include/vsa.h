@@ -95,7 +95,11 @@ enum vsa_gate_mode {
  *   Hq, Hkv       query heads and key/value heads, Hq % Hkv == 0; Q head h
  *                 reads KV head h / (Hq / Hkv)
  *   Sq, Skv       rows per batch entry (TND: total packed tokens Tq, Tkv)
- *   D             head dimension (this build: 128)
+ *   D             head dimension, 1 .. 128 ([Ascend] page: the operator takes
+ *                 head_dim <= 128). The kernels are built for 128; a smaller D
+ *                 runs them on copies of the inputs widened with zero columns
+ *                 (scores and outputs unchanged, the copies in the caller's
+ *                 workspace, results narrowed back), at the cost of D = 128.
  *   q_block       rows per Q block: 8, 16 or a multiple of 32 (8 and 16 run one
  *                 32-row wave per block, with the rows past the block idle)
  *   kv_block      keys per KV block, a multiple of 64
@@ -193,7 +197,7 @@ int vsa_abi_version(void);
 /* Host-only check of a problem (no device access). Messages for the cases
  * the pages name: "actual_seq_lengths must be specified",
  * "actual_seq_lengths_kv must be specified" (TND without cu_seqlens_q / _kv).
- * Limits of this build (VSA_ERR_UNSUPPORTED): D = 128; q_block 8, 16 or a
+ * Limits of this build (VSA_ERR_UNSUPPORTED): D <= 128; q_block 8, 16 or a
  * multiple of 32, kv_block a multiple of 64; fewer than 65536 heads in BSHD and
  * TND (row offsets of the tile loads are 24-bit); B*Hq*Qb*KVb and B*Hq*Sq below
  * 2^31; KVb small enough for the coarse kernels' LDS when top-k or a gate is on. */
@@ -321,7 +325,8 @@ enum vsa_kernel_id {
   VSA_KERNEL_SPARSE_DQ = 7,   /* Q-owned dQ                           */
   VSA_KERNEL_DQ_ATOMIC = 8,   /* atomic-dQ backward: accumulator clear and cast */
   VSA_KERNEL_DKDV_ORDER = 9,  /* persistent dK/dV grid: the longest-first span list */
-  VSA_KERNEL_COUNT = 10
+  VSA_KERNEL_PAD = 10,        /* D < 128: widening inputs, narrowing results */
+  VSA_KERNEL_COUNT = 11
 };
 
 int vsa_profile_begin(void);

@@ -71,7 +71,8 @@ def test_validate_rejects_bad_problems_with_messages():
     # 24-bit row offsets of the tile loads: token-major rows of 65536 heads are too long
     c, m = _code(_prob(layout="bshd", Hq=65536, Hkv=65536, Sq=256, Skv=256))
     assert c == vsa.ERR_UNSUPPORTED and "65536 heads" in m
-    assert _code(_prob(D=64))[0] == vsa.ERR_UNSUPPORTED
+    assert _code(_prob(D=256))[0] == vsa.ERR_UNSUPPORTED
+    assert _code(_prob(D=0, scale=1.0))[0] == vsa.ERR_INVALID_ARG
     assert _code(_prob(q_block=48))[0] == vsa.ERR_UNSUPPORTED
     assert _code(_prob(Sq=240, q_block=24))[0] == vsa.ERR_UNSUPPORTED
     assert _code(_prob(scale=float("nan")))[0] == vsa.ERR_INVALID_ARG
@@ -198,3 +199,19 @@ def test_per_entry_valid_counts_are_checked():
     assert c == vsa.ERR_INVALID_ARG and "needs the counts" in m
     with pytest.raises(ValueError):
         _prob(B=2, q_valid=torch.full((3, 3), 256, dtype=torch.int32))
+
+
+def test_head_dimensions_up_to_128():
+    """D in 1 .. 128 is accepted (the Ascend operator takes head_dim <= 128),
+    D = 129 is UNSUPPORTED; a D < 128 problem needs the D = 128 problem's
+    workspaces plus room for its widened copies, and the same saved state."""
+    for D in (1, 8, 64, 96, 128):
+        vsa.vsa_validate(_prob(D=D))
+    assert _code(_prob(D=129))[0] == vsa.ERR_UNSUPPORTED
+    full = vsa.vsa_sizes(_prob(D=128, topk=2, gate_mode="per_element"))
+    half = vsa.vsa_sizes(_prob(D=64, topk=2, gate_mode="per_element"))
+    assert half["saved"] == full["saved"]
+    q_rows, kv_rows = 1 * 768 * 2, 1 * 1024 * 2
+    copies_fwd = 2 * 128 * (3 * q_rows + 2 * kv_rows)  # q, out, gate; k, v
+    assert half["ws_fwd"] >= full["ws_fwd"] + copies_fwd
+    assert half["ws_bwd"] >= full["ws_bwd"] + copies_fwd + 2 * 128 * (3 * q_rows + 2 * kv_rows)

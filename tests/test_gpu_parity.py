@@ -536,3 +536,37 @@ def test_per_entry_valid_counts():
         if case.topk > 0:
             assert _topk_agreement(orc, res["map"]).all(), "top-k near-tie in a small case"
         _compare_case(case, res, orc)
+
+
+def _small_head_cases():
+    # D = 64: VSA tiles with top-k and the per-token gate, GQA, BSHD
+    yield build_case("d64_gated", dtype="bf16", layout="bshd", B=1, Hq=4, Hkv=2, D=64,
+                     q_var=[256, 61, 256], kv_var=[256, 0, 200, 256, 17], topk=3,
+                     map_kind="none", gate_mode="per_token", seed=81)
+    # D = 96: caller map, ragged tails, fp16 BHSD, a q-shaped gate
+    yield build_case("d96_elem", dtype="fp16", layout="bhsd", B=2, Hq=2, Hkv=1, D=96,
+                     q_block=64, kv_block=128, Sq=300, Skv=333, map_kind="bernoulli", map_p=0.5,
+                     gate_mode="per_element", gate_kind="scaled", seed=82)
+    # D = 40: the projected gate
+    yield build_case("d40_proj", dtype="bf16", layout="bshd", B=1, Hq=2, Hkv=2, D=40,
+                     q_var=[256, 100], kv_var=[256, 256, 31], topk=2, map_kind="none",
+                     gate_mode="projected", seed=83)
+    # D = 8: TND varlen GQA
+    yield build_case("d8_tnd", dtype="bf16", layout="tnd", Hq=4, Hkv=2, D=8, q_block=128,
+                     kv_block=128, q_lens=[65, 300, 7], kv_lens=[129, 400, 90],
+                     map_kind="bernoulli", map_p=0.6, seed=84)
+
+
+@pytest.mark.parametrize("case", list(_small_head_cases()), ids=lambda c: c.name)
+def test_head_dimensions_below_128(case):
+    """D < 128 runs the 128-column kernels on zero-widened copies: every output
+    and gradient (the projection's [dw | db] included) against the oracle at
+    the case's own D."""
+    _say(f"[{case.name}] D={case.D} layout={case.layout}")
+    res = run_case(case)
+    orc = oracle.Oracle(case, np.float32)
+    if case.topk > 0:
+        assert _topk_agreement(orc, res["map"]).all(), "top-k near-tie in a small case"
+    _compare_case(case, res, orc)
+    if case.gate_mode == "projected":
+        check("gate", orc.gate_values(), res["gate_vals"], (2e-3, 1e-2))
