@@ -771,6 +771,7 @@ __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdA
 // ---------------------------------------------------------------------------
 constexpr int LPT_LEVELS = 1024;
 
+template <int LEVELS = LPT_LEVELS>
 __device__ __forceinline__ int lpt_bin(const BwdArgs& a, int id) {
   const Geom& g = a.g;
   const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
@@ -790,8 +791,8 @@ __device__ __forceinline__ int lpt_bin(const BwdArgs& a, int id) {
   const int steps = dkdv_shape(live);  // 8, 4 or 2 chunk steps per Q block
   const long long work = live > 0 ? cnt * steps : 0;
   const long long wmax = (long long)g.group * g.Qb * 8;
-  const int level = (int)min<long long>(LPT_LEVELS - 1, work * (LPT_LEVELS - 1) / max(wmax, 1LL));
-  return (b * g.Hkv + hk) * LPT_LEVELS + (LPT_LEVELS - 1 - level);
+  const int level = (int)min<long long>(LEVELS - 1, work * (LEVELS - 1) / max(wmax, 1LL));
+  return (b * g.Hkv + hk) * LEVELS + (LEVELS - 1 - level);
 }
 
 // hist[bin + 1] counts the spans of each bin (hist zeroed before)
@@ -805,6 +806,44 @@ __global__ __launch_bounds__(256) void lpt_scatter_kernel(const BwdArgs a, int32
                                                            int32_t* order) {
   const int id = blockIdx.x * 256 + threadIdx.x;
   if (id < a.n_items) order[atomicAdd(&hist[lpt_bin(a, id)], 1)] = id;
+}
+
+// The same order for small problems in one launch: one work-group histograms
+// the bins in LDS (LPT_SMALL_LEVELS levels per KV head), scans them, scatters
+// the spans and clears the item counter.
+constexpr int LPT_SMALL_LEVELS = 256;
+constexpr int LPT_SMALL_BINS = 16384;
+
+__global__ __launch_bounds__(1024) void lpt_small_kernel(const BwdArgs a, int32_t* order,
+                                                         int32_t* counter) {
+  __shared__ int32_t hist[LPT_SMALL_BINS];
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int nb = a.g.B * a.g.Hkv * LPT_SMALL_LEVELS, n = a.n_items;
+  for (int x = t; x < nb; x += 1024) hist[x] = 0;
+  __syncthreads();
+  for (int id = t; id < n; id += 1024) atomicAdd(&hist[lpt_bin<LPT_SMALL_LEVELS>(a, id)], 1);
+  __syncthreads();
+  const int per = (nb + 1023) / 1024, beg = min(t * per, nb), end = min(beg + per, nb);
+  int32_t s = 0;
+  for (int x = beg; x < end; ++x) s += hist[x];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int32_t acc = part[t] - s;
+  for (int x = beg; x < end; ++x) {
+    const int32_t c = hist[x];
+    hist[x] = acc;
+    acc += c;
+  }
+  __syncthreads();
+  for (int id = t; id < n; id += 1024) order[atomicAdd(&hist[lpt_bin<LPT_SMALL_LEVELS>(a, id)], 1)] = id;
+  if (t == 0) *counter = 0;
 }
 
 // dq = scale * (the atomically accumulated dS K) + the unpooled compression
@@ -1051,9 +1090,17 @@ long long dkdv_items(const Geom& g) {
 }
 long long lpt_hist_entries(const Geom& g) { return (long long)g.B * g.Hkv * LPT_LEVELS + 2; }
 
+bool lpt_order_small(const Geom& g) {
+  return (long long)g.B * g.Hkv * LPT_SMALL_LEVELS <= LPT_SMALL_BINS && dkdv_items(g) <= 16384;
+}
+
 hipError_t launch_lpt_order(const BwdArgs& a, int32_t* hist, int32_t* order, hipStream_t st) {
   const long long n = a.n_items, nb = (long long)a.g.B * a.g.Hkv * LPT_LEVELS;
   if (n == 0) return hipSuccess;
+  if (lpt_order_small(a.g)) {  // hist need not be zero: only the counter is used
+    lpt_small_kernel<<<1, 1024, 0, st>>>(a, order, a.lpt_counter);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)((n + 255) / 256);
   lpt_count_kernel<<<grid, 256, 0, st>>>(a, hist);
   hipError_t e = launch_exclusive_scan(hist, nb, st);

@@ -115,7 +115,9 @@ hipError_t launch_dq_cast(const BwdArgs& a, int dtype, hipStream_t st);
 long long dkdv_items(const Geom& g);        // dK/dV spans of a problem
 long long lpt_hist_entries(const Geom& g);  // int32 entries of the order's histogram
 // longest-first order of the dK/dV spans into `order` (a.n_items entries);
-// `hist` (lpt_hist_entries) must be zero
+// `hist` (lpt_hist_entries) must be zero unless lpt_order_small(g), whose one
+// launch also clears a.lpt_counter
+bool lpt_order_small(const Geom& g);
 hipError_t launch_lpt_order(const BwdArgs& a, int32_t* hist, int32_t* order, hipStream_t st);
 hipError_t launch_exclusive_scan(int32_t* a, long long n, hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);

@@ -939,11 +939,12 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
     ba.persist_grid = cus;
     const long long nh = vsa::lpt_hist_entries(g);
     Prof pr(VSA_KERNEL_DKDV_ORDER, st);
-    e = vsa::launch_zero(w.lpt_hist, (size_t)nh * sizeof(int32_t), st);
+    ba.lpt_counter = w.lpt_hist + (nh - 1);
+    if (!vsa::lpt_order_small(g))  // the one-launch order clears the counter itself
+      e = vsa::launch_zero(w.lpt_hist, (size_t)nh * sizeof(int32_t), st);
     if (e == hipSuccess) e = vsa::launch_lpt_order(ba, w.lpt_hist, w.lpt_order, st);
     if (e != hipSuccess) return hip_fail(e, "dK/dV order");
     ba.lpt_order = w.lpt_order;
-    ba.lpt_counter = w.lpt_hist + (nh - 1);
   }
   if (atomic_dq) {  // the accumulator starts at zero (a fill kernel: safe under graph capture)
     Prof pr(VSA_KERNEL_DQ_ATOMIC, st);
