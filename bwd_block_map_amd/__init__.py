@@ -354,5 +354,5 @@ class Buffers:
 
 
 # PyTorch entry points (autograd over vsa_fwd / vsa_bwd)
-from .torch_api import (attention, block_sparse_attn, video_sparse_attn,  # noqa: E402
-                        video_sparse_attn_bshd)
+from .torch_api import (attention, block_sparse_attn, block_sparse_attn_tnd,  # noqa: E402
+                        video_sparse_attn, video_sparse_attn_bshd)

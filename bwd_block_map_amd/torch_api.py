@@ -15,7 +15,9 @@ test page (`video_sparse_attn` / `video_sparse_attn_bshd` usage):
 - the video wrappers build the tile map by pooled-score top-k inside the
   library and add the gated compression branch when a gate is given;
 - a projected gate (weights w [H, D] and bias b [H]) has the library compute
-  each token's gate as sigmoid(<q, w_h> + b_h) and return dw, db.
+  each token's gate as sigmoid(<q, w_h> + b_h) and return dw, db;
+- packed variable-length sequences ([T, H, D], the Ascend operator's TND
+  layout with per-sequence actual lengths) go through block_sparse_attn_tnd.
 
 Everything here is argument marshalling: every step of the computation runs in
 the library's HIP kernels.
@@ -88,8 +90,23 @@ class Spec:
     deterministic: bool = True
     # True: the gate slot holds the projected gate's parameters [w | b] (fp32)
     projected: bool = False
+    # packed layout ("tnd"): [B+1] int32 offsets of the sequences and the
+    # longest lengths
+    cu_q: Optional[torch.Tensor] = None
+    cu_kv: Optional[torch.Tensor] = None
+    max_q: int = 0
+    max_kv: int = 0
 
     def problem(self, q, k, gate):
+        if self.layout == "tnd":
+            Sq, Hq, D = (int(x) for x in q.shape)
+            Skv, Hkv = int(k.shape[0]), int(k.shape[1])
+            return make_problem(dtype=q.dtype, layout="tnd", B=int(self.cu_q.numel()) - 1, Hq=Hq,
+                                Hkv=Hkv, Sq=Sq, Skv=Skv, D=D, q_block=self.q_block,
+                                kv_block=self.kv_block, cu_seqlens_q=self.cu_q,
+                                cu_seqlens_kv=self.cu_kv, max_seqlen_q=self.max_q,
+                                max_seqlen_kv=self.max_kv, scale=self.scale,
+                                atomic_dq=not self.deterministic)
         B, Hq, Hkv, Sq, Skv, D = dims(q, k, self.layout)
         mode = "projected" if self.projected else gate_mode_of(gate, q, self.layout)
         return make_problem(dtype=q.dtype, layout=self.layout, B=B, Hq=Hq, Hkv=Hkv, Sq=Sq,
@@ -197,6 +214,46 @@ def block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_m
                 q_valid=_counts(q_valid, q.device), kv_valid=_counts(kv_valid, q.device),
                 deterministic=deterministic)
     out, lse = attention(q, k, v, spec, block_map=block_map, gate=gate)
+    return out, lse.detach()
+
+
+def block_sparse_attn_tnd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          block_map: torch.Tensor, block_shape: Sequence[int],
+                          actual_seq_lengths: Sequence[int],
+                          actual_seq_lengths_kv: Sequence[int], *, scale: Optional[float] = None,
+                          deterministic: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-sparse attention over packed variable-length sequences (the
+    [Ascend] operator's TND layout): q [Tq, Hq, D], k / v [Tkv, Hkv, D] hold
+    the sequences back to back, sequence b with actual_seq_lengths[b] query
+    and actual_seq_lengths_kv[b] key tokens; block_map [B, Hq, Qb, KVb] over
+    the blocks of the longest sequences, block_shape = (q_block, kv_block); Q
+    head h reads KV head h // (Hq / Hkv). Returns (out [Tq, Hq, D], lse
+    [Hq, Tq]), lse detached."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("TND tensors are 3-D [T, H, D]")
+    lq = [int(x) for x in actual_seq_lengths]
+    lk = [int(x) for x in actual_seq_lengths_kv]
+    if len(lq) != len(lk) or not lq:
+        raise ValueError("actual_seq_lengths and actual_seq_lengths_kv need one entry per sequence")
+    if sum(lq) != q.shape[0] or sum(lk) != k.shape[0]:
+        raise ValueError(f"the lengths sum to {sum(lq)} / {sum(lk)} tokens, the tensors hold "
+                         f"{q.shape[0]} / {k.shape[0]}")
+    qb, kb = (int(x) for x in block_shape)
+    mq, mk = max(lq), max(lk)
+    want = (len(lq), int(q.shape[1]), -(-mq // qb), -(-mk // kb))
+    if block_map.dim() != 4 or tuple(block_map.shape) != want:
+        raise ValueError(f"block_map must be {list(want)} (sequences, heads, Q blocks and KV "
+                         f"blocks of the longest sequences), got {list(block_map.shape)}")
+
+    def offsets(lens):
+        c = [0]
+        for x in lens:
+            c.append(c[-1] + x)
+        return torch.tensor(c, dtype=torch.int32, device=q.device)
+
+    spec = Spec(layout="tnd", q_block=qb, kv_block=kb, scale=scale, deterministic=deterministic,
+                cu_q=offsets(lq), cu_kv=offsets(lk), max_q=mq, max_kv=mk)
+    out, lse = attention(q, k, v, spec, block_map=block_map)
     return out, lse.detach()
 
 

@@ -43,3 +43,18 @@ def test_block_sparse_attn_checks_the_map_before_any_launch():
     bad_heads = torch.ones(1, 3, 2, 2, dtype=torch.uint8)
     with pytest.raises(ValueError):
         block_sparse_attn(q, q, q, bad_heads)
+
+
+def test_tnd_entry_checks_lengths_and_map_before_any_launch():
+    from bwd_block_map_amd.torch_api import block_sparse_attn_tnd
+    q = torch.empty(100, 4, 128, dtype=torch.bfloat16)
+    k = torch.empty(150, 2, 128, dtype=torch.bfloat16)
+    good = torch.ones(2, 4, 1, 1, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="sum to"):  # 60 + 30 != 100 query tokens
+        block_sparse_attn_tnd(q, k, k, good, (128, 128), [60, 30], [100, 50])
+    with pytest.raises(ValueError, match="one entry per sequence"):
+        block_sparse_attn_tnd(q, k, k, good, (128, 128), [60, 40], [150])
+    with pytest.raises(ValueError, match="block_map must be"):  # 2 KV blocks of 64 for 100 keys
+        block_sparse_attn_tnd(q, k, k, good, (128, 64), [60, 40], [100, 50])
+    with pytest.raises(ValueError, match="3-D"):
+        block_sparse_attn_tnd(q[None], k, k, good, (128, 128), [60, 40], [100, 50])
