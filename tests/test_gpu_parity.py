@@ -570,3 +570,27 @@ def test_head_dimensions_below_128(case):
     _compare_case(case, res, orc)
     if case.gate_mode == "projected":
         check("gate", orc.gate_values(), res["gate_vals"], (2e-3, 1e-2))
+
+
+def test_many_kv_tiles_at_the_coarse_kernels_limits():
+    """Pooled top-k over very many KV tiles, where the coarse kernels hold only
+    one or two score rows per work-group: the gated path at its largest KV tile
+    count (2175 tiles of 64 keys) and top-k alone at 20000 tiles (1.28 M keys),
+    against the oracle (selection exact, outputs and gradients within the
+    bars)."""
+    cases = [
+        build_case("many_kv_gated", dtype="bf16", layout="bshd", B=1, Hq=2, Hkv=1, D=128,
+                   q_block=256, kv_block=64, Sq=512, Skv=64 * 2175, topk=6, map_kind="none",
+                   gate_mode="per_token", seed=95),
+        build_case("many_kv_topk", dtype="bf16", layout="bhsd", B=1, Hq=1, Hkv=1, D=128,
+                   q_block=256, kv_block=64, Sq=256, Skv=64 * 20000, topk=8, map_kind="none",
+                   seed=96),
+    ]
+    for case in cases:
+        _say(f"[{case.name}] KVb={case.KVb} topk={case.topk} gate={case.gate_mode}")
+        res = run_case(case)
+        orc = oracle.Oracle(case, np.float32, threads=16)
+        assert _topk_agreement(orc, res["map"]).all(), "top-k near-tie"
+        _compare_case(case, res, orc)
+        del res, orc, case
+        torch.cuda.empty_cache()
