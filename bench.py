@@ -424,6 +424,9 @@ def main():
     ap.add_argument("--grid", choices=("auto", "persistent", "per-item"), default="auto",
                     help="grid of the dK/dV pass: the library's choice, the persistent "
                          "longest-first grid, or one work-group per span")
+    ap.add_argument("--gate", choices=("workload", "none", "per_token", "per_element", "projected"),
+                    default="workload",
+                    help="another gate form than the workload's (the 720p workload only)")
     ap.add_argument("--dout-unpadded", action="store_true",
                     help="draw dO without zeroing the padded slots of partial tiles")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -466,8 +469,12 @@ def main():
 
     torch.cuda.set_device(0)
     log(f"[bench] generating {args.workload} on cuda:0")
-    case = make_case(args.workload, device="cuda", **({"pad_dout": False} if args.dout_unpadded else {}))
+    kw = {"pad_dout": False} if args.dout_unpadded else {}
+    if args.gate != "workload":
+        kw["gate_mode"] = args.gate
+    case = make_case(args.workload, device="cuda", **kw)
     d = device_inputs(case)
+    proj = case.gate_mode == "projected"
     p = vsa.make_problem(
         dtype=case.torch_dtype, layout=case.layout, B=case.B, Hq=case.Hq, Hkv=case.Hkv,
         Sq=case.Sq, Skv=case.Skv, D=case.D, q_block=case.q_block, kv_block=case.kv_block,
@@ -475,18 +482,22 @@ def main():
         cu_seqlens_kv=d["cu_kv"], max_seqlen_q=max(case.q_lens) if case.q_lens else 0,
         max_seqlen_kv=max(case.kv_lens) if case.kv_lens else 0, scale=case.scale,
         topk=case.topk, gate_mode=case.gate_mode, atomic_dq=args.atomic_dq,
-        persistent={"auto": None, "persistent": True, "per-item": False}[args.grid])
+        persistent={"auto": None, "persistent": True, "per-item": False}[args.grid],
+        gate_proj=d["gate"] if proj else None)
     buf = vsa.Buffers(p, d["q"], training=True)
     bmap = d["map"] if case.topk == 0 else buf.map
     dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+    # the projected gate: its parameters are in the problem, the forward
+    # computes the gate values and the backward returns [dw | db]
+    gate = None if proj else d["gate"]
     dg = torch.empty_like(d["gate"]) if d["gate"] is not None else None
 
     def fwd():
-        vsa.vsa_fwd(p, d["q"], d["k"], d["v"], bmap, d["gate"], buf.out, buf.lse, buf.saved,
+        vsa.vsa_fwd(p, d["q"], d["k"], d["v"], bmap, gate, buf.out, buf.lse, buf.saved,
                     buf.ws_fwd)
 
     def bwd():
-        vsa.vsa_bwd(p, d["q"], d["k"], d["v"], d["gate"], d["dout"], buf.out, buf.lse, buf.saved,
+        vsa.vsa_bwd(p, d["q"], d["k"], d["v"], gate, d["dout"], buf.out, buf.lse, buf.saved,
                     dq, dk, dv, dg, buf.ws_bwd)
 
     for w in range(args.warmup):

@@ -281,11 +281,13 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
 // Coarse backward, row form: P_c, dS_c for CR2 rows (kept in workspace for the
 // column pass) and dQ_c = scale dS_c K_c. For dQ_c the pooled K rows stream
 // through an LDS tile with all loads of a tile in flight.
-// 8 rows per work-group: with 4, two work-groups share a CU at 1440 KV tiles,
-// but twice as many row blocks then stream every pooled K/V row (6 % slower)
-constexpr int CR2 = 8;
+// 8 rows per work-group (CR2): with 4, two work-groups share a CU at 1440 KV
+// tiles, but twice as many row blocks then stream every pooled K/V row (6 %
+// slower). With more KV tiles than 8 rows of P_c and dS_c fit in LDS, the
+// launch takes 4, 2 or 1 rows per work-group.
 constexpr int CT2 = 32;                  // pooled K rows per staging tile
 constexpr int TILE2_FLOATS = CT2 * HD;
+template <int CR2>
 __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a) {
   extern __shared__ float dsm[];
   const Geom& g = a.g;
@@ -357,8 +359,9 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a
     }
   }
   // dQ_c[r][d] = scale sum_j dS_c[r][j] K_c[j][d], CT2 pooled K rows at a time (tile[j][d])
-  constexpr int RH = CR2 / 2;  // rows per half of the work-group
+  constexpr int RH = CR2 > 1 ? CR2 / 2 : 1;  // rows per half of the work-group
   const int d = tid & (HD - 1), half = tid >> 7;
+  const bool rows_here = half * RH < CR2;  // one row: the second half idles
   float acc[RH];
 #pragma unroll
   for (int u = 0; u < RH; ++u) acc[u] = 0.f;
@@ -375,17 +378,19 @@ __global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a
     for (int k = 0; k < KLOADS; ++k) reinterpret_cast<float4*>(tile)[tid + 256 * k] = x[k];
     __syncthreads();
     const int nj = min(CT2, KVb - j0);
+    if (rows_here) {
 #pragma unroll 4
-    for (int jt = 0; jt < nj; ++jt) {
-      const float kv = tile[jt * HD + d];
+      for (int jt = 0; jt < nj; ++jt) {
+        const float kv = tile[jt * HD + d];
 #pragma unroll
-      for (int u = 0; u < RH; ++u) acc[u] = __builtin_fmaf(dS[(half * RH + u) * KVb + j0 + jt], kv, acc[u]);
+        for (int u = 0; u < RH; ++u) acc[u] = __builtin_fmaf(dS[(half * RH + u) * KVb + j0 + jt], kv, acc[u]);
+      }
     }
   }
 #pragma unroll
   for (int u = 0; u < RH; ++u) {
     const int rr = half * RH + u;
-    if (rr < nr) a.dqc[g.pq(b, h, i0 + rr) + d] = g.scale * acc[u];
+    if (rows_here && rr < nr) a.dqc[g.pq(b, h, i0 + rr) + d] = g.scale * acc[u];
   }
 }
 
@@ -468,9 +473,21 @@ __global__ void zero_kernel(uint8_t* p, size_t n) {
 
 }  // namespace
 
-size_t coarse_bwd_lds(int KVb) {
-  return ((size_t)2 * CR2 * KVb + 2 * CR2 * HD + CR2 + TILE2_FLOATS) * 4;
+namespace {
+size_t rows_lds(int cr2, int KVb) {
+  return ((size_t)2 * cr2 * KVb + 2 * cr2 * HD + cr2 + TILE2_FLOATS) * 4;
 }
+// rows per work-group of the coarse backward: 8 when they fit, else fewer
+int coarse_bwd_rows(int KVb) {
+  for (int cr = 8; cr > 1; cr >>= 1)
+    if (rows_lds(cr, KVb) <= 160 * 1024) return cr;
+  return 1;
+}
+}  // namespace
+
+// LDS of the coarse backward's row pass at its launch shape (above 160 KiB:
+// too many KV tiles for these kernels)
+size_t coarse_bwd_lds(int KVb) { return rows_lds(coarse_bwd_rows(KVb), KVb); }
 
 int coarse_rows_per_block(int KVb) {
   // scores [CR][KVb] + qc [CR][HD] + 4 histograms + the staging tile. Prefer
@@ -521,11 +538,15 @@ hipError_t launch_coarse_fwd(const CoarseArgs& a, bool want_topk, bool want_gate
 
 hipError_t launch_coarse_bwd(const CoarseArgs& a, hipStream_t st) {
   const Geom& g = a.g;
-  const long long nr = (long long)g.B * g.Hq * ((g.Qb + CR2 - 1) / CR2);
+  const int cr2 = coarse_bwd_rows(g.KVb);
+  const long long nr = (long long)g.B * g.Hq * ((g.Qb + cr2 - 1) / cr2);
   const long long nc = (long long)g.B * g.Hkv * ((g.KVb + CC - 1) / CC);
   if (nr == 0 || nc == 0) return hipSuccess;
   const size_t lds = coarse_bwd_lds(g.KVb);
-  coarse_bwd_rows_kernel<<<(unsigned)nr, 256, lds, st>>>(a);
+  if (cr2 == 8) coarse_bwd_rows_kernel<8><<<(unsigned)nr, 256, lds, st>>>(a);
+  else if (cr2 == 4) coarse_bwd_rows_kernel<4><<<(unsigned)nr, 256, lds, st>>>(a);
+  else if (cr2 == 2) coarse_bwd_rows_kernel<2><<<(unsigned)nr, 256, lds, st>>>(a);
+  else coarse_bwd_rows_kernel<1><<<(unsigned)nr, 256, lds, st>>>(a);
   coarse_bwd_cols_kernel<<<(unsigned)nc, 256, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -317,14 +317,25 @@ def _c4(seed=42, device="cpu", **kw):
                       device=device, **kw)
 
 
-def _c5(seed=42, device="cpu", **kw):
+def _c5(seed=42, device="cpu", gate_mode="per_token", **kw):
     """VSA-256 720p with the compression gate: latent 21x90x160 in (4,8,8)
     tiles -> 1440 tiles, B=1, H=40, bf16, BSHD, topk=144, per-token per-head
-    gate sigmoid(N(0,1))."""
+    gate sigmoid(N(0,1)) (gate_mode selects another gate form for measuring
+    it at this shape)."""
     var = vsa_tile_counts((21, 90, 160))
     return build_case("c5_vsa256_720p_gate", dtype="bf16", layout="bshd", B=1, Hq=40, D=128,
-                      q_var=var, kv_var=var, topk=144, map_kind="none", gate_mode="per_token",
+                      q_var=var, kv_var=var, topk=144, map_kind="none", gate_mode=gate_mode,
                       gate_kind="sigmoid", seed=seed, device=device, **kw)
+
+
+def _c5_vsa128(seed=42, device="cpu", **kw):
+    """The 720p latent in VSA-128 tiles: 21x90x160 in (2,8,8) tiles -> 11 x 12
+    x 20 = 2640 tiles of 128 tokens, B=1, H=40, bf16, BSHD, topk=288 (the same
+    tenth of the tiles as the 256-token workload), per-token gate."""
+    var = vsa_tile_counts((21, 90, 160), tile=(2, 8, 8))
+    return build_case("c5_vsa128_720p_gate", dtype="bf16", layout="bshd", B=1, Hq=40, D=128,
+                      q_block=128, kv_block=128, q_var=var, kv_var=var, topk=288, map_kind="none",
+                      gate_mode="per_token", gate_kind="sigmoid", seed=seed, device=device, **kw)
 
 
 def _p1(name, kv_var, q_var, topk, seed, gate=False):
@@ -369,6 +380,7 @@ CASES: Dict[str, Callable[..., Case]] = {
     "c3_tnd_gqa_page": _c3_page,
     "c4_vsa256_video": _c4,
     "c5_vsa256_720p_gate": _c5,
+    "c5_vsa128_720p_gate": _c5_vsa128,
     "p1_fwd_bwd": _p1("p1_fwd_bwd", [256, 173, 79, 256], [256] * 3, 2, 42),
     "p1_gated": _p1("p1_gated", [256, 200, 256, 91], [256] * 3, 2, 7, gate=True),
     "p1_partial_q": _p1("p1_partial_q", [256, 128, 256], [256, 61, 199], 2, 11),
