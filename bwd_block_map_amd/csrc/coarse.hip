@@ -9,13 +9,14 @@
 // O_c = softmax_j(C) V_c, and its gradient returns to the valid slots
 // divided by the tile's valid count.
 //
-// gfx950 design: these steps are small (tens of GFLOP at the largest video
-// shape) and run on fp32 VALU. Pooling is one work-group per tile with
-// coalesced 16-byte loads and an LDS reduction. The coarse kernels keep a
-// block of CR score rows in LDS, stream the pooled K/V tiles once per block,
+// gfx950 design: pooling is one work-group per tile with coalesced 16-byte
+// loads and an LDS reduction. The coarse contractions (scores, O_c, and in the
+// backward C, dP_c, dQ_c, dK_c, dV_c) run on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32) with both operands loaded straight into registers,
+// 16 bytes per lane. The row kernels keep up to 16 rows of scores in LDS,
 // select top-k per row with a 4-pass 8-bit radix select (per-wave LDS
-// histograms, ties resolved by ascending tile index with ballots) and write
-// the map bytes directly.
+// histograms, ties resolved by ascending tile index with ballots) and write the
+// map bytes directly.
 #include "kernels.hpp"
 
 namespace vsa {
@@ -67,27 +68,130 @@ __device__ __forceinline__ uint32_t fkey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The contractions of the coarse branch run on the fp32 matrix cores:
+// v_mfma_f32_16x16x4_f32 computes D[16][16] += A[16][4] B[4][16]; lane l
+// supplies A[l % 16][l / 16] and B[l / 16][l % 16] and holds
+// D[4 (l / 16) + v][l % 16] for v < 4.
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+__device__ __forceinline__ f32x4_t mfma16(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+constexpr int NWC = 8;        // waves of the row kernels (two per SIMD)
+constexpr int MR = 16;        // rows of one MFMA block
+constexpr int HD16 = HD / 16;
+
+// Dot products of pooled rows: lane (r = l % 16, kk = l / 16) holds d = 16 m +
+// 4 kk + {0..3} (m < HD / 16) of one row; the d order inside the sum is the
+// MFMA's (any split of d between the steps gives the same dot product).
+__device__ __forceinline__ void load_row(float4 (&x)[HD16], const float* row, int kk) {
+#pragma unroll
+  for (int m = 0; m < HD16; ++m) x[m] = *reinterpret_cast<const float4*>(row + 16 * m + 4 * kk);
+}
+__device__ __forceinline__ void zero_row(float4 (&x)[HD16]) {
+#pragma unroll
+  for (int m = 0; m < HD16; ++m) x[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+// D[i][j] = <X_i, Y_j> for the 16 rows X held by lanes i = l % 16 and the 16
+// rows Y held by lanes j = l % 16
+__device__ __forceinline__ f32x4_t rowdot16(const float4 (&x)[HD16], const float4 (&y)[HD16]) {
+  f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < HD16; ++m) {
+    c = mfma16(x[m].x, y[m].x, c);
+    c = mfma16(x[m].y, y[m].y, c);
+    c = mfma16(x[m].z, y[m].z, c);
+    c = mfma16(x[m].w, y[m].w, c);
+  }
+  return c;
+}
+
+// Score rows in LDS: row stride a multiple of 64 floats plus 4, so the MFMA
+// operand reads (16 rows x 4 consecutive tiles) and the result writes (4 rows x
+// 16 consecutive tiles) touch 64 distinct banks.
+__host__ __device__ __forceinline__ int score_ld(int KVb) { return ((KVb + 63) & ~63) + 4; }
+// the first LDS area also takes the 4 x 16 x HD partial sums of a row-times-
+// matrix product once its rows are consumed
+__host__ __device__ __forceinline__ long long row_area(int cr, int KVb) {
+  const long long n = (long long)cr * score_ld(KVb);
+  return n > 4LL * MR * HD ? n : 4LL * MR * HD;
+}
+
+// Out[r][d] = sum_j W[r][j] M[j][d] for the rows r < nr of a 16-row block, W in
+// LDS (stride ld), M pooled rows of HD floats. Wave w: d half (w & 1) and every
+// fourth group of four j (w >> 1); lane (r, kk) feeds W[r][j] as A and M[j][64
+// half + 4 r + c] as B of the MFMA whose accumulator c holds d = 64 half + 4 n +
+// c. The four partial sums meet in `red` (aliasing W: callers sync first), and
+// out(row, d, value) stores the sums in fixed order.
+template <class RowPtr, class Out>
+__device__ __forceinline__ void rows_times_pooled(const float* W, int ld, int nr, int KVb,
+                                                  RowPtr mrow, float* red, Out out) {
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kk = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave & 1, qj = wave >> 1;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nst = (KVb + 3) / 4;
+  const bool row_ok = r < nr;
+  // RB steps per batch, the next batch's loads issued before this batch's
+  // MFMAs (steps past the end add W = 0 times a clamped row)
+  constexpr int RB = 8;
+  float4 mb[RB], mn[RB];
+  auto load = [&](int t0, float4 (&m)[RB]) {
+#pragma unroll
+    for (int e = 0; e < RB; ++e) {
+      const int j = min(4 * (t0 + 4 * e) + kk, KVb - 1);
+      m[e] = *reinterpret_cast<const float4*>(mrow(j) + 64 * half + 4 * r);
+    }
+  };
+  auto step = [&](int t0, const float4 (&m)[RB]) {
+#pragma unroll
+    for (int e = 0; e < RB; ++e) {
+      const int j = 4 * (t0 + 4 * e) + kk;
+      const float w = (row_ok && j < KVb) ? W[r * ld + j] : 0.f;
+      acc[0] = mfma16(w, m[e].x, acc[0]);
+      acc[1] = mfma16(w, m[e].y, acc[1]);
+      acc[2] = mfma16(w, m[e].z, acc[2]);
+      acc[3] = mfma16(w, m[e].w, acc[3]);
+    }
+  };
+  if (qj < nst) load(qj, mb);
+  for (int t0 = qj; t0 < nst; t0 += 8 * RB) {
+    const int t1 = t0 + 4 * RB, t2 = t0 + 8 * RB;
+    if (t1 < nst) load(t1, mn);
+    step(t0, mb);
+    if (t2 < nst) load(t2, mb);
+    if (t1 < nst) step(t1, mn);
+  }
+  __syncthreads();  // W consumed
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(qj * MR + 4 * kk + v) * HD + 64 * half + 4 * r + c] = acc[c][v];
+  __syncthreads();
+  for (int t = tid; t < nr * HD; t += NWC * 64) {
+    const int row = t / HD, d = t % HD;
+    const float* x = red + row * HD + d;
+    out(row, d, ((x[0] + x[MR * HD]) + x[2 * MR * HD]) + x[3 * MR * HD]);
+  }
+}
+
 // Coarse scores for CR Q tiles, then (optionally) top-k -> map bytes and the
-// coarse attention O_c / lse_c. Dynamic LDS: sc[CR][KVb], qcs[CR][HD],
-// hist[4][256] and a staging tile of CT pooled K (transposed) or V rows. The
-// pooled K and V rows are streamed through the tile with coalesced loads; every
-// score and every O_c element keeps its sequential accumulation order over d
-// (scores) and over the KV tiles (O_c).
-constexpr int CT = 64;               // pooled rows per staging tile
-constexpr int CT_LD = CT + 1;        // padded row of the transposed K tile
-constexpr int TILE_FLOATS = HD * CT_LD;
-constexpr int TILE_LOADS = CT * HD / 4 / 256;  // 16-byte loads per thread for one tile
-// CR is a template argument: with a run-time row count every "r < CR" test
-// becomes a branch around one FMA and serialises the LDS reads behind it.
+// coarse attention O_c / lse_c. Dynamic LDS: sc[CR][score_ld] (at least the
+// 4 x 16 x HD partial sums of O_c) and hist[NWC][256]. Each wave forms 16 x 16
+// score blocks on the matrix cores with its Q rows and the block's pooled K rows
+// in registers (loaded straight from global memory, 16 bytes per lane); top-k is
+// a 4-pass 8-bit radix select per row; O_c = P_c V_c reads P_c from LDS and the
+// pooled V rows from global memory.
+// CR is a template argument so that the per-row stores unroll.
 template <int CR>
-__global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int want_topk, int want_gate) {
+__global__ __launch_bounds__(NWC * 64) void coarse_fwd_kernel(const CoarseArgs a, int want_topk, int want_gate) {
   extern __shared__ float dsm[];
   const Geom& g = a.g;
-  const int KVb = g.KVb;
+  const int KVb = g.KVb, LD = score_ld(KVb);
   float* sc = dsm;
-  float* qcs = sc + CR * KVb;
-  int* hist = reinterpret_cast<int*>(qcs + CR * HD);
-  float* tile = reinterpret_cast<float*>(hist + 4 * 256);
+  int* hist = reinterpret_cast<int*>(dsm + row_area(CR, KVb));
   const int nrb = (g.Qb + CR - 1) / CR;
   int id = blockIdx.x;
   const int rb = id % nrb;
@@ -95,68 +199,51 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
   const int h = id % g.Hq, b = id / g.Hq;
   const int hk = h / g.group;
   const int i0 = rb * CR, nr = min(CR, g.Qb - i0);
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kk = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  for (int t = tid; t < CR * HD; t += 256) {
-    const int r = t / HD, d = t % HD;
-    qcs[t] = r < nr ? a.qc[g.pq(b, h, i0 + r) + d] : 0.f;
-  }
-  __syncthreads();
-  // scores, CT KV tiles at a time: the tiles' pooled K rows are staged
-  // transposed (tile[d][j]); thread (wave w, lane j) forms rows w, w+4, .. of
-  // column j, accumulating over d in order
-  for (int j0 = 0; j0 < KVb; j0 += CT) {
-    __syncthreads();  // the previous tile is consumed
-    float4 kv[TILE_LOADS];  // all loads of the tile in flight at once
+  // scores: wave w takes the 16-tile column blocks w, w + NWC, ...
+  float4 qx[HD16];
+  if (r < nr) load_row(qx, a.qc + g.pq(b, h, i0 + r), kk);
+  else zero_row(qx);
+  // the next block's K rows are loaded while this block's MFMAs run
+  const int nblk = (KVb + 15) / 16;
+  auto kload = [&](int cb, float4 (&ky)[HD16]) {
+    load_row(ky, a.kc + g.pk(b, hk, min(cb * 16 + r, KVb - 1)), kk);
+  };
+  auto scores = [&](int cb, const float4 (&ky)[HD16]) {
+    const int j = cb * 16 + r;
+    const f32x4_t c = rowdot16(qx, ky);
+    if (j < KVb) {
+      const bool valid = g.kv_val(b, j) > 0;
 #pragma unroll
-    for (int k = 0; k < TILE_LOADS; ++k) {
-      const int t = tid + 256 * k, jj = t / (HD / 4), d4 = t % (HD / 4), j = min(j0 + jj, KVb - 1);
-      kv[k] = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j))[d4];
+      for (int v = 0; v < 4; ++v)
+        if (4 * kk + v < CR) sc[(4 * kk + v) * LD + j] = valid ? g.scale * c[v] : -INFINITY;
     }
-#pragma unroll
-    for (int k = 0; k < TILE_LOADS; ++k) {
-      const int t = tid + 256 * k, jj = t / (HD / 4), d4 = t % (HD / 4);
-      tile[(4 * d4 + 0) * CT_LD + jj] = kv[k].x;
-      tile[(4 * d4 + 1) * CT_LD + jj] = kv[k].y;
-      tile[(4 * d4 + 2) * CT_LD + jj] = kv[k].z;
-      tile[(4 * d4 + 3) * CT_LD + jj] = kv[k].w;
-    }
-    __syncthreads();
-    // rows wave + 4u, u < RU (all of them exist when CR is a multiple of 4)
-    constexpr int RU = (CR + 3) / 4;
-    const int j = j0 + lane;
-    float acc[RU];
-#pragma unroll
-    for (int u = 0; u < RU; ++u) acc[u] = 0.f;
-    if (CR % 4 == 0 || wave < CR) {
-#pragma unroll 8
-      for (int d = 0; d < HD; ++d) {
-        const float kv = tile[d * CT_LD + lane];
-#pragma unroll
-        for (int u = 0; u < RU; ++u) acc[u] = __builtin_fmaf(qcs[(wave + 4 * u) * HD + d], kv, acc[u]);
-      }
-      if (j < KVb) {
-        const bool valid = g.kv_val(b, j) > 0;
-#pragma unroll
-        for (int u = 0; u < RU; ++u) sc[(wave + 4 * u) * KVb + j] = valid ? g.scale * acc[u] : -INFINITY;
-      }
-    }
+  };
+  float4 ka[HD16], kb[HD16];
+  if (wave < nblk) kload(wave, ka);
+  for (int cb = wave; cb < nblk; cb += 2 * NWC) {
+    const int c1 = cb + NWC, c2 = cb + 2 * NWC;
+    if (c1 < nblk) kload(c1, kb);
+    scores(cb, ka);
+    if (c2 < nblk) kload(c2, ka);
+    if (c1 < nblk) scores(c1, kb);
   }
   __syncthreads();
 
   if (want_topk) {
     int* hw = hist + wave * 256;
-    for (int r = wave; r < nr; r += 4) {
-      const float* row = sc + r * KVb;
+    for (int rr = wave; rr < nr; rr += NWC) {
+      const float* row = sc + rr * LD;
       int nv = 0;
       for (int j0 = 0; j0 < KVb; j0 += 64) {
         const int j = j0 + lane;
         nv += __popcll(__ballot(j < KVb && row[j] != -INFINITY));
       }
-      int kk = min(a.topk, nv);
+      int kth = min(a.topk, nv);
       uint32_t prefix = 0, pmask = 0;
-      if (kk > 0) {
+      if (kth > 0) {
         for (int shift = 24; shift >= 0; shift -= 8) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) hw[lane * 4 + u] = 0;
@@ -181,7 +268,7 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
             const int v = __shfl_up(incl, off, 64);
             if (lane >= off) incl += v;
           }
-          const unsigned long long hit = __ballot(incl >= kk);
+          const unsigned long long hit = __ballot(incl >= kth);
           const int L = __ffsll((long long)hit) - 1;
           int above = __shfl(incl - tot, L, 64);  // elements in bins above lane L's
           int digit = 0;
@@ -189,7 +276,7 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
             int acc = above;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              if (acc + cnt[u] >= kk) {
+              if (acc + cnt[u] >= kth) {
                 digit = 255 - 4 * lane - u;
                 above = acc;
                 break;
@@ -199,14 +286,14 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
           }
           digit = __shfl(digit, L, 64);
           above = __shfl(above, L, 64);
-          kk -= above;
+          kth -= above;
           prefix |= (uint32_t)digit << shift;
           pmask |= 0xffu << shift;
           __builtin_amdgcn_wave_barrier();
         }
       }
-      // select: keys above the threshold, plus the first kk keys equal to it
-      uint8_t* mrow = a.map + (((long long)b * g.Hq + h) * g.Qb + i0 + r) * KVb;
+      // select: keys above the threshold, plus the first kth keys equal to it
+      uint8_t* mrow = a.map + (((long long)b * g.Hq + h) * g.Qb + i0 + rr) * KVb;
       int taken_eq = 0;
       const unsigned long long below = (1ull << lane) - 1ull;
       for (int j0 = 0; j0 < KVb; j0 += 64) {
@@ -217,7 +304,7 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
         const bool eq = valid && u == prefix;
         const unsigned long long be = __ballot(eq);
         const int rank = taken_eq + __popcll(be & below);
-        const bool sel = valid && (u > prefix || (eq && rank < kk));
+        const bool sel = valid && (u > prefix || (eq && rank < kth));
         if (j < KVb) mrow[j] = sel ? 1 : 0;
         taken_eq += __popcll(be);
       }
@@ -227,8 +314,8 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
   if (want_gate) {
     __syncthreads();
     // row softmax in place, lse_c
-    for (int r = wave; r < nr; r += 4) {
-      float* row = sc + r * KVb;
+    for (int rr = wave; rr < nr; rr += NWC) {
+      float* row = sc + rr * LD;
       float m = -INFINITY;
       for (int j = lane; j < KVb; j += 64) m = fmaxf(m, row[j]);
 #pragma unroll
@@ -240,224 +327,233 @@ __global__ __launch_bounds__(256) void coarse_fwd_kernel(const CoarseArgs a, int
       for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
       const float inv = l > 0.f ? 1.f / l : 0.f;
       for (int j = lane; j < KVb; j += 64) row[j] = m == -INFINITY ? 0.f : __expf(row[j] - m) * inv;
-      if (lane == 0) a.lse_c[((long long)b * g.Hq + h) * g.Qb + i0 + r] = l > 0.f ? m + __logf(l) : -INFINITY;
+      if (lane == 0) a.lse_c[((long long)b * g.Hq + h) * g.Qb + i0 + rr] = l > 0.f ? m + __logf(l) : -INFINITY;
     }
     __syncthreads();
-    // O_c[r][d] = sum_j P[r][j] V_c[j][d], CT pooled V rows at a time (tile[j][d])
-    const int d = tid & (HD - 1), half = tid >> 7;
-    float acc[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-    for (int j0 = 0; j0 < KVb; j0 += CT) {
-      __syncthreads();  // the previous tile is consumed
-      float4 vv[TILE_LOADS];
-#pragma unroll
-      for (int k = 0; k < TILE_LOADS; ++k) {
-        const int t = tid + 256 * k, jj = t / (HD / 4), d4 = t % (HD / 4), j = min(j0 + jj, KVb - 1);
-        vv[k] = reinterpret_cast<const float4*>(a.vc + g.pk(b, hk, j))[d4];
-      }
-#pragma unroll
-      for (int k = 0; k < TILE_LOADS; ++k) reinterpret_cast<float4*>(tile)[tid + 256 * k] = vv[k];
-      __syncthreads();
-      const int nj = min(CT, KVb - j0);
-      if (CR == 16 || half * 8 < CR) {
-#pragma unroll 4
-        for (int jj = 0; jj < nj; ++jj) {
-          const float v = tile[jj * HD + d];
-#pragma unroll
-          for (int u = 0; u < (CR < 8 ? CR : 8); ++u)
-            acc[u] = __builtin_fmaf(sc[(half * 8 + u) * KVb + j0 + jj], v, acc[u]);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int r = half * 8 + u;
-      if (r < nr) a.oc[g.pq(b, h, i0 + r) + d] = acc[u];
-    }
+    // O_c = P_c V_c
+    rows_times_pooled(sc, LD, nr, KVb, [&](int j) { return a.vc + g.pk(b, hk, j); }, sc,
+                      [&](int row, int d, float o) { a.oc[g.pq(b, h, i0 + row) + d] = o; });
   }
 }
 
-// Coarse backward, row form: P_c, dS_c for CR2 rows (kept in workspace for the
-// column pass) and dQ_c = scale dS_c K_c. For dQ_c the pooled K rows stream
-// through an LDS tile with all loads of a tile in flight.
-// 8 rows per work-group (CR2): with 4, two work-groups share a CU at 1440 KV
-// tiles, but twice as many row blocks then stream every pooled K/V row (6 %
-// slower). With more KV tiles than 8 rows of P_c and dS_c fit in LDS, the
-// launch takes 4, 2 or 1 rows per work-group.
-constexpr int CT2 = 32;                  // pooled K rows per staging tile
-constexpr int TILE2_FLOATS = CT2 * HD;
-template <int CR2>
-__global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const CoarseArgs a) {
+// Coarse backward, row form, 16 Q tiles per work-group. The scores are formed
+// transposed on the matrix cores, C^T = K_c Q_c^T and dP^T = V_c dO_c^T, so
+// lane (r, kk) ends with row r at tiles j = 16 cb + 4 kk + v (v < 4), exactly
+// the A operand of a product over j. In the same sweep it takes P = exp(C -
+// lse_c), W = P dP, the row sum s = sum_j W, and accumulates U = W K_c and
+// Z = P K_c; dQ_c = scale (U - s Z) = scale dS_c K_c with dS_c = P (dP - s).
+// P and W go to the workspace with s per row; the column pass forms dS_c =
+// W - s P from them. Dynamic LDS: the q_c and dO_c rows (B operands of the
+// scores), then the waves' partial U, Z and s.
+constexpr int QLD = HD + 4;  // padded pooled row: conflict-free 16-byte reads
+__global__ __launch_bounds__(NWC * 64) void coarse_bwd_rows_kernel(const CoarseArgs a) {
   extern __shared__ float dsm[];
+  float* qs = dsm;                       // [MR][QLD]
+  float* os = qs + MR * QLD;             // [MR][QLD]
+  float* red = dsm;                      // after the sweep: [NWC][2][MR][HD]
+  float* ssum = dsm + NWC * 2 * MR * HD; // [NWC][MR]
   const Geom& g = a.g;
   const int KVb = g.KVb;
-  float* P = dsm;                 // [CR2][KVb]
-  float* dS = P + CR2 * KVb;      // [CR2][KVb]
-  float* qcs = dS + CR2 * KVb;    // [CR2][HD]
-  float* dos = qcs + CR2 * HD;    // [CR2][HD]
-  float* lsc = dos + CR2 * HD;    // [CR2]
-  float* tile = lsc + CR2;        // [CT2][HD]
-  const int nrb = (g.Qb + CR2 - 1) / CR2;
+  const int nrb = (g.Qb + MR - 1) / MR;
   int id = blockIdx.x;
   const int rb = id % nrb;
   id /= nrb;
   const int h = id % g.Hq, b = id / g.Hq;
   const int hk = h / g.group;
-  const int i0 = rb * CR2, nr = min(CR2, g.Qb - i0);
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int i0 = rb * MR, nr = min(MR, g.Qb - i0);
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kk = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  for (int t = tid; t < CR2 * HD; t += 256) {
-    const int r = t / HD, d = t % HD;
-    qcs[t] = r < nr ? a.qc[g.pq(b, h, i0 + r) + d] : 0.f;
-    dos[t] = r < nr ? a.doc[g.pq(b, h, i0 + r) + d] : 0.f;
+  const long long rowbase = ((long long)b * g.Hq + h) * g.Qb + i0;
+
+  for (int t = tid; t < MR * HD / 4; t += NWC * 64) {
+    const int row = t / (HD / 4), d = 4 * (t % (HD / 4));
+    const bool ok = row < nr;
+    *reinterpret_cast<float4*>(qs + row * QLD + d) =
+        ok ? *reinterpret_cast<const float4*>(a.qc + g.pq(b, h, i0 + row) + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(os + row * QLD + d) =
+        ok ? *reinterpret_cast<const float4*>(a.doc + g.pq(b, h, i0 + row) + d) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (tid < CR2) lsc[tid] = tid < nr ? a.lse_c[((long long)b * g.Hq + h) * g.Qb + i0 + tid] : -INFINITY;
   __syncthreads();
-  for (int j = tid; j < KVb; j += 256) {
-    const bool valid = g.kv_val(b, j) > 0;
-    float cs[CR2], dp[CR2];
+  const bool row_ok = r < nr;
+  const float lse_r = row_ok ? a.lse_c[rowbase + r] : -INFINITY;
+  float* prow = a.ps + (rowbase + r) * KVb;
+  float* wrow = a.dss + (rowbase + r) * KVb;
+  const bool vec_store = (KVb & 3) == 0;
+
+  f32x4_t U[2][4], Z[2][4];
 #pragma unroll
-    for (int r = 0; r < CR2; ++r) cs[r] = dp[r] = 0.f;
-    if (valid) {
-      const float4* kp = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j));
-      const float4* vp = reinterpret_cast<const float4*>(a.vc + g.pk(b, hk, j));
-      // unrolled so that the loads of eight steps are in flight together
-      // (one step at a time waits out an L2 round trip per 4 elements)
-#pragma unroll 8
-      for (int d4 = 0; d4 < HD / 4; ++d4) {
-        const float4 kv = kp[d4], vv = vp[d4];
+  for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int r = 0; r < CR2; ++r) {
-          const float4 qv = *reinterpret_cast<const float4*>(qcs + r * HD + 4 * d4);
-          const float4 ov = *reinterpret_cast<const float4*>(dos + r * HD + 4 * d4);
-          cs[r] += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
-          dp[r] += ov.x * vv.x + ov.y * vv.y + ov.z * vv.z + ov.w * vv.w;
-        }
+    for (int c = 0; c < 4; ++c) U[h2][c] = Z[h2][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float sacc = 0.f;
+  const int nblk = (KVb + 15) / 16;
+  auto kvload = [&](int cb, float4 (&ky)[HD16], float4 (&vy)[HD16]) {
+    const int jc = min(cb * 16 + r, KVb - 1);
+    load_row(ky, a.kc + g.pk(b, hk, jc), kk);
+    load_row(vy, a.vc + g.pk(b, hk, jc), kk);
+  };
+  for (int cb = wave; cb < nblk; cb += NWC) {
+    float4 ky[HD16], vy[HD16];
+    kvload(cb, ky, vy);
+    // this block's K rows as the B operand of U and Z (tile 16 cb + 4 kk + v,
+    // d = 64 h2 + 4 r + {0..3}), loaded while the scores run
+    float4 kd[4][2];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        kd[v][h2] = *reinterpret_cast<const float4*>(
+            a.kc + g.pk(b, hk, min(cb * 16 + 4 * kk + v, KVb - 1)) + 64 * h2 + 4 * r);
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < HD16; ++m) {
+      const float4 q = *reinterpret_cast<const float4*>(qs + r * QLD + 16 * m + 4 * kk);
+      const float4 o = *reinterpret_cast<const float4*>(os + r * QLD + 16 * m + 4 * kk);
+      c = mfma16(ky[m].x, q.x, c);
+      c = mfma16(ky[m].y, q.y, c);
+      c = mfma16(ky[m].z, q.z, c);
+      c = mfma16(ky[m].w, q.w, c);
+      dp = mfma16(vy[m].x, o.x, dp);
+      dp = mfma16(vy[m].y, o.y, dp);
+      dp = mfma16(vy[m].z, o.z, dp);
+      dp = mfma16(vy[m].w, o.w, dp);
+    }
+    const int j0 = cb * 16 + 4 * kk;
+    float pv[4], wv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = j0 + v;
+      const bool valid = j < KVb && lse_r != -INFINITY && g.kv_val(b, j) > 0;
+      const float p = valid ? __expf(g.scale * c[v] - lse_r) : 0.f;
+      pv[v] = p;
+      wv[v] = p == 0.f ? 0.f : p * dp[v];
+      sacc += wv[v];
+    }
+    if (row_ok) {
+      if (vec_store && j0 + 3 < KVb) {
+        *reinterpret_cast<float4*>(prow + j0) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        *reinterpret_cast<float4*>(wrow + j0) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (j0 + v < KVb) {
+            prow[j0 + v] = pv[v];
+            wrow[j0 + v] = wv[v];
+          }
       }
     }
 #pragma unroll
-    for (int r = 0; r < CR2; ++r) {
-      const float p = (valid && lsc[r] != -INFINITY) ? __expf(g.scale * cs[r] - lsc[r]) : 0.f;
-      P[r * KVb + j] = p;
-      dS[r * KVb + j] = p == 0.f ? 0.f : dp[r];
-    }
-  }
-  __syncthreads();
-  for (int rr = wave; rr < nr; rr += 4) {
-    float s = 0.f;
-    for (int j = lane; j < KVb; j += 64) s += P[rr * KVb + j] * dS[rr * KVb + j];
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    const long long ro = (((long long)b * g.Hq + h) * g.Qb + i0 + rr) * KVb;
-    for (int j = lane; j < KVb; j += 64) {
-      const float p = P[rr * KVb + j];
-      const float ds = p * (dS[rr * KVb + j] - s);
-      dS[rr * KVb + j] = ds;
-      a.dss[ro + j] = ds;
-      a.ps[ro + j] = p;
-    }
-  }
-  // dQ_c[r][d] = scale sum_j dS_c[r][j] K_c[j][d], CT2 pooled K rows at a time (tile[j][d])
-  constexpr int RH = CR2 > 1 ? CR2 / 2 : 1;  // rows per half of the work-group
-  const int d = tid & (HD - 1), half = tid >> 7;
-  const bool rows_here = half * RH < CR2;  // one row: the second half idles
-  float acc[RH];
-#pragma unroll
-  for (int u = 0; u < RH; ++u) acc[u] = 0.f;
-  constexpr int KLOADS = CT2 * HD / 4 / 256;
-  for (int j0 = 0; j0 < KVb; j0 += CT2) {
-    __syncthreads();  // dS is final / the previous tile is consumed
-    float4 x[KLOADS];
-#pragma unroll
-    for (int k = 0; k < KLOADS; ++k) {
-      const int t = tid + 256 * k, j = min(j0 + t / (HD / 4), KVb - 1), d4 = t % (HD / 4);
-      x[k] = reinterpret_cast<const float4*>(a.kc + g.pk(b, hk, j))[d4];
-    }
-#pragma unroll
-    for (int k = 0; k < KLOADS; ++k) reinterpret_cast<float4*>(tile)[tid + 256 * k] = x[k];
-    __syncthreads();
-    const int nj = min(CT2, KVb - j0);
-    if (rows_here) {
-#pragma unroll 4
-      for (int jt = 0; jt < nj; ++jt) {
-        const float kv = tile[jt * HD + d];
-#pragma unroll
-        for (int u = 0; u < RH; ++u) acc[u] = __builtin_fmaf(dS[(half * RH + u) * KVb + j0 + jt], kv, acc[u]);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        U[h2][0] = mfma16(wv[v], kd[v][h2].x, U[h2][0]);
+        U[h2][1] = mfma16(wv[v], kd[v][h2].y, U[h2][1]);
+        U[h2][2] = mfma16(wv[v], kd[v][h2].z, U[h2][2]);
+        U[h2][3] = mfma16(wv[v], kd[v][h2].w, U[h2][3]);
+        Z[h2][0] = mfma16(pv[v], kd[v][h2].x, Z[h2][0]);
+        Z[h2][1] = mfma16(pv[v], kd[v][h2].y, Z[h2][1]);
+        Z[h2][2] = mfma16(pv[v], kd[v][h2].z, Z[h2][2]);
+        Z[h2][3] = mfma16(pv[v], kd[v][h2].w, Z[h2][3]);
       }
-    }
   }
+  sacc += __shfl_xor(sacc, 16, 64);
+  sacc += __shfl_xor(sacc, 32, 64);
+  __syncthreads();  // q_c, dO_c consumed: the area takes the partial sums
+  if (kk == 0) ssum[wave * MR + r] = sacc;
 #pragma unroll
-  for (int u = 0; u < RH; ++u) {
-    const int rr = half * RH + u;
-    if (rows_here && rr < nr) a.dqc[g.pq(b, h, i0 + rr) + d] = g.scale * acc[u];
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int o = (4 * kk + v) * HD + 64 * h2 + 4 * r + c;
+        red[(wave * 2 + 0) * MR * HD + o] = U[h2][c][v];
+        red[(wave * 2 + 1) * MR * HD + o] = Z[h2][c][v];
+      }
+  __syncthreads();
+  if (tid < nr) {
+    float sr = 0.f;
+    for (int w = 0; w < NWC; ++w) sr += ssum[w * MR + tid];
+    a.csum[rowbase + tid] = sr;
+  }
+  for (int t = tid; t < nr * HD; t += NWC * 64) {
+    const int row = t / HD, d = t % HD;
+    float sr = 0.f, u = 0.f, z = 0.f;
+    for (int w = 0; w < NWC; ++w) {
+      sr += ssum[w * MR + row];
+      u += red[(w * 2 + 0) * MR * HD + t];
+      z += red[(w * 2 + 1) * MR * HD + t];
+    }
+    a.dqc[g.pq(b, h, i0 + row) + d] = g.scale * (u - sr * z);
   }
 }
 
-// Coarse backward, column form: dK_c = scale sum dS_c^T Q_c, dV_c = sum P_c^T dO_c
-// over the Q heads of the group (16 KV tiles per work-group, thread = (d, 8
-// tiles)). The Q tiles' pooled rows and this block's dS_c / P_c columns are
-// staged in LDS CI tiles at a time, all loads of a stage in flight.
-constexpr int CC = 16;
-constexpr int CI = 32;
+// Coarse backward, column form: dK_c = scale sum dS_c^T Q_c and dV_c = sum
+// P_c^T dO_c over the Q tiles of every head of the group. A work-group owns 32
+// KV tiles (two 16-row MFMA blocks per wave); wave w computes dK_c (w even) or
+// dV_c (w odd) for the d half w >> 1, lane (r, kk) feeding dS_c[i][j] = W - s_i
+// P (or P_c) as A and Q_c[i][64 half + 4 r + c] (or dO_c) as B, four tiles i
+// per step.
+constexpr int CCOL = 32;
 __global__ __launch_bounds__(256) void coarse_bwd_cols_kernel(const CoarseArgs a) {
-  __shared__ float4 qo[2][CI][HD / 4];  // q_c | dO_c rows
-  __shared__ float pd[2][CI][CC];       // dS_c | P_c of this block's columns
   const Geom& g = a.g;
   const int KVb = g.KVb;
-  const int ncb = (KVb + CC - 1) / CC;
+  const int ncb = (KVb + CCOL - 1) / CCOL;
   int id = blockIdx.x;
   const int cb = id % ncb;
   id /= ncb;
   const int hk = id % g.Hkv, b = id / g.Hkv;
-  const int tid = threadIdx.x, d = tid & (HD - 1), half = tid >> 7;
-  const int j0 = cb * CC + half * 8;
-  float dk[8], dv[8];
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kk = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int is_v = wave & 1, half = wave >> 1;
+  const float* A = is_v ? a.ps : a.dss;
+  const float* X = is_v ? a.doc : a.qc;
+  const int j0 = cb * CCOL;
+  f32x4_t acc[2][4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) dk[u] = dv[u] = 0.f;
-  constexpr int QLOADS = 2 * CI * HD / 4 / 256, PLOADS = 2 * CI * CC / 256;
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[u][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bool ok0 = j0 + r < KVb, ok1 = j0 + 16 + r < KVb;
+  const int nst = (g.Qb + 3) / 4;
   for (int hh = 0; hh < g.group; ++hh) {
     const int h = hk * g.group + hh;
-    for (int i0 = 0; i0 < g.Qb; i0 += CI) {
-      float4 x[QLOADS];
-      float y[PLOADS];
-#pragma unroll
-      for (int k = 0; k < QLOADS; ++k) {
-        const int t = tid + 256 * k, arr = t / (CI * HD / 4), rem = t % (CI * HD / 4);
-        const int i = min(i0 + rem / (HD / 4), g.Qb - 1), d4 = rem % (HD / 4);
-        x[k] = reinterpret_cast<const float4*>((arr ? a.doc : a.qc) + g.pq(b, h, i))[d4];
+    const long long rowbase = ((long long)b * g.Hq + h) * g.Qb;
+#pragma unroll 8
+    for (int t = 0; t < nst; ++t) {
+      const int i = 4 * t + kk, ic = min(i, g.Qb - 1);
+      const float4 x = *reinterpret_cast<const float4*>(X + g.pq(b, h, ic) + 64 * half + 4 * r);
+      const float* arow = A + (rowbase + ic) * KVb + j0 + r;
+      float a0 = (i < g.Qb && ok0) ? arow[0] : 0.f;
+      float a1 = (i < g.Qb && ok1) ? arow[16] : 0.f;
+      if (!is_v) {  // dS_c = W - s P
+        const float* prow = a.ps + (rowbase + ic) * KVb + j0 + r;
+        const float si = a.csum[rowbase + ic];
+        a0 = (i < g.Qb && ok0) ? a0 - si * prow[0] : 0.f;
+        a1 = (i < g.Qb && ok1) ? a1 - si * prow[16] : 0.f;
       }
-#pragma unroll
-      for (int k = 0; k < PLOADS; ++k) {
-        const int t = tid + 256 * k, arr = t / (CI * CC), rem = t % (CI * CC);
-        const int i = min(i0 + rem / CC, g.Qb - 1), j = cb * CC + rem % CC;
-        const long long ro = (((long long)b * g.Hq + h) * g.Qb + i) * KVb;
-        y[k] = j < KVb ? (arr ? a.ps : a.dss)[ro + j] : 0.f;
-      }
-      __syncthreads();  // the previous stage is consumed
-#pragma unroll
-      for (int k = 0; k < QLOADS; ++k) (&qo[0][0][0])[tid + 256 * k] = x[k];
-#pragma unroll
-      for (int k = 0; k < PLOADS; ++k) (&pd[0][0][0])[tid + 256 * k] = y[k];
-      __syncthreads();
-      const int ni = min(CI, g.Qb - i0);
-      const float* qrow = reinterpret_cast<const float*>(&qo[0][0][0]);
-      const float* orow = reinterpret_cast<const float*>(&qo[1][0][0]);
-      for (int ii = 0; ii < ni; ++ii) {
-        const float q = qrow[ii * HD + d], o = orow[ii * HD + d];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          dk[u] = __builtin_fmaf(pd[0][ii][half * 8 + u], q, dk[u]);
-          dv[u] = __builtin_fmaf(pd[1][ii][half * 8 + u], o, dv[u]);
-        }
-      }
+      acc[0][0] = mfma16(a0, x.x, acc[0][0]);
+      acc[0][1] = mfma16(a0, x.y, acc[0][1]);
+      acc[0][2] = mfma16(a0, x.z, acc[0][2]);
+      acc[0][3] = mfma16(a0, x.w, acc[0][3]);
+      acc[1][0] = mfma16(a1, x.x, acc[1][0]);
+      acc[1][1] = mfma16(a1, x.y, acc[1][1]);
+      acc[1][2] = mfma16(a1, x.z, acc[1][2]);
+      acc[1][3] = mfma16(a1, x.w, acc[1][3]);
     }
   }
+  float* out = is_v ? a.dvc : a.dkc;
+  const float f = is_v ? 1.f : g.scale;
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    if (j0 + u < KVb) {
-      a.dkc[g.pk(b, hk, j0 + u) + d] = g.scale * dk[u];
-      a.dvc[g.pk(b, hk, j0 + u) + d] = dv[u];
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = j0 + 16 * u + 4 * kk + v;
+      if (j < KVb) {
+        float* o = out + g.pk(b, hk, j) + 64 * half + 4 * r;
+        *reinterpret_cast<float4*>(o) =
+            make_float4(f * acc[u][0][v], f * acc[u][1][v], f * acc[u][2][v], f * acc[u][3][v]);
+      }
     }
 }
 
@@ -474,32 +570,20 @@ __global__ void zero_kernel(uint8_t* p, size_t n) {
 }  // namespace
 
 namespace {
-size_t rows_lds(int cr2, int KVb) {
-  return ((size_t)2 * cr2 * KVb + 2 * cr2 * HD + cr2 + TILE2_FLOATS) * 4;
-}
-// rows per work-group of the coarse backward: 8 when they fit, else fewer
-int coarse_bwd_rows(int KVb) {
-  for (int cr = 8; cr > 1; cr >>= 1)
-    if (rows_lds(cr, KVb) <= 160 * 1024) return cr;
-  return 1;
-}
+size_t fwd_lds(int cr, int KVb) { return (size_t)(row_area(cr, KVb) + NWC * 256) * 4; }
+constexpr size_t ROWS_LDS = (size_t)(NWC * 2 * MR * HD + NWC * MR) * 4;
+static_assert(2 * MR * QLD <= NWC * 2 * MR * HD, "pooled rows fit the partial-sum area");
 }  // namespace
 
-// LDS of the coarse backward's row pass at its launch shape (above 160 KiB:
-// too many KV tiles for these kernels)
-size_t coarse_bwd_lds(int KVb) { return rows_lds(coarse_bwd_rows(KVb), KVb); }
+// LDS of the coarse backward's row pass (independent of the KV tile count)
+size_t coarse_bwd_lds(int) { return ROWS_LDS; }
 
+// Q tiles per work-group of the coarse forward: the most (up to one 16-row MFMA
+// block) whose score rows fit in LDS; 0: KVb too large for these kernels.
 int coarse_rows_per_block(int KVb) {
-  // scores [CR][KVb] + qc [CR][HD] + 4 histograms + the staging tile. Prefer
-  // the largest CR with which two work-groups share a CU's 160 KiB (a single
-  // four-wave work-group leaves each SIMD one wave to hide LDS latency with),
-  // else the largest that fits at all.
-  auto need = [&](int cr) { return ((long long)cr * (KVb + HD) + 4 * 256 + TILE_FLOATS) * 4; };
   for (int cr = 16; cr >= 1; cr >>= 1)
-    if (need(cr) <= 80 * 1024) return cr;
-  int cr = 16;
-  while (cr > 1 && need(cr) > 160 * 1024) cr >>= 1;
-  return need(cr) <= 160 * 1024 ? cr : 0;  // 0: KVb too large for these kernels
+    if (fwd_lds(cr, KVb) <= 160 * 1024) return cr;
+  return 0;
 }
 
 hipError_t launch_pool(const Geom& g, int dtype, const void* q, const void* k, const void* v,
@@ -524,29 +608,24 @@ hipError_t launch_coarse_fwd(const CoarseArgs& a, bool want_topk, bool want_gate
   const int cr = coarse_rows_per_block(g.KVb);
   const long long n = (long long)g.B * g.Hq * ((g.Qb + cr - 1) / cr);
   if (n == 0) return hipSuccess;
-  const size_t lds = ((size_t)cr * (g.KVb + HD) + 4 * 256 + TILE_FLOATS) * 4;
+  const size_t lds = fwd_lds(cr, g.KVb);
   const int tk = want_topk ? 1 : 0, gt = want_gate ? 1 : 0;
   switch (cr) {
-    case 16: coarse_fwd_kernel<16><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
-    case 8: coarse_fwd_kernel<8><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
-    case 4: coarse_fwd_kernel<4><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
-    case 2: coarse_fwd_kernel<2><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
-    default: coarse_fwd_kernel<1><<<(unsigned)n, 256, lds, st>>>(a, tk, gt); break;
+    case 16: coarse_fwd_kernel<16><<<(unsigned)n, NWC * 64, lds, st>>>(a, tk, gt); break;
+    case 8: coarse_fwd_kernel<8><<<(unsigned)n, NWC * 64, lds, st>>>(a, tk, gt); break;
+    case 4: coarse_fwd_kernel<4><<<(unsigned)n, NWC * 64, lds, st>>>(a, tk, gt); break;
+    case 2: coarse_fwd_kernel<2><<<(unsigned)n, NWC * 64, lds, st>>>(a, tk, gt); break;
+    default: coarse_fwd_kernel<1><<<(unsigned)n, NWC * 64, lds, st>>>(a, tk, gt); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_coarse_bwd(const CoarseArgs& a, hipStream_t st) {
   const Geom& g = a.g;
-  const int cr2 = coarse_bwd_rows(g.KVb);
-  const long long nr = (long long)g.B * g.Hq * ((g.Qb + cr2 - 1) / cr2);
-  const long long nc = (long long)g.B * g.Hkv * ((g.KVb + CC - 1) / CC);
+  const long long nr = (long long)g.B * g.Hq * ((g.Qb + MR - 1) / MR);
+  const long long nc = (long long)g.B * g.Hkv * ((g.KVb + CCOL - 1) / CCOL);
   if (nr == 0 || nc == 0) return hipSuccess;
-  const size_t lds = coarse_bwd_lds(g.KVb);
-  if (cr2 == 8) coarse_bwd_rows_kernel<8><<<(unsigned)nr, 256, lds, st>>>(a);
-  else if (cr2 == 4) coarse_bwd_rows_kernel<4><<<(unsigned)nr, 256, lds, st>>>(a);
-  else if (cr2 == 2) coarse_bwd_rows_kernel<2><<<(unsigned)nr, 256, lds, st>>>(a);
-  else coarse_bwd_rows_kernel<1><<<(unsigned)nr, 256, lds, st>>>(a);
+  coarse_bwd_rows_kernel<<<(unsigned)nr, NWC * 64, ROWS_LDS, st>>>(a);
   coarse_bwd_cols_kernel<<<(unsigned)nc, 256, 0, st>>>(a);
   return hipGetLastError();
 }

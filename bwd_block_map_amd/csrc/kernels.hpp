@@ -95,7 +95,8 @@ struct CoarseArgs {
   // backward
   const float* doc;
   float* ps;      // workspace [B,Hq,Qb,KVb]: P_c
-  float* dss;     // workspace [B,Hq,Qb,KVb]: dS_c
+  float* dss;     // workspace [B,Hq,Qb,KVb]: W = P_c dP_c (dS_c = W - csum P_c)
+  float* csum;    // workspace [B,Hq,Qb]: row sums of W
   float* dqc;
   float* dkc;
   float* dvc;

@@ -195,6 +195,7 @@ struct BwdWs {
   float* dvc;
   float* ps;
   float* dss;
+  float* csum;
   float* dlogit;  // VSA_GATE_PROJECTED: dL/dz per row, laid out like lse
   float* dwp;     // VSA_GATE_PROJECTED: per-Q-block partial sums of dL/dz q
   float* dbp;     // VSA_GATE_PROJECTED: per-Q-block partial sums of dL/dz
@@ -219,6 +220,7 @@ BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
     w.dvc = c.take<float>((long long)p->B * p->Hkv * p->KVb * p->D);
     w.ps = c.take<float>((long long)p->B * p->Hq * p->Qb * p->KVb);
     w.dss = c.take<float>((long long)p->B * p->Hq * p->Qb * p->KVb);
+    w.csum = c.take<float>((long long)p->B * p->Hq * p->Qb);
   }
   if (p->gate_mode == VSA_GATE_PROJECTED) {
     w.dlogit = c.take<float>(std::max(rows_total(p), 1LL));
@@ -895,6 +897,7 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
     ca.doc = w.doc;
     ca.ps = w.ps;
     ca.dss = w.dss;
+    ca.csum = w.csum;
     ca.dqc = w.dqc;
     ca.dkc = w.dkc;
     ca.dvc = w.dvc;

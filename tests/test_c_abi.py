@@ -87,10 +87,10 @@ def test_validate_rejects_bad_problems_with_messages():
     c, _ = _code(_prob(layout="tnd", Sq=30, Skv=40, max_seqlen_q=30, max_seqlen_kv=40,
                        q_block=128, kv_block=128, cu_seqlens_q=fake, cu_seqlens_kv=fake, topk=2))
     assert c == vsa.ERR_UNSUPPORTED
-    # the coarse kernels keep one score row of every KV tile in LDS: 32000 tiles
-    # do not fit even with one Q tile per work-group (31000 do)
-    vsa.vsa_validate(_prob(B=1, Hq=1, Hkv=1, Sq=256, Skv=31000 * 64, kv_block=64, topk=1))
-    c, m = _code(_prob(B=1, Hq=1, Hkv=1, Sq=256, Skv=32000 * 64, kv_block=64, topk=1))
+    # the coarse kernels keep one score row of every KV tile in LDS: 39000 tiles
+    # do not fit even with one Q tile per work-group (38000 do)
+    vsa.vsa_validate(_prob(B=1, Hq=1, Hkv=1, Sq=256, Skv=38000 * 64, kv_block=64, topk=1))
+    c, m = _code(_prob(B=1, Hq=1, Hkv=1, Sq=256, Skv=39000 * 64, kv_block=64, topk=1))
     assert c == vsa.ERR_UNSUPPORTED and "too large for the coarse kernels" in m
 
 
