@@ -254,8 +254,10 @@ def _short_kernel(name):
 
 def summarize_counters(counter_csv, agent_csv, workload, command):
     """Per-kernel MFMA use from one rocprofv3 --pmc pass (PMC_COUNTERS) over a
-    bench step: executed MFMA work (every MFMA here is a 32x32x16 one, 32768
-    flop), the share of cycles the MFMA pipes were busy, the sustained clock,
+    bench step: executed MFMA work (the attention kernels issue 32x32x16 bf16 or
+    fp16 MFMAs, 32768 flop each, against the 2.5 PF dense peak; the coarse
+    kernels 16x16x4 fp32 ones, 2048 flop, against 157.3 TF), the share of
+    cycles the MFMA pipes were busy, the sustained clock,
     instruction mix per MFMA and, for the sparse stages, HBM GB/s from the
     traffic file. Durations are the counter run's own dispatch timestamps."""
     import csv
@@ -291,11 +293,13 @@ def summarize_counters(counter_csv, agent_csv, workload, command):
              "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs): the share of",
              "# cycles the MFMA pipes worked; clock = GRBM_GUI_ACTIVE / XCDs / duration (the",
              "# sustained engine clock during the kernel); executed TFLOP/s counts every issued",
-             "# MFMA (padding included), % of 2.5 PF against the dense bf16 peak at 2.4 GHz.",
+             "# MFMA (padding included); % peak against the dense peak of the kernel's MFMA",
+             "# type at 2.4 GHz: 2.5 PF for the bf16/fp16 attention kernels, 157.3 TF for the",
+             "# fp32 coarse kernels.",
              "# HBM GB/s: FETCH_SIZE + WRITE_SIZE bytes per launch (traffic file, copy-calibrated)",
              "# / duration.",
              "",
-             f"{'kernel':44s} {'calls':>5s} {'ms':>8s} {'GHz':>5s} {'exec TF/s':>9s} {'%2.5PF':>6s} "
+             f"{'kernel':44s} {'calls':>5s} {'ms':>8s} {'GHz':>5s} {'exec TF/s':>9s} {'%peak':>6s} "
              f"{'MFMA busy':>9s} {'VALU/MFMA':>9s} {'LDS/MFMA':>8s} {'SALU/MFMA':>9s} {'HBM GB/s':>8s}"]
     for n, a in sorted(agg.items(), key=lambda kv: -kv[1]["s"]):
         c, k = a["c"], a["n"]
@@ -303,11 +307,13 @@ def summarize_counters(counter_csv, agent_csv, workload, command):
         mf = c.get("SQ_INSTS_MFMA", 0.0) / k
         grbm = c.get("GRBM_GUI_ACTIVE", 0.0) / k
         ghz = grbm / n_xcc / sec * 1e-9 if sec > 0 else 0.0
-        tf = mf * 32768 / sec * 1e-12 if sec > 0 else 0.0
+        fp32 = n.startswith("coarse")  # v_mfma_f32_16x16x4_f32
+        peak = 157.3 if fp32 else 2500.0
+        tf = mf * (2048 if fp32 else 32768) / sec * 1e-12 if sec > 0 else 0.0
         busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / k / (grbm / n_xcc * n_simd) if grbm else 0.0
         ratio = (lambda x: f"{c.get(x, 0.0) / k / mf:9.2f}" if mf else f"{'-':>9s}")
         gbs = f"{traffic[n]['bytes'] / sec * 1e-9:8.0f}" if n in traffic and sec > 0 else "-"
-        lines.append(f"{n[:44]:44s} {k:5d} {sec * 1e3:8.2f} {ghz:5.2f} {tf:9.1f} {100 * tf / 2500:6.1f} "
+        lines.append(f"{n[:44]:44s} {k:5d} {sec * 1e3:8.2f} {ghz:5.2f} {tf:9.1f} {100 * tf / peak:6.1f} "
                      f"{100 * busy:8.1f}% {ratio('SQ_INSTS_VALU')} {ratio('SQ_INSTS_LDS')[1:]} "
                      f"{ratio('SQ_INSTS_SALU')} {gbs:>8s}")
     path = COUNTERS_FILE.format(workload=workload)

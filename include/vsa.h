@@ -200,7 +200,8 @@ int vsa_abi_version(void);
  * Limits of this build (VSA_ERR_UNSUPPORTED): D <= 128; q_block 8, 16 or a
  * multiple of 32, kv_block a multiple of 64; fewer than 65536 heads in BSHD and
  * TND (row offsets of the tile loads are 24-bit); B*Hq*Qb*KVb and B*Hq*Sq below
- * 2^31; KVb small enough for the coarse kernels' LDS when top-k or a gate is on. */
+ * 2^31; with top-k or a gate, KVb <= 38848 (one row of coarse scores per KV tile
+ * in the coarse forward's LDS). */
 int vsa_validate(const vsa_problem* p);
 
 /*
