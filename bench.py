@@ -534,6 +534,14 @@ def main():
     fwd_ms, bwd_ms = float(np.median(fwd_all)), float(np.median(bwd_all))
     step_ms = wall * 1e3 / args.steps
     log(f"[bench] timed {args.steps} steps: fwd {fwd_ms:.2f} ms, bwd {bwd_ms:.2f} ms")
+    # the same steps once more, without the per-kernel and per-call events (an
+    # untimed extra: on the small workloads the events add visible latency)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    plain_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     per_kernel = {k: {"ms_per_launch": (ms / n if n else 0.0), "launches_per_step": n / args.steps}
                   for k, (ms, n) in prof.items()}
@@ -573,6 +581,7 @@ def main():
                    "dkdv_grid": {"auto": "library's choice (persistent at >= 8 spans per CU)",
                                  "persistent": "persistent, longest first",
                                  "per-item": "one work-group per span"}[args.grid]},
+        "ms_per_step_without_events": round(plain_ms, 3),
         "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
         "fwd_ms_min": round(float(min(fwd_all)), 3), "bwd_ms_min": round(float(min(bwd_all)), 3),
         "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2),

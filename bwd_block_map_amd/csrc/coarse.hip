@@ -23,13 +23,23 @@ namespace vsa {
 
 namespace {
 
+// One launch pools q, k and v: tiles [0, nq) are the Q tiles, the next nk the
+// K tiles and the last nk the V tiles (tile wg0 + blockIdx.x).
 template <class ET>
-__global__ __launch_bounds__(256) void pool_kernel(const Geom g, const uint16_t* __restrict__ x,
-                                                   int is_q, float* __restrict__ out) {
+__global__ __launch_bounds__(256) void pool_kernel(const Geom g, const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v, float* __restrict__ qc,
+                                                   float* __restrict__ kc, float* __restrict__ vc,
+                                                   long long wg0) {
   using E = Elem<ET>;
   __shared__ float red[16][HD];
+  const long long nq = (long long)g.B * g.Hq * g.Qb, nk = (long long)g.B * g.Hkv * g.KVb;
+  const long long t = wg0 + blockIdx.x;
+  const bool is_q = t < nq;
+  const uint16_t* x = is_q ? q : t < nq + nk ? k : v;
+  float* out = is_q ? qc : t < nq + nk ? kc : vc;
+  int id = (int)(is_q ? t : (t - nq) % nk);
   const int heads = is_q ? g.Hq : g.Hkv, nb = is_q ? g.Qb : g.KVb;
-  int id = blockIdx.x;
   const int blk = id % nb;
   id /= nb;
   const int h = id % heads, b = id / heads;
@@ -42,8 +52,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const Geom g, const uint16_t*
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = 0.f;
   for (int r = slot; r < n; r += 16) {
-    const uint4 v = ldg16(x + base + (long long)r * rs + 8 * dg);
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
+    const uint4 xv = ldg16(x + base + (long long)r * rs + 8 * dg);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&xv);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       acc[2 * u] += E::lo(w[u]);
@@ -588,15 +598,14 @@ int coarse_rows_per_block(int KVb) {
 
 hipError_t launch_pool(const Geom& g, int dtype, const void* q, const void* k, const void* v,
                        float* qc, float* kc, float* vc, hipStream_t st) {
-  const unsigned nq = (unsigned)((long long)g.B * g.Hq * g.Qb);
-  const unsigned nk = (unsigned)((long long)g.B * g.Hkv * g.KVb);
+  const long long nq = (long long)g.B * g.Hq * g.Qb, nk = (long long)g.B * g.Hkv * g.KVb;
+  const long long n = nq + 2 * nk;
+  constexpr long long CHUNK = 1LL << 30;  // work-groups per launch
   auto go = [&](auto tag) {
     using ET = decltype(tag);
-    if (nq) pool_kernel<ET><<<nq, 256, 0, st>>>(g, (const uint16_t*)q, 1, qc);
-    if (nk) {
-      pool_kernel<ET><<<nk, 256, 0, st>>>(g, (const uint16_t*)k, 0, kc);
-      pool_kernel<ET><<<nk, 256, 0, st>>>(g, (const uint16_t*)v, 0, vc);
-    }
+    for (long long b0 = 0; b0 < n; b0 += CHUNK)
+      pool_kernel<ET><<<(unsigned)std::min(CHUNK, n - b0), 256, 0, st>>>(
+          g, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, qc, kc, vc, b0);
   };
   if (dtype == VSA_BF16) go(bf16_tag{});
   else go(f16_tag{});

@@ -126,13 +126,20 @@ __global__ __launch_bounds__(1024) void index_scan(int32_t* __restrict__ row_ptr
 // Small maps in one launch (the three launches above cost more than the work
 // for, e.g., a [2, 8, 32, 32] map): one work-group stages the map in LDS with
 // coalesced loads, counts every row there (a thread per row), scans the counts,
-// writes row_ptr and fills col. Same CSR as the three-kernel path.
+// writes row_ptr and fills col. Same CSR as the three-kernel path. Launched
+// with two work-groups it builds both directions at once: work-group 1 the
+// KV-owned index into (row_ptr1, col1).
 constexpr int SMALL_ROWS = 8192;       // rows whose counts fit in LDS
 constexpr int SMALL_MAP = 64 * 1024;   // map bytes staged in LDS
 
 __global__ __launch_bounds__(1024) void index_small(Geom g, const uint8_t* __restrict__ map,
-                                                    int kv_owned, int32_t* __restrict__ row_ptr,
-                                                    int32_t* __restrict__ col, long long cap) {
+                                                    int kv_owned0, int32_t* __restrict__ row_ptr0,
+                                                    int32_t* __restrict__ col0,
+                                                    int32_t* __restrict__ row_ptr1,
+                                                    int32_t* __restrict__ col1, long long cap) {
+  const int kv_owned = blockIdx.x ? 1 : kv_owned0;
+  int32_t* __restrict__ row_ptr = blockIdx.x ? row_ptr1 : row_ptr0;
+  int32_t* __restrict__ col = blockIdx.x ? col1 : col0;
   __shared__ uint8_t mp[SMALL_MAP];
   __shared__ int32_t start[SMALL_ROWS];
   __shared__ int32_t part[1024];
@@ -211,7 +218,7 @@ hipError_t launch_index(const Geom& g, const uint8_t* map, int kv_owned, int32_t
   }
   const long long staged = (g.map_bstride ? g.B : 1LL) * g.Hq * g.Qb * g.KVb;
   if (rows <= SMALL_ROWS && staged <= SMALL_MAP) {
-    index_small<<<1, 1024, 0, st>>>(g, map, kv_owned, row_ptr, col, cap);
+    index_small<<<1, 1024, 0, st>>>(g, map, kv_owned, row_ptr, col, nullptr, nullptr, cap);
   } else if (!kv_owned) {
     const unsigned grid = (unsigned)((rows + 3) / 4);
     index_count_q<<<grid, 256, 0, st>>>(g, map, row_ptr);
@@ -224,6 +231,18 @@ hipError_t launch_index(const Geom& g, const uint8_t* map, int kv_owned, int32_t
     index_fill_kv<<<grid, 256, 0, st>>>(g, map, row_ptr, col, cap);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_index_both(const Geom& g, const uint8_t* map, int32_t* q_rp, int32_t* q_col,
+                             int32_t* kv_rp, int32_t* kv_col, long long cap, hipStream_t st) {
+  const long long rq = (long long)g.B * g.Hq * g.Qb, rk = (long long)g.B * g.Hq * g.KVb;
+  const long long staged = (g.map_bstride ? g.B : 1LL) * g.Hq * g.Qb * g.KVb;
+  if (rq > 0 && rk > 0 && rq <= SMALL_ROWS && rk <= SMALL_ROWS && staged <= SMALL_MAP) {
+    index_small<<<2, 1024, 0, st>>>(g, map, 0, q_rp, q_col, kv_rp, kv_col, cap);
+    return hipGetLastError();
+  }
+  const hipError_t e = launch_index(g, map, 0, q_rp, q_col, cap, st);
+  return e != hipSuccess ? e : launch_index(g, map, 1, kv_rp, kv_col, cap, st);
 }
 
 }  // namespace vsa

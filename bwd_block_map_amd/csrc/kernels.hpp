@@ -104,6 +104,9 @@ struct CoarseArgs {
 
 hipError_t launch_index(const Geom& g, const uint8_t* map, int kv_owned, int32_t* row_ptr,
                         int32_t* col, long long cap, hipStream_t st);
+// both directions (Q-owned, then KV-owned); one launch for small maps
+hipError_t launch_index_both(const Geom& g, const uint8_t* map, int32_t* q_rp, int32_t* q_col,
+                             int32_t* kv_rp, int32_t* kv_col, long long cap, hipStream_t st);
 hipError_t launch_pool(const Geom& g, int dtype, const void* q, const void* k, const void* v,
                        float* qc, float* kc, float* vc, hipStream_t st);
 hipError_t launch_coarse_fwd(const CoarseArgs& a, bool want_topk, bool want_gate, hipStream_t st);

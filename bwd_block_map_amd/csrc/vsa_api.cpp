@@ -598,14 +598,10 @@ int fwd_impl(const vsa_problem* p, const void* q, const void* k, const void* v, 
   int32_t* q_col = saved ? s.q_col : w.q_col;
   {
     Prof pr(ws_scratch ? -1 : VSA_KERNEL_INDEX, st);
-    e = vsa::launch_index(g, sel_map, 0, q_rp, q_col, cap, st);
+    e = saved ? vsa::launch_index_both(g, sel_map, q_rp, q_col, s.kv_rp, s.kv_col, cap, st)
+              : vsa::launch_index(g, sel_map, 0, q_rp, q_col, cap, st);
   }
-  if (e != hipSuccess) return hip_fail(e, "index (Q-owned)");
-  if (saved) {
-    Prof pr(ws_scratch ? -1 : VSA_KERNEL_INDEX, st);
-    e = vsa::launch_index(g, sel_map, 1, s.kv_rp, s.kv_col, cap, st);
-    if (e != hipSuccess) return hip_fail(e, "index (KV-owned)");
-  }
+  if (e != hipSuccess) return hip_fail(e, "index");
   vsa::FwdArgs fa{};
   fa.g = g;
   fa.q = (const uint16_t*)q;
