@@ -92,8 +92,8 @@ constexpr int MR = 16;        // rows of one MFMA block
 constexpr int HD16 = HD / 16;
 
 // Dot products of pooled rows: lane (r = l % 16, kk = l / 16) holds d = 16 m +
-// 4 kk + {0..3} (m < HD / 16) of one row; the d order inside the sum is the
-// MFMA's (any split of d between the steps gives the same dot product).
+// 4 kk + {0..3} (m < HD / 16) of one row. Any assignment of the d to the MFMA
+// steps sums the same products; only the rounding order depends on it.
 __device__ __forceinline__ void load_row(float4 (&x)[HD16], const float* row, int kk) {
 #pragma unroll
   for (int m = 0; m < HD16; ++m) x[m] = *reinterpret_cast<const float4*>(row + 16 * m + 4 * kk);
@@ -128,7 +128,7 @@ __host__ __device__ __forceinline__ long long row_area(int cr, int KVb) {
 }
 
 // Out[r][d] = sum_j W[r][j] M[j][d] for the rows r < nr of a 16-row block, W in
-// LDS (stride ld), M pooled rows of HD floats. Wave w: d half (w & 1) and every
+// LDS (stride ld), M pooled rows of HD floats (the coarse forward's O_c). Wave w: d half (w & 1) and every
 // fourth group of four j (w >> 1); lane (r, kk) feeds W[r][j] as A and M[j][64
 // half + 4 r + c] as B of the MFMA whose accumulator c holds d = 64 half + 4 n +
 // c. The four partial sums meet in `red` (aliasing W: callers sync first), and
