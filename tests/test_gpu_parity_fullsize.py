@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from tests.gpu_run import run_case  # noqa: E402
+from tests.gpu_run import device_inputs, run_case  # noqa: E402
 from tests.test_gpu_parity import _topk_agreement  # noqa: E402
 
 
@@ -152,3 +152,19 @@ def test_c5_720p_gate_full_size():
 def test_c5_720p_gate_full_size_atomic_dq():
     """The same checks on the backward that adds dQ inside the dK/dV walk."""
     _fullsize("c5_vsa256_720p_gate", heads=[3, 21, 38], nrows=384, atomic_dq=True)
+
+
+def test_c5_720p_gate_is_bit_reproducible():
+    """Two runs of the whole 720p workload (forward and backward, the launch
+    configuration bench.py times, persistent dK/dV grid included) give the same
+    map, out, lse and gradients bit for bit: the backward has no atomics and
+    every reduction runs in a fixed order."""
+    case = make_case("c5_vsa256_720p_gate", device="cuda")
+    d = device_inputs(case)
+    a = run_case(case, d=d, keep_device=True)
+    a = {k: v.clone() for k, v in a.items() if v is not None}
+    b = run_case(case, d=d, keep_device=True)
+    for k, v in a.items():
+        same = torch.equal(v, b[k])
+        _say(f"  {k:6s} bit-identical: {same}")
+        assert same, f"{k} differs between two runs"
