@@ -58,39 +58,58 @@ __global__ __launch_bounds__(256) void index_fill_q(Geom g, const uint8_t* __res
   }
 }
 
-// KV-owned count / fill: one thread per column (b, h, j), walking i; lanes of a
-// wave read consecutive bytes of one map row per step.
-__global__ __launch_bounds__(256) void index_count_kv(Geom g, const uint8_t* __restrict__ map,
-                                                      int32_t* __restrict__ row_ptr) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long rows = (long long)g.B * g.Hq * g.KVb;
-  if (t >= rows) return;
+// KV-owned count / fill: a work-group takes 64 columns (b, h, j) and its four
+// waves split each column's rows i into four segments; lanes of a wave read
+// 64 consecutive map bytes of one row per step. The fill places a segment
+// after the live entries of the segments above it, so the columns stay in
+// ascending row order.
+constexpr int KV_SEG = 4;
+__device__ __forceinline__ int kv_seg_count(const Geom& g, const uint8_t* __restrict__ map, long long t,
+                                            int seg, int* nq_out, const uint8_t** m_out, int* i0,
+                                            int* i1) {
   const int j = (int)(t % g.KVb);
   const long long bh = t / g.KVb;
   const int h = (int)(bh % g.Hq), b = (int)(bh / g.Hq);
+  const bool col_ok = j < g.nkb(b) && g.kv_val(b, j) > 0;
+  const int nq = col_ok ? g.nqb(b) : 0;
+  const int per = (nq + KV_SEG - 1) / KV_SEG;
+  *i0 = min(seg * per, nq);
+  *i1 = min(*i0 + per, nq);
+  *m_out = map + b * g.map_bstride + (long long)h * g.Qb * g.KVb + j;
+  *nq_out = nq;
   int cnt = 0;
-  if (j < g.nkb(b) && g.kv_val(b, j) > 0) {
-    const uint8_t* m = map + b * g.map_bstride + (long long)h * g.Qb * g.KVb + j;
-    const int nq = g.nqb(b);
-    for (int i = 0; i < nq; ++i) cnt += m[(long long)i * g.KVb] != 0;
-  }
-  row_ptr[t + 1] = cnt;
+  for (int i = *i0; i < *i1; ++i) cnt += (*m_out)[(long long)i * g.KVb] != 0;
+  return cnt;
+}
+
+__global__ __launch_bounds__(256) void index_count_kv(Geom g, const uint8_t* __restrict__ map,
+                                                      int32_t* __restrict__ row_ptr) {
+  __shared__ int part[KV_SEG][64];
+  const int lane = threadIdx.x & 63, seg = threadIdx.x >> 6;
+  const long long t = (long long)blockIdx.x * 64 + lane;
+  const long long rows = (long long)g.B * g.Hq * g.KVb;
+  int nq = 0, i0 = 0, i1 = 0;
+  const uint8_t* m = nullptr;
+  part[seg][lane] = t < rows ? kv_seg_count(g, map, t, seg, &nq, &m, &i0, &i1) : 0;
+  __syncthreads();
+  if (seg == 0 && t < rows) row_ptr[t + 1] = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
 }
 
 __global__ __launch_bounds__(256) void index_fill_kv(Geom g, const uint8_t* __restrict__ map,
                                                      const int32_t* __restrict__ row_ptr,
                                                      int32_t* __restrict__ col, long long cap) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  __shared__ int part[KV_SEG][64];
+  const int lane = threadIdx.x & 63, seg = threadIdx.x >> 6;
+  const long long t = (long long)blockIdx.x * 64 + lane;
   const long long rows = (long long)g.B * g.Hq * g.KVb;
+  int nq = 0, i0 = 0, i1 = 0;
+  const uint8_t* m = nullptr;
+  part[seg][lane] = t < rows ? kv_seg_count(g, map, t, seg, &nq, &m, &i0, &i1) : 0;
+  __syncthreads();
   if (t >= rows) return;
-  const int j = (int)(t % g.KVb);
-  const long long bh = t / g.KVb;
-  const int h = (int)(bh % g.Hq), b = (int)(bh / g.Hq);
-  if (j >= g.nkb(b) || g.kv_val(b, j) == 0) return;
-  const uint8_t* m = map + b * g.map_bstride + (long long)h * g.Qb * g.KVb + j;
-  const int nq = g.nqb(b);
   long long pos = row_ptr[t];
-  for (int i = 0; i < nq; ++i)
+  for (int s2 = 0; s2 < seg; ++s2) pos += part[s2][lane];
+  for (int i = i0; i < i1; ++i)
     if (m[(long long)i * g.KVb] != 0) {
       if (pos < cap) col[pos] = i;
       ++pos;
@@ -225,7 +244,7 @@ hipError_t launch_index(const Geom& g, const uint8_t* map, int kv_owned, int32_t
     index_scan<<<1, 1024, 0, st>>>(row_ptr, rows);
     index_fill_q<<<grid, 256, 0, st>>>(g, map, row_ptr, col, cap);
   } else {
-    const unsigned grid = (unsigned)((rows + 255) / 256);
+    const unsigned grid = (unsigned)((rows + 63) / 64);
     index_count_kv<<<grid, 256, 0, st>>>(g, map, row_ptr);
     index_scan<<<1, 1024, 0, st>>>(row_ptr, rows);
     index_fill_kv<<<grid, 256, 0, st>>>(g, map, row_ptr, col, cap);
