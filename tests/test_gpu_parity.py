@@ -575,15 +575,16 @@ def test_head_dimensions_below_128(case):
 def test_many_kv_tiles_at_the_coarse_kernels_limits():
     """Pooled top-k over very many KV tiles, where the coarse forward holds only
     a few score rows per work-group: the gated path with 1001 (a tile count
-    that is not a multiple of 4 or 16), 2640, 8000 and 12000 KV tiles (16, 8,
-    4 and 2 rows per work-group) and top-k alone at 20000 tiles (1.28 M keys,
-    one row), against the oracle (selection exact, outputs and gradients
+    that is not a multiple of 4 or 16), 2640, 8000, 12000 and 36000 KV tiles
+    (16, 8, 4, 2 and 1 rows per work-group; the compression backward's LDS
+    does not grow with the tile count) and top-k alone at 20000 tiles (1.28 M
+    keys, one row), against the oracle (selection exact, outputs and gradients
     within the bars)."""
     cases = [
         build_case(f"many_kv_gated_{n}", dtype="bf16", layout="bshd", B=1, Hq=2, Hkv=1, D=128,
                    q_block=256, kv_block=64, Sq=512, Skv=64 * n, topk=6, map_kind="none",
                    gate_mode="per_token", seed=95 + n)
-        for n in (1001, 2640, 8000, 12000)
+        for n in (1001, 2640, 8000, 12000, 36000)
     ] + [
         build_case("many_kv_topk", dtype="bf16", layout="bhsd", B=1, Hq=1, Hkv=1, D=128,
                    q_block=256, kv_block=64, Sq=256, Skv=64 * 20000, topk=8, map_kind="none",
