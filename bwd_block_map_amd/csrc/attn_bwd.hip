@@ -229,7 +229,6 @@ __global__ __launch_bounds__(HD) void gate_proj_grad_kernel(const Geom g, const 
 // flight while one is computed; the KV-owned list of the current head sits in
 // LDS a page at a time.
 constexpr int DKDV_NW = 8;
-constexpr int DKDV_SPAN = 256;
 constexpr int DKDV_LIST_CAP = 1024;
 
 // AQ: the variant that also adds each chunk's dQ = dS K into a float
@@ -711,14 +710,14 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int t
 template <class ET, bool AQ>
 __device__ __forceinline__ void dkdv_item(const BwdArgs& a, uint8_t* smem, int tid, int id) {
   const Geom& g = a.g;
-  const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
+  const int nspan = (g.kv_block + a.span - 1) / a.span;
   const int span = id % nspan;
   id /= nspan;
   const int j = id % g.KVb;
   id /= g.KVb;
   const int hk = id % g.Hkv, b = id / g.Hkv;
-  const int k0 = span * DKDV_SPAN;
-  const int kend = min(g.kv_exist(b, j), min(g.kv_block, k0 + DKDV_SPAN));  // existing keys < kend
+  const int k0 = span * a.span;
+  const int kend = min(g.kv_exist(b, j), min(g.kv_block, k0 + a.span));  // existing keys < kend
   if (k0 >= kend) return;
   const int nval = g.kv_val(b, j);
   const int live = max(0, min(kend, nval) - k0);  // live keys of the span
@@ -741,7 +740,7 @@ template <class ET, bool AQ, bool PERSIST>
 __global__ __launch_bounds__(DKDV_NW * 64, 2) void sparse_dkdv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[AQ ? DKDV_LDS_AQ : DKDV_LDS];
   if constexpr (!PERSIST) {
-    const int nspan = (a.g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
+    const int nspan = (a.g.kv_block + a.span - 1) / a.span;
     dkdv_item<ET, AQ>(a, smem, threadIdx.x, xcd_group(blockIdx.x, gridDim.x, nspan));
   } else {
     __shared__ int next_item;
@@ -774,14 +773,14 @@ constexpr int LPT_LEVELS = 1024;
 template <int LEVELS = LPT_LEVELS>
 __device__ __forceinline__ int lpt_bin(const BwdArgs& a, int id) {
   const Geom& g = a.g;
-  const int nspan = (g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN;
+  const int nspan = (g.kv_block + a.span - 1) / a.span;
   const int span = id % nspan;
   int r = id / nspan;
   const int j = r % g.KVb;
   r /= g.KVb;
   const int hk = r % g.Hkv, b = r / g.Hkv;
-  const int k0 = span * DKDV_SPAN;
-  const int kend = min(g.kv_exist(b, j), min(g.kv_block, k0 + DKDV_SPAN));
+  const int k0 = span * a.span;
+  const int kend = min(g.kv_exist(b, j), min(g.kv_block, k0 + a.span));
   const int live = max(0, min(kend, g.kv_val(b, j)) - k0);
   long long cnt = 0;
   for (int hh = 0; hh < g.group; ++hh) {
@@ -1039,7 +1038,7 @@ hipError_t launch_pre_t(const PreArgs& a, hipStream_t st) {
 template <class ET>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
-  const long long n = dkdv_items(g);
+  const long long n = dkdv_items(g, a.span);
   if (n == 0) return hipSuccess;
   if (a.lpt_order) {
     const unsigned grid = (unsigned)(n < a.persist_grid ? n : a.persist_grid);
@@ -1085,19 +1084,19 @@ hipError_t launch_sparse_dkdv(const BwdArgs& a, int dtype, hipStream_t st) {
 hipError_t launch_sparse_dq(const BwdArgs& a, int dtype, hipStream_t st) {
   return dtype == VSA_BF16 ? launch_dq_t<bf16_tag>(a, st) : launch_dq_t<f16_tag>(a, st);
 }
-long long dkdv_items(const Geom& g) {
-  return (long long)g.B * g.Hkv * g.KVb * ((g.kv_block + DKDV_SPAN - 1) / DKDV_SPAN);
+long long dkdv_items(const Geom& g, int span) {
+  return (long long)g.B * g.Hkv * g.KVb * ((g.kv_block + span - 1) / span);
 }
 long long lpt_hist_entries(const Geom& g) { return (long long)g.B * g.Hkv * LPT_LEVELS + 2; }
 
-bool lpt_order_small(const Geom& g) {
-  return (long long)g.B * g.Hkv * LPT_SMALL_LEVELS <= LPT_SMALL_BINS && dkdv_items(g) <= 16384;
+bool lpt_order_small(const Geom& g, int span) {
+  return (long long)g.B * g.Hkv * LPT_SMALL_LEVELS <= LPT_SMALL_BINS && dkdv_items(g, span) <= 16384;
 }
 
 hipError_t launch_lpt_order(const BwdArgs& a, int32_t* hist, int32_t* order, hipStream_t st) {
   const long long n = a.n_items, nb = (long long)a.g.B * a.g.Hkv * LPT_LEVELS;
   if (n == 0) return hipSuccess;
-  if (lpt_order_small(a.g)) {  // hist need not be zero: only the counter is used
+  if (lpt_order_small(a.g, a.span)) {  // hist need not be zero: only the counter is used
     lpt_small_kernel<<<1, 1024, 0, st>>>(a, order, a.lpt_counter);
     return hipGetLastError();
   }

@@ -57,6 +57,9 @@ struct BwdArgs {
   int32_t* lpt_counter;
   int n_items;
   int persist_grid;
+  // keys per dK/dV work item: DKDV_SPAN, or DKDV_SPAN_MIN when the items of
+  // that size still fit on the compute units at once
+  int span;
 };
 
 // Row term and gate-side reductions of the backward.
@@ -116,12 +119,14 @@ hipError_t launch_bwd_pre(const PreArgs& a, int dtype, hipStream_t st);
 hipError_t launch_sparse_dkdv(const BwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_sparse_dq(const BwdArgs& a, int dtype, hipStream_t st);
 hipError_t launch_dq_cast(const BwdArgs& a, int dtype, hipStream_t st);
-long long dkdv_items(const Geom& g);        // dK/dV spans of a problem
+constexpr int DKDV_SPAN = 256;     // keys per dK/dV work item
+constexpr int DKDV_SPAN_MIN = 64;  // ... on problems whose 64-key items fit on the CUs at once
+long long dkdv_items(const Geom& g, int span);  // dK/dV spans of a problem
 long long lpt_hist_entries(const Geom& g);  // int32 entries of the order's histogram
 // longest-first order of the dK/dV spans into `order` (a.n_items entries);
 // `hist` (lpt_hist_entries) must be zero unless lpt_order_small(g), whose one
 // launch also clears a.lpt_counter
-bool lpt_order_small(const Geom& g);
+bool lpt_order_small(const Geom& g, int span);
 hipError_t launch_lpt_order(const BwdArgs& a, int32_t* hist, int32_t* order, hipStream_t st);
 hipError_t launch_exclusive_scan(int32_t* a, long long n, hipStream_t st);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);

@@ -211,7 +211,7 @@ BwdWs carve_bwd(const vsa_problem* p, void* base, size_t* bytes) {
   if (!(p->flags & VSA_FLAG_NO_PERSISTENT)) {  // the persistent grid may be used
     const vsa::Geom g = make_geom(p);
     w.lpt_hist = c.take<int32_t>(vsa::lpt_hist_entries(g));
-    w.lpt_order = c.take<int32_t>(std::max(vsa::dkdv_items(g), 1LL));
+    w.lpt_order = c.take<int32_t>(std::max(vsa::dkdv_items(g, vsa::DKDV_SPAN_MIN), 1LL));
   }
   if (p->gate_mode != VSA_GATE_NONE) {
     w.doc = c.take<float>((long long)p->B * p->Hq * p->Qb * p->D);
@@ -925,21 +925,25 @@ int vsa_bwd(const vsa_problem* p, const void* q, const void* k, const void* v, c
   ba.col = s.kv_col;
   const bool atomic_dq = (p->flags & VSA_FLAG_ATOMIC_DQ) != 0;
   ba.dqacc = atomic_dq ? w.dqacc : nullptr;
-  bool persistent = false;
   int cus = 0;
-  if (!(p->flags & VSA_FLAG_NO_PERSISTENT)) {
-    rc = compute_units((hipStream_t)stream, &cus);
-    if (rc != VSA_OK) return rc;
-    persistent = (p->flags & VSA_FLAG_PERSISTENT) ||
-                 vsa::dkdv_items(g) >= (long long)VSA_PERSISTENT_MIN_SPANS_PER_CU * cus;
-  }
+  rc = compute_units((hipStream_t)stream, &cus);
+  if (rc != VSA_OK) return rc;
+  // work items of 256 keys; of 64 when even those fit on the compute units at
+  // once (one work-group per CU): a small problem's dK/dV time is then the
+  // length of one item's walk, which is shorter for fewer keys
+  ba.span = (g.kv_block > vsa::DKDV_SPAN_MIN && vsa::dkdv_items(g, vsa::DKDV_SPAN_MIN) <= cus)
+                ? vsa::DKDV_SPAN_MIN : vsa::DKDV_SPAN;
+  const bool persistent =
+      !(p->flags & VSA_FLAG_NO_PERSISTENT) &&
+      ((p->flags & VSA_FLAG_PERSISTENT) ||
+       vsa::dkdv_items(g, ba.span) >= (long long)VSA_PERSISTENT_MIN_SPANS_PER_CU * cus);
   if (persistent) {  // longest-first list of the dK/dV spans
-    ba.n_items = (int)vsa::dkdv_items(g);
+    ba.n_items = (int)vsa::dkdv_items(g, ba.span);
     ba.persist_grid = cus;
     const long long nh = vsa::lpt_hist_entries(g);
     Prof pr(VSA_KERNEL_DKDV_ORDER, st);
     ba.lpt_counter = w.lpt_hist + (nh - 1);
-    if (!vsa::lpt_order_small(g))  // the one-launch order clears the counter itself
+    if (!vsa::lpt_order_small(g, ba.span))  // the one-launch order clears the counter itself
       e = vsa::launch_zero(w.lpt_hist, (size_t)nh * sizeof(int32_t), st);
     if (e == hipSuccess) e = vsa::launch_lpt_order(ba, w.lpt_hist, w.lpt_order, st);
     if (e != hipSuccess) return hip_fail(e, "dK/dV order");
