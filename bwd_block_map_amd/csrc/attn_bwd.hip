@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
   const int tid = threadIdx.x, slot = tid >> 4, dg = tid & 15;
   const long long qrs = g.q_rs(), qb = g.q_base(b, h);
   const bool gated = a.gate_mode != VSA_GATE_NONE;
-  // live extent: 1 + the last row whose q or dO has a non-zero element
+  // live extent: 1 + the last row whose dO has a non-zero element (a row with
+  // dO = 0 has dP = 0 and Dr = 0, so dS = 0 whatever its query)
   __shared__ int live_end;
   if (tid == 0) live_end = 0;
   __syncthreads();
@@ -79,10 +80,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
     const long long off = qb + (long long)(blk0 + s) * qrs + 8 * dg;
     const uint4 dv = ldg16(a.dout + off);
     const uint4 ov = ldg16(a.osel + off);
-    const uint4 qv = ldg16(a.q + off);
-    // the row is live when one of its 16 lanes sees a non-zero element (either
-    // sign of zero counts as zero); the wave holds rows 4w .. 4w+3
-    const uint32_t nz = (dv.x | dv.y | dv.z | dv.w | qv.x | qv.y | qv.z | qv.w) & 0x7fff7fffu;
+    const uint4 qv = proj ? ldg16(a.q + off) : make_uint4(0, 0, 0, 0);  // for the gate only
+    // the row is live when one of its 16 lanes sees a non-zero element of dO
+    // (either sign of zero counts as zero); the wave holds rows 4w .. 4w+3
+    const uint32_t nz = (dv.x | dv.y | dv.z | dv.w) & 0x7fff7fffu;
     if ((__ballot(nz != 0) >> (16 * (slot & 3))) & 0xffffull) lend = s + 1;
     const uint32_t* dw = reinterpret_cast<const uint32_t*>(&dv);
     const uint32_t* ow = reinterpret_cast<const uint32_t*>(&ov);
@@ -390,10 +391,10 @@ __device__ __forceinline__ void dkdv_span(const BwdArgs& a, uint8_t* smem, int t
     int se = 0, left = 0;
     long long cq = 0, cl = 0;
     bool more = true;
-    // Rows past a block's live extent have q = 0 and dO = 0 (the padded slots
-    // of partial video tiles, where callers pass a zero gradient): their dS is
-    // 0 and they add exactly nothing to dK and dV, so the walk stops there and
-    // passes over blocks without a live row.
+    // Rows past a block's live extent have dO = 0 (the padded slots of partial
+    // video tiles, where callers pass a zero gradient): their dP and Dr are 0,
+    // so dS = 0 and they add exactly nothing to dK and dV; the walk stops there
+    // and passes over blocks without a live row.
     auto settle = [&]() {  // from entry se of head hh, find the next entry with live rows
       for (;;) {
         while (se >= cnt) {
@@ -940,8 +941,8 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
   const int e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[rid]);  // uniform: the walk stays scalar
   const int cnt = __builtin_amdgcn_readfirstlane(a.row_ptr[rid + 1]) - e0;
 
-  // Rows past the block's live extent have q = 0 and dO = 0 (the padded slots
-  // of partial video tiles, where callers pass a zero gradient), so dS = 0: a
+  // Rows past the block's live extent have dO = 0 (the padded slots of
+  // partial video tiles, where callers pass a zero gradient), so dS = 0: a
   // wave made only of them skips the walk's arithmetic (its dq rows are the
   // compression term or zero), and a work-group made only of them skips the walk.
   const int qlive = a.qlive[rid];

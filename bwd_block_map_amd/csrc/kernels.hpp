@@ -32,8 +32,8 @@ struct BwdArgs {
   const uint16_t* dout;
   const float* lse2;       // lse * log2(e), +inf for rows without a live key
   const float* dr;         // rowsum(dO * O_sel), laid out like lse
-  // per Q block [B,Hq,Qb]: 1 + its last row whose q or dO is not zero (the
-  // rows after it add nothing to dK / dV and have dS = 0)
+  // per Q block [B,Hq,Qb]: 1 + its last row whose dO is not zero (the rows
+  // after it add nothing to dK / dV and have dS = 0)
   const int32_t* qlive;
   const int32_t* row_ptr;  // Q-owned (dQ) or KV-owned (dK/dV) CSR
   const int32_t* col;

@@ -9,6 +9,8 @@ for validity against the oracle's scores and only agreeing rows are compared.
 
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -303,6 +305,27 @@ def test_rows_with_zero_query_and_zero_gradient_are_skipped_exactly():
         dq = res["dq"] if layout == "bhsd" else res["dq"].transpose(0, 2, 1, 3)
         for i, qv in enumerate(case.q_var.tolist()):
             assert np.all(dq[:, :, i * 256 + qv:(i + 1) * 256] == 0), (case.name, i)
+
+
+def test_rows_with_zero_gradient_and_nonzero_query_are_skipped_exactly():
+    """The backward's live extent follows dO alone: padded slots with a
+    non-zero query but a zero gradient (dP = 0 and Dr = 0, so dS = 0) are
+    skipped like all-zero ones, and dq stays exactly zero there."""
+    case = build_case("zero_grad_rows", dtype="bf16", layout="bshd", B=1, Hq=2, Hkv=1, D=128,
+                      q_var=[61, 256, 199], kv_var=[256, 100, 64], map_kind="ones", seed=29)
+    # queries in the padded slots (the gradient there stays zero)
+    pad = np.concatenate([np.arange(i * 256 + n, (i + 1) * 256) for i, n in enumerate(case.q_var.tolist())])
+    noise = torch.randn(case.q.shape, generator=torch.Generator().manual_seed(31)).to(case.q.dtype)
+    q = case.q.clone()
+    q[:, pad] = noise[:, pad]
+    case = dataclasses.replace(case, q=q)
+    _say(f"[{case.name}]")
+    assert float(case.dout[:, pad].abs().max()) == 0 and float(case.q[:, pad].abs().max()) > 0
+    res = run_case(case)
+    _compare_case(case, res, oracle.Oracle(case, np.float32))
+    dq = res["dq"].transpose(0, 2, 1, 3)
+    for i, qv in enumerate(case.q_var.tolist()):
+        assert np.all(dq[:, :, i * 256 + qv:(i + 1) * 256] == 0), i
 
 
 def test_bhsd_and_bshd_are_bit_identical():
