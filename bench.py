@@ -13,7 +13,7 @@ query x valid key pairs: 4*D flops per pair for the forward (QK^T and PV) and
 rate; fwd and bwd are also reported separately, with their fraction of the
 MI355X dense bf16 MFMA peak.
 
-Prints one JSON line. `--gpus N` with N > 1 is refused: this build runs on
+Prints one JSON line. `--gpus N` with N > 1 is refused: the library runs on
 one GPU.
 """
 
@@ -465,8 +465,8 @@ def main():
                           args.copy_probe, args.workload, args.traffic_command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(sharding by head groups is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the path would shard by head groups, each GPU running its heads independently)", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 

@@ -9,7 +9,7 @@
 
 namespace vsa {
 
-constexpr int HD = 128;  // head dimension of this build
+constexpr int HD = 128;  // head dimension the kernels are built for
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;

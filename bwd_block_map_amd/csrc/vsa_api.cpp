@@ -271,7 +271,7 @@ int validate(const vsa_problem* p) {
     return fail(VSA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
   if (p->D < 1) return fail(VSA_ERR_INVALID_ARG, "D must be positive");
   if (p->D > vsa::HD)
-    return fail(VSA_ERR_UNSUPPORTED, "head dimension %d: this build takes D <= 128", p->D);
+    return fail(VSA_ERR_UNSUPPORTED, "head dimension %d: the kernels take D <= 128", p->D);
   if (p->q_block < 1 || p->kv_block < 1)
     return fail(VSA_ERR_INVALID_ARG, "q_block and kv_block must be positive");
   if ((p->q_block % 32 != 0 && p->q_block != 8 && p->q_block != 16) || p->kv_block % 64 != 0)

@@ -56,7 +56,7 @@ extern "C" {
 enum vsa_status {
   VSA_OK = 0,
   VSA_ERR_INVALID_ARG = 1, /* bad shape, pointer or combination: nothing launched */
-  VSA_ERR_UNSUPPORTED = 2, /* valid request that this build has no kernel for    */
+  VSA_ERR_UNSUPPORTED = 2, /* valid request the library has no kernel for        */
   VSA_ERR_WORKSPACE = 3,   /* workspace or saved-state buffer too small          */
   VSA_ERR_HIP = 4          /* a HIP runtime or launch error                      */
 };
@@ -197,7 +197,7 @@ int vsa_abi_version(void);
 /* Host-only check of a problem (no device access). Messages for the cases
  * the pages name: "actual_seq_lengths must be specified",
  * "actual_seq_lengths_kv must be specified" (TND without cu_seqlens_q / _kv).
- * Limits of this build (VSA_ERR_UNSUPPORTED): D <= 128; q_block 8, 16 or a
+ * Limits of the library (VSA_ERR_UNSUPPORTED): D <= 128; q_block 8, 16 or a
  * multiple of 32, kv_block a multiple of 64; fewer than 65536 heads in BSHD and
  * TND (row offsets of the tile loads are 24-bit); B*Hq*Qb*KVb and B*Hq*Sq below
  * 2^31; with top-k or a gate, KVb <= 38848 (one row of coarse scores per KV tile
