@@ -76,10 +76,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const PreArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) ocv[u] = ocp[u];
   }
+  // the next pass's dO and O_sel rows are loaded before this pass's stores
+  uint4 dv_n = make_uint4(0, 0, 0, 0), ov_n = make_uint4(0, 0, 0, 0);
+  if (slot < qexist) {
+    const long long off = qb + (long long)(blk0 + slot) * qrs + 8 * dg;
+    dv_n = ldg16(a.dout + off);
+    ov_n = ldg16(a.osel + off);
+  }
   for (int s = slot; s < qexist; s += 16) {
     const long long off = qb + (long long)(blk0 + s) * qrs + 8 * dg;
-    const uint4 dv = ldg16(a.dout + off);
-    const uint4 ov = ldg16(a.osel + off);
+    const uint4 dv = dv_n, ov = ov_n;
+    if (s + 16 < qexist) {
+      dv_n = ldg16(a.dout + off + 16 * qrs);
+      ov_n = ldg16(a.osel + off + 16 * qrs);
+    }
     const uint4 qv = proj ? ldg16(a.q + off) : make_uint4(0, 0, 0, 0);  // for the gate only
     // the row is live when one of its 16 lanes sees a non-zero element of dO
     // (either sign of zero counts as zero); the wave holds rows 4w .. 4w+3
