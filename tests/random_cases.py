@@ -17,7 +17,7 @@ import numpy as np
 
 from workloads.synth import build_case
 
-N_CASES = 36
+N_CASES = 60  # problems 36 .. 59 are larger (more tiles, blocks and heads)
 
 
 def _counts(rng, tiles, tile, batch):
@@ -32,28 +32,29 @@ def random_case(i: int):
     """Problem i: (case, run options) with run options {atomic_dq, persistent}."""
     rng = np.random.default_rng(7100 + i)
     kind = ("video", "plain", "tnd")[i % 3]
+    big = i >= 36
     dtype = ("bf16", "fp16")[int(rng.integers(2))]
     D = int(rng.choice([128, 128, 128, 96, 64, 40]))
-    Hkv = int(rng.integers(1, 3))
+    Hkv = int(rng.integers(1, 5 if big else 3))
     Hq = Hkv * int(rng.choice([1, 2, 4]))
     seed = 500 + i
     if kind == "video":
         tile = int(rng.choice([64, 128, 256]))
         B = int(rng.integers(1, 3))
         per_entry = B > 1 and rng.random() < 0.5
-        nq, nk = int(rng.integers(1, 7)), int(rng.integers(1, 9))
+        nq, nk = int(rng.integers(1, 21 if big else 7)), int(rng.integers(1, 41 if big else 9))
         q_var = _counts(rng, nq, tile, B if per_entry else 0)
         kv_var = _counts(rng, nk, tile, B if per_entry else 0)
         gate = str(rng.choice(["none", "per_token", "per_element", "projected"]))
         case = build_case(f"rand{i}_video", dtype=dtype, layout=str(rng.choice(["bhsd", "bshd"])),
                           B=B, Hq=Hq, Hkv=Hkv, D=D, q_block=tile, kv_block=tile,
                           q_var=q_var.tolist(), kv_var=kv_var.tolist(),
-                          topk=int(rng.integers(1, nk + 2)), map_kind="none", gate_mode=gate,
+                          topk=int(rng.integers(1, min(nk, 12) + 2)), map_kind="none", gate_mode=gate,
                           pad_dout=bool(rng.integers(2)), seed=seed)
     elif kind == "plain":
         qb = int(rng.choice([8, 16, 32, 64, 96, 128, 256]))
         kb = int(rng.choice([64, 128, 192, 256, 320]))
-        Sq, Skv = int(rng.integers(1, 700)), int(rng.integers(1, 1000))
+        Sq, Skv = int(rng.integers(1, 3000 if big else 700)), int(rng.integers(1, 4000 if big else 1000))
         topk = int(rng.integers(1, 4)) if rng.random() < 0.3 else 0
         gate = str(rng.choice(["none", "per_token"])) if topk else "none"
         case = build_case(f"rand{i}_plain", dtype=dtype, layout=str(rng.choice(["bhsd", "bshd"])),
@@ -62,8 +63,8 @@ def random_case(i: int):
                           map_p=float(rng.uniform(0.1, 0.9)), gate_mode=gate, seed=seed)
     else:
         n = int(rng.integers(1, 5))
-        q_lens = rng.integers(1, 300, n).tolist()
-        kv_lens = rng.integers(1, 400, n).tolist()
+        q_lens = rng.integers(1, 1200 if big else 300, n).tolist()
+        kv_lens = rng.integers(1, 1600 if big else 400, n).tolist()
         case = build_case(f"rand{i}_tnd", dtype=dtype, layout="tnd", Hq=Hq, Hkv=Hkv, D=D,
                           q_block=int(rng.choice([16, 32, 64, 128])),
                           kv_block=int(rng.choice([64, 128])), q_lens=q_lens, kv_lens=kv_lens,
