@@ -328,6 +328,19 @@ def test_rows_with_zero_gradient_and_nonzero_query_are_skipped_exactly():
         assert np.all(dq[:, :, i * 256 + qv:(i + 1) * 256] == 0), i
 
 
+@pytest.mark.parametrize("q_lens,kv_lens", [([20, 50], [0, 40]), ([0, 50, 7], [30, 0, 9])],
+                         ids=["no_keys", "no_queries_and_no_keys"])
+def test_tnd_sequences_of_length_zero(q_lens, kv_lens):
+    """Packed sequences without queries or without keys: a sequence with no
+    keys gives rows without a live key (out = 0, lse = -inf, dq = 0), one with
+    no queries contributes nothing, and the other sequences are unaffected."""
+    case = build_case("tnd_empty", dtype="bf16", layout="tnd", Hq=2, Hkv=1, D=128, q_block=32,
+                      kv_block=64, q_lens=q_lens, kv_lens=kv_lens, map_kind="ones", seed=3)
+    _say(f"[tnd_empty] q_lens={q_lens} kv_lens={kv_lens}")
+    res = run_case(case)
+    _compare_case(case, res, oracle.Oracle(case, np.float32))
+
+
 def test_bhsd_and_bshd_are_bit_identical():
     a = make_case("p1_gated", layout="bhsd")
     b = _as_bshd(a)
