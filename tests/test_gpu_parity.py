@@ -341,6 +341,23 @@ def test_tnd_sequences_of_length_zero(q_lens, kv_lens):
     _compare_case(case, res, oracle.Oracle(case, np.float32))
 
 
+@pytest.mark.parametrize("gate_mode", ["per_token", "projected"])
+def test_batch_entry_without_any_key(gate_mode):
+    """Per-entry valid counts where one batch entry has no valid key at all:
+    its coarse softmax has an empty domain (lse_c = -inf, O_c = 0), top-k
+    selects nothing, its rows come out as zero with lse = -inf and zero
+    gradients, and the other entry is unaffected."""
+    case = build_case("no_keys_entry", dtype="bf16", layout="bshd", B=2, Hq=2, Hkv=1, D=128,
+                      q_var=[[256, 61], [256, 256]], kv_var=[[256, 0, 100], [0, 0, 0]], topk=2,
+                      map_kind="none", gate_mode=gate_mode, seed=41)
+    _say(f"[no_keys_entry {gate_mode}]")
+    res = run_case(case)
+    orc = oracle.Oracle(case, np.float32)
+    assert _topk_agreement(orc, res["map"]).all()
+    _compare_case(case, res, orc)
+    assert not res["map"][1].any()
+
+
 def test_bhsd_and_bshd_are_bit_identical():
     a = make_case("p1_gated", layout="bhsd")
     b = _as_bshd(a)
