@@ -386,8 +386,8 @@ __global__ __launch_bounds__(NWC * 64) void coarse_bwd_rows_kernel(const CoarseA
   __syncthreads();
   const bool row_ok = r < nr;
   const float lse_r = row_ok ? a.lse_c[rowbase + r] : -INFINITY;
-  float* prow = a.ps + (rowbase + r) * KVb;
-  float* wrow = a.dss + (rowbase + r) * KVb;
+  float* prow = row_ok ? a.ps + (rowbase + r) * KVb : nullptr;   // used only for rows that exist
+  float* wrow = row_ok ? a.dss + (rowbase + r) * KVb : nullptr;
   const bool vec_store = (KVb & 3) == 0;
 
   f32x4_t U[2][4], Z[2][4];
