@@ -106,89 +106,139 @@ def _host_threads():
     return (min(aff, int(share)) if share and share.isdigit() and int(share) > 0 else aff), aff
 
 
+def _head0(case):
+    """Head 0 (and the KV head it reads) of every batch entry of a workload, with
+    its own geometry, block map and gate; tensors on the host."""
+    import dataclasses
+    if case.layout == "bshd":
+        sl = (slice(None), slice(None), slice(0, 1))
+    else:  # bhsd [B, H, S, D] and tnd [T, H, D]: heads on dim 1
+        sl = (slice(None), slice(0, 1))
+    pick = {n: getattr(case, n)[sl].contiguous().cpu() for n in ("q", "k", "v", "dout")}
+    gate = case.gate
+    if gate is not None:
+        if case.gate_mode == "projected":  # [w (Hq x D) | b (Hq)]: head 0's row and bias
+            gate = torch.cat([gate[:case.D], gate[case.Hq * case.D:case.Hq * case.D + 1]])
+        else:
+            gate = gate[sl]
+        gate = gate.contiguous().cpu()
+    bmap = case.block_map[:, 0:1].contiguous().cpu() if case.block_map is not None else None
+    return dataclasses.replace(case, name=case.name + "_head0", Hq=1, Hkv=1, gate=gate,
+                               block_map=bmap, **pick)
+
+
 def cpu_baseline(case, gpu_valid_pairs, target_s=12.0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload,
     fwd and bwd timed separately and each extrapolated linearly to the whole
     workload by its valid (q, k) pair count (labelled as such).
 
-    Sample: head 0 of the workload with its own pooled-score top-k selection.
-    fwd: every row of a random set of Q tiles (oracle fwd_rows). bwd: the full
-    oracle backward (row pass with dq, key pass with dk/dv, compression
-    backward) of the same head with the selection restricted to a random set of
-    Q tiles. Rates are in the bench's unit: 4*D (fwd) and 10*D (bwd) flop per
-    valid pair of the sample."""
+    Sample: head 0 of every batch entry, with the workload's own selection (its
+    pooled-score top-k, or its block map). fwd: every row of a random set of
+    (batch entry, Q tile) pairs (oracle fwd_rows). bwd: the full oracle backward
+    (row pass with dq, key pass with dk/dv, compression backward) of the same
+    head with the selection restricted to a random set of them. Rates are in
+    the bench's unit: 4*D (fwd) and 10*D (bwd) flop per valid pair of the
+    sample."""
     import oracle
-    from workloads.synth import build_case
 
     threads, aff = _host_threads()
-    sub = build_case(case.name + "_head0", dtype=case.dtype, layout=case.layout, B=1, Hq=1,
-                     Hkv=1, D=case.D, q_block=case.q_block, kv_block=case.kv_block,
-                     q_var=case.q_var, kv_var=case.kv_var, topk=case.topk, map_kind="none",
-                     gate_mode=case.gate_mode, seed=0)
-    sl = (slice(None), slice(None), slice(0, 1)) if case.layout == "bshd" else \
-        (slice(None), slice(0, 1))
-    tens = {n: getattr(case, n)[sl].contiguous().cpu() for n in ("q", "k", "v", "dout")}
-    tens["gate"] = case.gate[sl].contiguous().cpu() if case.gate is not None else None
-    orc = oracle.Oracle(sub, np.float32, threads=threads, tensors=tens)
+    sub = _head0(case)
+    orc = oracle.Oracle(sub, np.float32, threads=threads)
     t0 = time.perf_counter()
-    bmap = orc.block_map()  # pooling + top-k of the head
+    bmap = orc.block_map()  # the head's selection (pooling + top-k when the workload has it)
     t_sel = time.perf_counter() - t0
-    kv = np.asarray(sub.kv_var, np.float64)
-    qv = np.minimum(np.asarray(sub.q_var, np.float64), sub.q_block)
+    Bm = bmap.shape[0]
     rng = np.random.default_rng(1234)
-    tiles = rng.permutation(sub.Qb)
+    tiles = rng.permutation(sub.B * sub.Qb)  # (batch entry, Q tile) as b * Qb + t
 
-    def pairs(ts):  # valid (q, k) pairs of the listed Q tiles
-        return float(sum(qv[t] * kv[bmap[0, 0, t].astype(bool)].sum() for t in ts))
+    def rows_end(b):  # rows of entry b that exist
+        return sub.q_lens[b] if sub.layout == "tnd" else sub.Sq
+
+    def masked(ts):  # the selection restricted to the listed tiles
+        m = np.zeros((sub.B, 1, sub.Qb, sub.KVb), np.uint8)
+        for x in ts:
+            b, t = divmod(int(x), sub.Qb)
+            m[b, 0, t] = bmap[b if Bm > 1 else 0, 0, t]
+        return m
+
+    def pairs(ts):  # valid (q, k) pairs of the listed tiles
+        return valid_pairs(sub, torch.from_numpy(masked(ts)))[0]
 
     def rows_of(ts):
-        return np.array([[0, 0, t * sub.q_block + r] for t in ts for r in range(sub.q_block)],
-                        np.int32)
+        rows = []
+        for x in ts:
+            b, t = divmod(int(x), sub.Qb)
+            rows += [[b, 0, s] for s in range(t * sub.q_block, min((t + 1) * sub.q_block, rows_end(b)))]
+        return np.array(rows, np.int32).reshape(-1, 3)
 
     def bwd_of(ts):
-        m = np.zeros_like(bmap)
-        m[0, 0, ts] = bmap[0, 0, ts]
-        o = oracle.Oracle(sub, np.float32, threads=threads, tensors=tens)
-        o.set_map(m)
+        o = oracle.Oracle(sub, np.float32, threads=threads)
+        o.set_map(masked(ts))
         t = time.perf_counter()
         o.bwd()
         return time.perf_counter() - t
 
-    # forward: a warm-up tile (thread start-up), a calibration on four tiles,
-    # then a sample sized to 40 % of the time target
+    n = len(tiles)
+    def timed(fn, reps):
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        return (time.perf_counter() - t) / reps
+
+    def reps_for(one, budget):
+        return int(min(1000, max(1, budget / max(one, 1e-5))))
+
+    # forward: a warm-up tile (thread start-up) and a calibration on up to four
+    # tiles give the cost of one tile; the sample is the whole head (repeated)
+    # when it fits 40 % of the time target, else a random set of tiles that does
     orc.fwd_rows(rows_of(tiles[:1]))
-    t0 = time.perf_counter()
-    orc.fwd_rows(rows_of(tiles[1:5]))
-    one = (time.perf_counter() - t0) / 4
-    nf = int(max(1, min(len(tiles) // 2, 0.4 * target_s / max(one, 1e-4))))
-    fs = tiles[5:5 + nf]
-    t0 = time.perf_counter()
-    orc.fwd_rows(rows_of(fs))
-    t_f = time.perf_counter() - t0
+    cal = tiles[:min(n, 4)]
+    one = timed(lambda: orc.fwd_rows(rows_of(cal)), 1) / len(cal)
+    if n * one <= 0.4 * target_s:
+        fs = tiles
+        rows = rows_of(fs)
+        reps_f = reps_for(n * one, 0.4 * target_s)
+    else:
+        fs = tiles[:int(max(1, min(n, 0.4 * target_s / one)))]
+        rows = rows_of(fs)
+        reps_f = 1
+    t_f = timed(lambda: orc.fwd_rows(rows), reps_f)
     # backward: a call has a fixed cost (the head's pooling, coarse branch and
-    # key scan) besides its per-tile one; two calibration calls (2 and 8 tiles)
-    # separate them, and the sample is sized to 60 % of the time target
-    c2, c8 = bwd_of(tiles[-2:]), bwd_of(tiles[-8:])
-    per = max((c8 - c2) / 6, 1e-4)
-    fixed = max(c2 - 2 * per, 0.0)
-    nb = int(max(1, min(len(tiles) // 2, (0.6 * target_s - fixed) / per)))
-    bs = tiles[-nb:]
-    t_b = bwd_of(bs)
+    # key scan) besides its per-tile one; two calibration calls separate them,
+    # and the sample (whole head or a tile set) gets 60 % of the time target
+    lo, hi = tiles[-min(n, 2):], tiles[-min(n, 8):]
+    c_lo, c_hi = bwd_of(lo), bwd_of(hi)
+    per = max((c_hi - c_lo) / max(len(hi) - len(lo), 1), 1e-5)
+    fixed = max(c_lo - len(lo) * per, 0.0)
+    if fixed + n * per <= 0.6 * target_s:
+        bs = tiles
+        reps_b = reps_for(fixed + n * per, 0.6 * target_s)
+    else:
+        bs = tiles[-int(max(1, min(n, (0.6 * target_s - fixed) / per))):]
+        reps_b = 1
+    t_b = sum(bwd_of(bs) for _ in range(reps_b)) / reps_b
     pf, pb = pairs(fs), pairs(bs)
+    if pf <= 0 or pb <= 0:
+        return {"value": None, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": "the sampled tiles hold no valid pair", "cpu_model": _cpu_model(),
+                "affinity_cores": aff}
     fwd_rate = 4.0 * sub.D * pf / t_f / 1e12
     bwd_rate = 10.0 * sub.D * pb / t_b / 1e12
     t_f_all = t_f * gpu_valid_pairs / pf
     t_b_all = t_b * gpu_valid_pairs / pb
+    sel = "its own top-k selection" if case.topk > 0 else "the workload's block map"
     return {
         "value": (4.0 + 10.0) * sub.D * gpu_valid_pairs / (t_f_all + t_b_all) / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fp32 oracle on head 0 of {case.Hq} with its own top-k selection: fwd of "
-                   f"all {sub.q_block} rows of {len(fs)} random Q tiles ({t_f:.1f} s), full "
-                   f"backward with the selection cut to {len(bs)} other Q tiles ({t_b:.1f} s); "
-                   f"rates over the sampled valid pairs; whole-workload seconds extrapolated "
-                   f"linearly by valid pairs"),
+        "sample": (f"fp32 oracle on head 0 of {case.Hq} with {sel}: fwd of the rows of "
+                   f"{len(fs)} random (batch entry, Q tile) pairs ({t_f:.2f} s), full backward "
+                   + ("of the head" if len(bs) == n else f"with the selection cut to {len(bs)} of them")
+                   + f" ({t_b:.2f} s)"
+                   + (f", the mean of {reps_f} and {reps_b} runs" if reps_f * reps_b > 1 else "")
+                   + "; rates over the sampled valid pairs; whole-workload seconds "
+                   "extrapolated linearly by valid pairs"),
         "fwd_tflops": round(fwd_rate, 4), "bwd_tflops": round(bwd_rate, 4),
         "fwd_seconds_sample": round(t_f, 2), "bwd_seconds_sample": round(t_b, 2),
         "fwd_seconds_extrapolated": round(t_f_all, 1),
