@@ -17,7 +17,7 @@ import numpy as np
 
 from workloads.synth import build_case
 
-N_CASES = 60  # problems 36 .. 59 are larger (more tiles, blocks and heads)
+N_CASES = 120  # problems 36 .. 119 are larger (more tiles, blocks and heads)
 
 
 def _counts(rng, tiles, tile, batch):
