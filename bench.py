@@ -485,6 +485,8 @@ def main():
                     help="another gate form than the workload's (the 720p workload only)")
     ap.add_argument("--dout-unpadded", action="store_true",
                     help="draw dO without zeroing the padded slots of partial tiles")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="after timing, copy BYTES on the device once (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -592,6 +594,30 @@ def main():
         bwd()
     torch.cuda.synchronize()
     plain_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # --graph: one step captured in a HIP graph (the library allocates nothing
+    # and records no memset node) and replayed; an untimed extra showing what a
+    # caller that captures its step sees where launch latency dominates
+    graph_ms = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # a warm-up step on the capture stream
+            fwd()
+            bwd()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fwd()
+            bwd()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        log(f"[bench] graph replay: {graph_ms:.3f} ms per step")
 
     per_kernel = {k: {"ms_per_launch": (ms / n if n else 0.0), "launches_per_step": n / args.steps}
                   for k, (ms, n) in prof.items()}
@@ -632,6 +658,7 @@ def main():
                                  "persistent": "persistent, longest first",
                                  "per-item": "one work-group per span"}[args.grid]},
         "ms_per_step_without_events": round(plain_ms, 3),
+        "ms_per_step_graph": None if graph_ms is None else round(graph_ms, 4),
         "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
         "fwd_ms_min": round(float(min(fwd_all)), 3), "bwd_ms_min": round(float(min(bwd_all)), 3),
         "fwd_tflops": round(fwd_t, 2), "bwd_tflops": round(bwd_t, 2),
