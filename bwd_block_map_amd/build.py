@@ -41,8 +41,6 @@ EXTRA = {
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     extra = EXTRA.get(src, [])
-    if os.environ.get("VSA_MFMA_VGPR_FORM") is not None:  # build experiments
-        extra = ["-mllvm", f"-amdgpu-mfma-vgpr-form={os.environ['VSA_MFMA_VGPR_FORM']}"]
     cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
