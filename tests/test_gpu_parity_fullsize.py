@@ -6,7 +6,8 @@ The oracle cannot evaluate whole heads at these sizes in seconds, so it checks
 near-tie under the oracle's pooled scores), (b) sampled rows (out, lse, dq)
 across full, partial and padded Q rows of the sampled heads, (c) dk/dv of
 sampled KV tiles of every valid-count kind (256, 64 and, at 720p, 16 valid
-keys; the least-selected tile of each kind) spread over the sampled heads, and
+keys; the least-selected tile of each kind, spread over the sampled heads, and
+the most-selected full tile of the first sampled head), and
 (d) over all heads, two identities that hold at any size: the key-shift
 identity sum_t dk_t = 0 and the value-shift identity
 sum_t dv_t = sum_s dO_s (+ sum_s gate_s dO_s with the gate).
@@ -133,12 +134,23 @@ def _fullsize(name, heads, nrows, atomic_dq=False):
             if cand:
                 j = int(min(cand, key=lambda x: cnt[x]))
                 tiles.append((hl, j, int(cnt[j])))
+        if hl == 0 and not atomic_dq:
+            # and the most-selected full tile of the first sampled head: one of
+            # the longest KV-owned walks, whose large sums are held to the bf16
+            # rounding-floor bar (its rows cost the oracle most of a head's
+            # forward, so the atomic-dQ run, whose dK/dV pass is the same, skips it)
+            cand = [j for j in np.nonzero((kvv == sub.kv_block) & (cnt > 0))[0] if j not in bad]
+            if cand:
+                j = int(max(cand, key=lambda x: cnt[x]))
+                tiles.append((hl, j, int(cnt[j])))
     tk, tv = orc.dkdv_tiles(np.array([[0, hl, j] for hl, j, _ in tiles], np.int32))
     for n, (hl, j, c) in enumerate(tiles):
         sl = slice(j * sub.kv_block, (j + 1) * sub.kv_block)
         _say(f"  head {heads[hl]} tile {j}: valid {kvv[j]}, selected by {c} Q tiles")
-        check(f"dk {heads[hl]}/{j}", tk[n], res["dk"][0, sl, heads[hl]].float().cpu().numpy(), GRAD_TOL)
-        check(f"dv {heads[hl]}/{j}", tv[n], res["dv"][0, sl, heads[hl]].float().cpu().numpy(), GRAD_TOL)
+        check(f"dk {heads[hl]}/{j}", tk[n], res["dk"][0, sl, heads[hl]].float().cpu().numpy(),
+              GRAD_TOL, case.dtype)
+        check(f"dv {heads[hl]}/{j}", tv[n], res["dv"][0, sl, heads[hl]].float().cpu().numpy(),
+              GRAD_TOL, case.dtype)
 
 
 def test_c4_video_full_size():
