@@ -967,6 +967,9 @@ __global__ __launch_bounds__(NW * 64, 2) void sparse_dq_kernel(const BwdArgs a) 
     // dQ^T += K^T dS^T over its two key steps of 16
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
+      // a chunk of at most 32 keys: its second half is all padding, whose
+      // dS = 0 adds exactly nothing
+      if (hf == 1 && rem <= 32) break;
       f32x16_t sv, pv;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = pv[r] = 0.f;
